@@ -1,0 +1,430 @@
+"""Pins of the oracle to things other than itself (CPU only).
+
+Each check below is independent of the oracle's code: hand-derived closed forms from
+tests/golden, torch's SDPA on dense padded tensors built from the logical stream (never the
+pool), invariants the method implies, and brute force through flat-index pool addressing.
+The mutant tests at the end plant plausible mistakes in the oracle and show that each one
+fails at least one pin.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.paged_attention as pa
+from helpers import causal_last_rows, dense_sdpa, golden_array, load_golden
+from paged_kv_cache_247_amd import workload as W
+
+LN2 = math.log(2.0)
+
+
+def _golden_case(case):
+    k = golden_array(case["k_cache"])
+    v = golden_array(case["v_cache"])
+    q = golden_array(case["q"])
+    bt = np.array(case["block_tables"], dtype=np.int32)
+    L = np.array(case["context_lens"], dtype=np.int32)
+    return q, k, v, bt, L
+
+
+# ---------------------------------------------------------------- closed forms (golden)
+
+def check_golden_decode():
+    worst = 0.0
+    for case in load_golden()["cases"]:
+        q, k, v, bt, L = _golden_case(case)
+        out = oracle.decode(q, k, v, bt, L, LN2, case["num_kv_heads"], "f64")
+        exp = golden_array(case["expected_out"])
+        worst = max(worst, oracle.max_abs_err(out, exp))
+    return worst
+
+
+def test_golden_decode():
+    assert check_golden_decode() < 1e-12
+
+
+def check_golden_partials():
+    case = load_golden()["cases"][0]
+    q, k, v, bt, L = _golden_case(case)
+    P = case["partition_size"]
+    m, l, o = oracle.decode_partials(q, k, v, bt, L, LN2, case["num_kv_heads"], "f64", P)
+    em = golden_array(case["expected_max_logits_ln2"]) * LN2
+    el = golden_array(case["expected_exp_sums"])
+    eo = golden_array(case["expected_tmp_out"])
+    written = ~np.isnan(em)
+    assert np.array_equal(written, ~np.isnan(m)), "written partitions differ"
+    err = max(np.abs(m[written] - em[written]).max(), np.abs(l[written] - el[written]).max(),
+              np.abs(o[written] - eo[written]).max())
+    red = oracle.reduce_partials(m, l, o, L, P)
+    return max(err, oracle.max_abs_err(red, golden_array(case["expected_out"])))
+
+
+def test_golden_partials_and_reduce():
+    assert check_golden_partials() < 1e-12
+
+
+def check_golden_write():
+    wc = load_golden()["write_case"]
+    N, Hkv, S, D = wc["num_blocks"], wc["num_kv_heads"], wc["block_size"], wc["head_dim"]
+    k0 = np.zeros((N, Hkv, S, D))
+    v0 = np.zeros((N, Hkv, D, S))
+    k, v = oracle.write_cache(k0, v0, golden_array(wc["key"]), golden_array(wc["value"]),
+                              np.array(wc["slot_mapping"], dtype=np.int64), S)
+    return (np.array_equal(k, golden_array(wc["expected_k_cache"]))
+            and np.array_equal(v, golden_array(wc["expected_v_cache"])))
+
+
+def test_golden_write():
+    assert check_golden_write()
+
+
+# ---------------------------------------------------------------- library routine: SDPA
+
+def check_dense(wl):
+    c = wl.cfg
+    kc, vc = oracle.write_cache(wl.k_cache, wl.v_cache, wl.key, wl.value, wl.slot_mapping,
+                                c.block_size)
+    if len(wl.block_mapping):
+        (kc,), (vc,) = oracle.copy_blocks([kc], [vc], wl.block_mapping)
+    out = oracle.decode(wl.q, kc, vc, wl.block_tables, wl.context_lens, c.scale,
+                        c.num_kv_heads, c.dtype)
+    return oracle.max_abs_err(out, dense_sdpa(wl))
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_paged_equals_padded_dense_sdpa(name):
+    wl = W.generate(W.SMALL[name], keep_logical=True)
+    assert check_dense(wl) < 1e-12
+
+
+@pytest.mark.parametrize("name", ["c1", "c3", "c5"])
+def test_decode_is_last_row_of_causal_recompute(name):
+    wl = W.generate(W.SMALL[name], keep_logical=True)
+    c = wl.cfg
+    kc, vc = oracle.write_cache(wl.k_cache, wl.v_cache, wl.key, wl.value, wl.slot_mapping,
+                                c.block_size)
+    out = oracle.decode(wl.q, kc, vc, wl.block_tables, wl.context_lens, c.scale,
+                        c.num_kv_heads, c.dtype)
+    assert oracle.max_abs_err(out, causal_last_rows(wl)) < 1e-12
+
+
+# ---------------------------------------------------------------- invariants
+
+def _step_pool(wl):
+    c = wl.cfg
+    kc, vc = oracle.write_cache(wl.k_cache, wl.v_cache, wl.key, wl.value, wl.slot_mapping,
+                                c.block_size)
+    if len(wl.block_mapping):
+        (kc,), (vc,) = oracle.copy_blocks([kc], [vc], wl.block_mapping)
+    return kc, vc
+
+
+def _decode(wl, kc, vc, tables=None, dtype=None, scale=None, q=None):
+    c = wl.cfg
+    return oracle.decode(wl.q if q is None else q, kc, vc,
+                         wl.block_tables if tables is None else tables, wl.context_lens,
+                         c.scale if scale is None else scale, c.num_kv_heads,
+                         dtype or c.dtype)
+
+
+@pytest.mark.parametrize("name", ["c1", "c3", "c4", "c5"])
+def test_block_permutation_invariance(name):
+    wl = W.generate(W.SMALL[name])
+    base = _decode(wl, *_step_pool(wl))
+    for seed in (1, 2):
+        wp = W.permute_pool(wl, seed)
+        assert np.array_equal(_decode(wp, *_step_pool(wp)), base)
+
+
+def test_shared_prefix_equals_private_copy():
+    wl = W.generate(W.SMALL["c4"])
+    c = wl.cfg
+    kc, vc = oracle.write_cache(wl.k_cache, wl.v_cache, wl.key, wl.value, wl.slot_mapping,
+                                c.block_size)
+    shared = _decode(wl, kc, vc, tables=wl.block_tables_before)
+    (kc2,), (vc2,) = oracle.copy_blocks([kc], [vc], wl.block_mapping)
+    private = _decode(wl, kc2, vc2, tables=wl.block_tables)
+    assert (wl.block_tables != wl.block_tables_before).any()
+    assert np.array_equal(shared, private)
+
+
+def _mean_v(wl):
+    c = wl.cfg
+    out = np.zeros((c.num_seqs, c.num_heads, c.head_dim))
+    for i in range(c.num_seqs):
+        m = wl.logical_v[i].astype(np.float64).mean(axis=0)  # [Hkv, D]
+        out[i] = np.repeat(m, c.group, axis=0)
+    return out
+
+
+def test_uniform_weights_give_mean_of_v():
+    wl = W.generate(W.SMALL["c3"].replace(dtype="f32"), keep_logical=True)
+    kc, vc = _step_pool(wl)
+    ref = _mean_v(wl)
+    assert oracle.max_abs_err(_decode(wl, kc, vc, q=np.zeros_like(wl.q)), ref) < 1e-12
+    assert oracle.max_abs_err(_decode(wl, kc, vc, scale=0.0), ref) < 1e-12
+    # every key row of a kv head equal -> equal logits
+    kc_eq = kc.copy()
+    kc_eq[:] = kc[wl.block_tables[0, 0], :, 0:1, :]
+    assert oracle.max_abs_err(_decode(wl, kc_eq, vc), ref) < 1e-12
+
+
+def test_one_token_context_returns_that_row():
+    cfg = W.SMALL["c3"].replace(dtype="f32")
+    wl = W.generate(cfg, keep_logical=True, lens=np.ones(cfg.num_seqs, dtype=np.int32))
+    out = _decode(wl, *_step_pool(wl))
+    for i in range(cfg.num_seqs):
+        assert np.array_equal(out[i], np.repeat(wl.logical_v[i][0].astype(np.float64),
+                                                cfg.group, axis=0))
+
+
+def test_empty_context_gives_zero():
+    cfg = W.SMALL["c3"]
+    wl = W.generate(cfg)
+    lens = wl.context_lens.copy()
+    lens[[0, 3]] = 0
+    c = wl.cfg
+    kc, vc = _step_pool(wl)
+    out = oracle.decode(wl.q, kc, vc, wl.block_tables, lens, c.scale, c.num_kv_heads, c.dtype)
+    assert not out[[0, 3]].any()
+    m, l, o = oracle.decode_partials(wl.q, kc, vc, wl.block_tables, lens, c.scale,
+                                     c.num_kv_heads, c.dtype, 64)
+    assert np.isnan(m[[0, 3]]).all()
+    assert not oracle.reduce_partials(m, l, o, lens, 64)[[0, 3]].any()
+
+
+def check_split(wl, P):
+    c = wl.cfg
+    kc, vc = _step_pool(wl)
+    single = _decode(wl, kc, vc)
+    m, l, o = oracle.decode_partials(wl.q, kc, vc, wl.block_tables, wl.context_lens, c.scale,
+                                     c.num_kv_heads, c.dtype, P)
+    return oracle.max_abs_err(oracle.reduce_partials(m, l, o, wl.context_lens, P), single)
+
+
+@pytest.mark.parametrize("name", ["c1", "c3", "c5"])
+def test_split_context_equals_single_pass(name):
+    wl = W.generate(W.SMALL[name])
+    S = wl.cfg.block_size
+    for P in (S, 2 * S, 64, 4096):
+        assert check_split(wl, P) < 1e-12
+
+
+def _f64_workload(name, lens=None, dyadic=False):
+    cfg = W.SMALL[name].replace(dtype="f32")
+    wl = W.generate(cfg, lens=lens)
+    kc, vc = _step_pool(wl)
+    kc, vc = kc.astype(np.float64), vc.astype(np.float64)
+    q = wl.q.astype(np.float64)
+    if dyadic:  # multiples of 2^-8: sums of a few stay exact in fp64
+        kc, vc, q = (np.round(a * 256) / 256 for a in (kc, vc, q))
+    return wl, kc, vc, q
+
+
+def test_token_order_invariance():
+    cfg = W.SMALL["c3"]
+    lens = np.random.default_rng(3).integers(1, 20, cfg.num_seqs) * cfg.block_size
+    wl, kc, vc, q = _f64_workload("c3", lens=lens.astype(np.int32))
+    base = _decode(wl, kc, vc, dtype="f64", q=q)
+    rng = np.random.default_rng(11)
+    pi = rng.permutation(cfg.block_size)  # reorder positions inside every block
+    kp, vp = kc[:, :, pi, :], vc[:, :, :, pi]
+    tables = wl.block_tables.copy()
+    for i in range(cfg.num_seqs):  # and reorder the blocks of every sequence
+        nb = int(wl.context_lens[i]) // cfg.block_size
+        tables[i, :nb] = tables[i, rng.permutation(nb)]
+    out = _decode(wl, kp, vp, tables=tables, dtype="f64", q=q)
+    assert oracle.max_abs_err(out, base) < 1e-12
+
+
+def test_key_shift_invariance():
+    wl, kc, vc, q = _f64_workload("c3", dyadic=True)
+    base = _decode(wl, kc, vc, dtype="f64", q=q)
+    shift = np.random.default_rng(5).integers(-4, 5, (wl.cfg.num_kv_heads, 1, wl.cfg.head_dim))
+    out = _decode(wl, kc + shift[None], vc, dtype="f64", q=q)
+    assert oracle.max_abs_err(out, base) < 1e-9
+
+
+def test_linearity_in_v():
+    wl, kc, vc, q = _f64_workload("c3")
+    v2 = np.random.default_rng(9).standard_normal(vc.shape)
+    a, b = 0.75, -2.5
+    lhs = _decode(wl, kc, a * vc + b * v2, dtype="f64", q=q)
+    rhs = a * _decode(wl, kc, vc, dtype="f64", q=q) + b * _decode(wl, kc, v2, dtype="f64", q=q)
+    assert oracle.max_abs_err(lhs, rhs) < 1e-12
+
+
+# ---------------------------------------------------------------- brute force, layout
+
+def brute_decode(q, kc, vc, tables, lens, scale, Hkv):
+    """Pure-Python loops with math.exp / math.fsum, reading the pools as flat lists through
+    the layout's element offsets ((b*Hkv + g)*S + t)*D + d and ((b*Hkv + g)*D + d)*S + t."""
+    B, H, D = q.shape
+    N, _, S, _ = kc.shape
+    kf = kc.astype(np.float64).ravel().tolist()
+    vf = vc.astype(np.float64).ravel().tolist()
+    G = H // Hkv
+    out = [[[0.0] * D for _ in range(H)] for _ in range(B)]
+    for i in range(B):
+        L = int(lens[i])
+        for h in range(H):
+            g = h // G
+            logits, rows = [], []
+            for pos in range(L):
+                b, t = int(tables[i][pos // S]), pos % S
+                krow = [kf[((b * Hkv + g) * S + t) * D + d] for d in range(D)]
+                vrow = [vf[((b * Hkv + g) * D + d) * S + t] for d in range(D)]
+                logits.append(scale * math.fsum(float(q[i, h, d]) * krow[d] for d in range(D)))
+                rows.append(vrow)
+            if not L:
+                continue
+            mx = max(logits)
+            w = [math.exp(s - mx) for s in logits]
+            tot = math.fsum(w)
+            for d in range(D):
+                out[i][h][d] = math.fsum(w[t] * rows[t][d] for t in range(L)) / tot
+    return np.array(out)
+
+
+def test_brute_force_tiny():
+    cfg = W.Config("tiny", 3, 4, 2, 4, 2, 12, "f32", 99, "uniform", len_lo=1, len_hi=6)
+    wl = W.generate(cfg)
+    kc, vc = _step_pool(wl)
+    out = _decode(wl, kc, vc)
+    ref = brute_decode(wl.q, kc, vc, wl.block_tables, wl.context_lens, cfg.scale, 2)
+    assert oracle.max_abs_err(out, ref) < 1e-12
+
+
+def test_gather_follows_layout_statement():
+    """Encode each pool element's own index in its value and check the gathered rows."""
+    N, Hkv, S, D = 7, 2, 4, 3
+    b, g, t, d = np.meshgrid(np.arange(N), np.arange(Hkv), np.arange(S), np.arange(D),
+                             indexing="ij")
+    code = b * 1000 + g * 100 + t * 10 + d  # value of element (b, g, t, d) of K, V alike
+    kc = code.astype(np.float64)
+    vc = code.transpose(0, 1, 3, 2).astype(np.float64)  # v_cache[b, g, d, t]
+    row = np.array([5, 2, 6], dtype=np.int32)
+    K, V = oracle.gather(kc, vc, row, 10, 1, S, "f64")
+    pos = np.arange(10)
+    expect = (row[pos // S][:, None] * 1000 + 100 + (pos % S)[:, None] * 10
+              + np.arange(D)[None, :])
+    assert np.array_equal(K, expect) and np.array_equal(V, expect)
+
+
+def test_copy_blocks_oracle():
+    rng = np.random.default_rng(0)
+    ks = [rng.standard_normal((6, 2, 4, 3)) for _ in range(2)]
+    vs = [rng.standard_normal((6, 2, 3, 4)) for _ in range(2)]
+    mapping = np.array([[1, 4], [1, 0], [3, 5]])
+    nk, nv = oracle.copy_blocks(ks, vs, mapping)
+    for L in range(2):
+        for src, dst in mapping:
+            assert np.array_equal(nk[L][dst], ks[L][src]) and np.array_equal(nv[L][dst], vs[L][src])
+        for untouched in (1, 2, 3):
+            assert np.array_equal(nk[L][untouched], ks[L][untouched])
+    with pytest.raises(AssertionError):
+        oracle.copy_blocks(ks, vs, np.array([[1, 4], [4, 2]]))
+
+
+def test_bf16_upcast_is_exact():
+    bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0001, 0x7F7F, 0x3EAB], dtype=np.uint16)
+    expect = [1.0, -1.0, 3.140625, 2.0 ** -133, 3.3895313892515355e38, 0.333984375]
+    assert oracle.to_f64(bits, "bf16").tolist() == expect
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def _all_pins_pass():
+    ok = check_golden_decode() < 1e-12 and check_golden_partials() < 1e-12
+    ok = ok and check_golden_write()
+    for name in ("c1", "c3", "c5"):
+        wl = W.generate(W.SMALL[name], keep_logical=True)
+        ok = ok and check_dense(wl) < 1e-12 and check_split(wl, 2 * wl.cfg.block_size) < 1e-12
+    return bool(ok)
+
+
+def test_pins_pass_on_the_oracle():
+    assert _all_pins_pass()
+
+
+def _bad_attend_no_scale(qv, K, V, scale):
+    s = K @ qv
+    p = np.exp(s - s.max())
+    return (p @ V) / p.sum()
+
+
+def _bad_gather_full_last_block(k_cache, v_cache, table_row, L, g, S, dtype):
+    K, V = _orig_gather(k_cache, v_cache, table_row, -(-int(L) // S) * S, g, S, dtype)
+    return K, V
+
+
+def _bad_gather_shifted_table(k_cache, v_cache, table_row, L, g, S, dtype):
+    row = np.roll(np.asarray(table_row), -1)
+    row[row < 0] = table_row[0]
+    return _orig_gather(k_cache, v_cache, row, L, g, S, dtype)
+
+
+def _bad_gather_wrong_head(k_cache, v_cache, table_row, L, g, S, dtype):
+    return _orig_gather(k_cache, v_cache, table_row, L, (g + 1) % k_cache.shape[1], S, dtype)
+
+
+def _bad_reduce_sign(m, l, o, context_lens, P):
+    B, H, _, D = o.shape
+    out = np.zeros((B, H, D))
+    for i in range(B):
+        n = pa.num_partitions(context_lens[i], P)
+        for h in range(H):
+            M = m[i, h, :n].max()
+            w = l[i, h, :n] * np.exp(M - m[i, h, :n])
+            out[i, h] = (w @ o[i, h, :n]) / w.sum()
+    return out
+
+
+def _bad_write_swapped(k_cache, v_cache, key, value, slot_mapping, block_size):
+    S = block_size
+    k, v = k_cache.copy(), v_cache.copy()
+    for t, s in enumerate(slot_mapping):
+        if s >= 0:
+            k[s % S, :, s // S, :] = key[t]
+            v[s % S, :, :, s // S] = value[t]
+    return k, v
+
+
+def _bad_decode_gqa(q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads, dtype):
+    B, H, D = q.shape
+    out = np.zeros((B, H, D))
+    qf = pa.to_f64(q, dtype)
+    for i in range(B):
+        L = int(context_lens[i])
+        for h in range(H if L else 0):
+            K, V = pa.gather(k_cache, v_cache, block_tables[i], L, h % num_kv_heads,
+                             k_cache.shape[2], dtype)
+            out[i, h] = pa._attend(qf[i, h], K, V, scale)
+    return out
+
+
+_orig_gather = pa.gather
+
+
+@pytest.mark.parametrize("attr,mutant", [
+    ("_attend", _bad_attend_no_scale),
+    ("decode", _bad_decode_gqa),
+    ("gather", _bad_gather_full_last_block),
+    ("gather", _bad_gather_shifted_table),
+    ("gather", _bad_gather_wrong_head),
+    ("reduce_partials", _bad_reduce_sign),
+    ("write_cache", _bad_write_swapped),
+])
+def test_planted_mistake_fails_a_pin(monkeypatch, attr, mutant):
+    monkeypatch.setattr(pa, attr, mutant)
+    monkeypatch.setattr(oracle, attr, mutant, raising=False)
+    with np.errstate(all="ignore"):
+        try:
+            ok = _all_pins_pass()
+        except (AssertionError, IndexError, ValueError):
+            ok = False
+    assert not ok, f"planted mistake in {attr} went unnoticed"
