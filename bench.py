@@ -1,0 +1,199 @@
+"""Paged decode benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3] [--kernel auto]
+                    [--partition-size P] [--no-cpu-baseline]
+
+One step is one pass of the whole hot path over one batch: copy-on-write block copies (when
+the workload has them), the cache write of each sequence's newest token, paged decode, and the
+partition merge when the context is split. Inputs are resident in HBM before timing starts.
+Prints one JSON line: KV-read GB/s over the step (value), attended tokens/s, the decode
+kernel's roofline figures (timed per launch with HIP events on the launch stream) and the
+oracle's CPU throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published peak
+
+# Launch configuration the benchmark uses for each workload: (kernel family, partition size).
+LAUNCH = {
+    "c1": ("auto", 0),
+    "c2": ("auto", 0),
+    "c3": ("auto", 512),
+    "c4": ("auto", 512),
+    "c5": ("auto", 512),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description="paged decode benchmark (one GPU)")
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c3", choices=sorted(LAUNCH))
+    ap.add_argument("--kernel", default=None, choices=["auto", "valu", "mfma"])
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
+                    help="also run a plain device copy of this many GiB (counter calibration)")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, target_s: float):
+    """Oracle decode (fp64 numpy, one thread) on the first sequences of the workload."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    c = wl.cfg
+    order = np.arange(c.num_seqs)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.decode(wl.q[:1], wl.k_cache, wl.v_cache, wl.block_tables[:1],
+                      wl.context_lens[:1], c.scale, c.num_kv_heads, c.dtype)
+        per_tok = (time.perf_counter() - t0) / max(int(wl.context_lens[0]), 1)
+        budget = target_s / max(per_tok, 1e-9)
+        cum = np.cumsum(wl.context_lens[order].astype(np.int64))
+        n = int(min(max(np.searchsorted(cum, budget) + 1, 1), c.num_seqs))
+        idx = order[:n]
+        t0 = time.perf_counter()
+        oracle.decode(wl.q[idx], wl.k_cache, wl.v_cache, wl.block_tables[idx],
+                      wl.context_lens[idx], c.scale, c.num_kv_heads, c.dtype)
+        dt = time.perf_counter() - t0
+    toks = int(wl.context_lens[idx].astype(np.int64).sum())
+    kvb = toks * c.num_kv_heads * c.head_dim * (4 if c.dtype == "f32" else 2) * 2
+    return {"value": kvb / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} of {c.num_seqs} sequences ({toks} context tokens), "
+                      f"fp64 numpy decode, one thread, {dt:.1f} s",
+            "attended_tokens_per_s": toks / dt,
+            "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the "
+              "decode path is single-GPU, see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    sys.path.insert(0, os.path.join(os.path.dirname(os.path.abspath(__file__)), "tests"))
+    import paged_kv_cache_247_amd as pk
+    from paged_kv_cache_247_amd import workload as W
+
+    pk.load()  # fails loudly when the library is not built
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    name = args.config
+    kernel, P = LAUNCH[name]
+    kernel = args.kernel or kernel
+    P = P if args.partition_size is None else args.partition_size
+    cfg = W.CONFIGS[name]
+    t0 = time.time()
+    wl = W.generate(cfg, poison="zero")
+    print(f"[bench] generated {name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
+
+    def dev(a, bf=False):
+        a = np.ascontiguousarray(a)
+        if bf:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    bf = cfg.dtype == "bf16"
+    q, kc, vc = dev(wl.q, bf), dev(wl.k_cache, bf), dev(wl.v_cache, bf)
+    key, value = dev(wl.key, bf), dev(wl.value, bf)
+    slots, bt, lens = dev(wl.slot_mapping), dev(wl.block_tables), dev(wl.context_lens)
+    mapping = dev(wl.block_mapping.reshape(-1, 2))
+    out = torch.empty((cfg.num_seqs, cfg.num_heads, cfg.head_dim), dtype=dt, device="cuda")
+    ws = pk.partition_workspace(cfg.num_seqs, cfg.num_heads, cfg.head_dim, wl.max_context_len,
+                                P, q.device) if P else None
+    maxlen = wl.max_context_len
+    has_copy = len(wl.block_mapping) > 0
+    ev = []
+
+    def step(record):
+        if has_copy:
+            pk.copy_blocks([kc], [vc], mapping)
+        pk.reshape_and_cache(key, value, kc, vc, slots)
+        if record:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        pk.paged_attention_decode(None if P else out, q, kc, vc, bt, lens, maxlen, cfg.scale,
+                                  P, ws, kernel=kernel)
+        if record:
+            e1.record()
+            ev.append((e0, e1))
+        if P:
+            pk.paged_attention_reduce(out, ws, lens, P)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+    dec_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    print(f"[bench] {args.steps} steps, {ms_step:.4f} ms/step, decode {dec_ms:.4f} ms/launch",
+          file=sys.stderr, flush=True)
+
+    kvb = wl.kv_bytes()
+    value = kvb / (ms_step * 1e-3) / 1e9
+    achieved = kvb / (dec_ms * 1e-3) / 1e9
+    ukvb = wl.unique_kv_bytes() if has_copy else kvb
+    line = {
+        "metric": "paged decode KV-read GB/s (% of MI355X HBM peak) + attended tokens/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{name}: {cfg.description}", "num_seqs": cfg.num_seqs,
+                   "num_heads": cfg.num_heads, "num_kv_heads": cfg.num_kv_heads,
+                   "head_dim": cfg.head_dim, "block_size": cfg.block_size,
+                   "num_blocks": cfg.num_blocks, "seed": cfg.seed,
+                   "context_tokens": wl.total_tokens, "max_context_len": maxlen,
+                   "kernel": kernel, "partition_size": P, "kv_bytes": kvb,
+                   "unique_kv_bytes": ukvb},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "attended_tokens_per_s": round(wl.total_tokens / (ms_step * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "kernel": "paged_attention_decode",
+                     "ms_per_launch": round(dec_ms, 5), "bytes_per_launch": kvb},
+    }
+    if args.copy_calibration_gib > 0:
+        n = int(args.copy_calibration_gib * (1 << 30)) // 4
+        a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = n * 4
+    if not args.no_cpu_baseline:
+        del q, kc, vc
+        print("[bench] timing the oracle on the CPU", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,165 @@
+/*
+ * pagedkv.h -- C ABI of a PagedAttention decode library for AMD Instinct MI355X (gfx950).
+ *
+ * The problem (sources are the three pages this library follows):
+ *   - A sequence's KV cache is split into fixed-size blocks that live anywhere in a physical
+ *     pool; a per-sequence block table links logical blocks to physical ones (Qualiteg,
+ *     "About PagedAttention for LLM serving", "Deepening Our Understanding ..." item 1-2 and
+ *     "There are logical blocks and physical blocks, and the two are linked by a block
+ *     table").
+ *   - A special kernel removes padding: each sequence of the ragged batch uses exactly its own
+ *     context length (same post, "In a Nutshell ..." item 2-1).
+ *   - The attention operator must therefore be computed over non-contiguous KV-cache blocks
+ *     (vAttention paper, section 3.1 "Requires re-writing the attention kernel"), here for
+ *     one new query token per sequence (decode), with grouped-query attention.
+ *   - Requests sharing a prefix share its KV blocks (Hacker News discussion of
+ *     PagedAttention, replies on prefix sharing); a private copy of a shared block is made
+ *     with pkv_copy_blocks before it diverges.
+ *
+ * Operation: out[i,h,:] = softmax(scale * q[i,h,:] . K_i^T) V_i, where K_i, V_i are the first
+ * L_i = context_lens[i] logical positions of sequence i in kv head h / (H / Hkv). The pages
+ * give no equation; this is the plain scaled-dot-product reading, every cached position
+ * visible to the newest query. context_lens[i] counts the token written this step.
+ *
+ * Layouts (row-major, contiguous; T = the element type named by pkv_dtype):
+ *   q, out         [B, H, D]        T
+ *   k_cache        [N, Hkv, S, D]   T   -- token rows; a (block, kv head) tile is S*D contiguous
+ *   v_cache        [N, Hkv, D, S]   T   -- head_dim rows of S positions; also one contiguous tile
+ *   key, value     [T_new, Hkv, D]  T   -- the new tokens of this step
+ *   slot_mapping   [T_new]          int64, slot = block_id * S + position_in_block
+ *   block_tables   [B, MB]          int32; entries at or past ceil(L_i / S) are never read
+ *   context_lens   [B]              int32
+ *   block_mapping  [M, 2]           int64 (src, dst) pairs
+ *   partition workspace (split-context mode, fp32):
+ *     max_logits, exp_sums [B, H, NPmax];  tmp_out [B, H, NPmax, D]
+ *     with NPmax = ceil(max_context_len / partition_size).
+ *     For partition p of sequence i, head h: max_logits = max of the natural-log logits
+ *     scale*q.k over the partition, exp_sums = sum exp(logit - max_logits), tmp_out = the
+ *     partition's normalised output. Partitions p >= ceil(L_i / partition_size) are not
+ *     written.
+ *
+ * Ownership and threading: every pointer argument marked "device" is caller-owned device
+ * memory; the library allocates and frees nothing and keeps no state beyond its compiled
+ * kernels. All compute calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ * stream) and are reentrant.
+ *
+ * Errors: arguments are validated on the host before anything is enqueued; a failed check
+ * returns PKV_ERR_INVALID_ARGUMENT or PKV_ERR_UNSUPPORTED and enqueues nothing. A failed
+ * kernel launch returns PKV_ERR_HIP (pkv_last_hip_error gives the hipError_t). Errors during
+ * execution surface at the caller's next synchronisation. pkv_last_error_message returns a
+ * thread-local description of the last failure.
+ *
+ * Caller contract that is not checked (it would need a device-to-host copy): block ids are in
+ * [0, N); L_i <= MB * S and L_i <= max_context_len; slots are distinct; copy pairs have
+ * distinct destinations and no destination is also a source. So that a broken contract can
+ * never make a kernel touch memory outside the buffers: kernels clamp block ids into [0, N),
+ * clamp L_i into [0, MB * S] (and the partition count into [0, NPmax]) and skip slots outside
+ * [0, N * S); the results for the affected sequences are then undefined.
+ *
+ * Supported shapes: D in {64, 128}; S in {16, 32}; G = H / Hkv in {1, 2, 4, 8, 16}
+ * (fp32 and the VALU kernel: G <= 8); partition_size 0 or a positive multiple of S.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARGUMENT = 1, /* a size, pointer or alignment is wrong */
+  PKV_ERR_UNSUPPORTED = 2,      /* a valid shape this build has no kernel for */
+  PKV_ERR_HIP = 3               /* the HIP runtime refused a launch */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+/* Decode kernel family. AUTO picks MFMA for fp16/bf16 with G >= 4 (the query group makes the
+ * per-block product a dense G x D by D x S matrix product) and the VALU kernel otherwise. */
+typedef enum { PKV_KERNEL_AUTO = 0, PKV_KERNEL_VALU = 1, PKV_KERNEL_MFMA = 2 } pkv_kernel;
+
+/* Write this step's new K/V rows into the pool: for each t < num_tokens with slot
+ * s = slot_mapping[t] in [0, num_blocks * block_size):
+ *   k_cache[s / S, h, s % S, :] = key[t, h, :];  v_cache[s / S, h, :, s % S] = value[t, h, :]
+ * for every kv head h. Negative slots are skipped (a padding convention). Bit copies.
+ * Source: the cache update of each generation step (Qualiteg post, the past_key_values loop
+ * in "Deepening Our Understanding ..."), placed by slot into blocks (item 1-2).
+ * key, value: device [T_new, Hkv, D]; k_cache, v_cache: device pools; slot_mapping: device
+ * int64 [T_new]. 16-byte aligned key/value/k_cache/v_cache. num_tokens may be 0. */
+pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cache,
+                                 void* v_cache, const int64_t* slot_mapping,
+                                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks, pkv_dtype dtype,
+                                 void* stream);
+
+/* Paged decode attention (the operation at the top of this file) of one query token per
+ * sequence. partition_size == 0: single pass, writes `out`; max_logits/exp_sums/tmp_out must
+ * be NULL. partition_size > 0 (a multiple of block_size): split-context mode, writes the
+ * partition workspace only; call pkv_paged_attention_reduce afterwards on the same stream.
+ * Source: vAttention section 3.1 (attention over non-contiguous KV-cache blocks); Qualiteg
+ * post items 1-2 and 2-1 (blocks, block table, no padding).
+ * out, q: device [B, H, D]; k_cache, v_cache: device pools of num_blocks blocks;
+ * block_tables: device int32 [B, MB]; context_lens: device int32 [B]; max_context_len: a
+ * host-side upper bound of every L_i (sizes the partition grid); scale: the logit scale
+ * (usually 1/sqrt(D)). L_i = 0 gives a zero output row (single pass) or no partials. */
+pkv_status pkv_paged_attention_decode(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t max_context_len, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, pkv_dtype dtype,
+    int32_t partition_size, float* max_logits, float* exp_sums, float* tmp_out, void* stream);
+
+/* The same operation with an explicit kernel family (for measurement and testing).
+ * PKV_KERNEL_MFMA needs fp16/bf16; PKV_KERNEL_VALU needs G <= 8. */
+pkv_status pkv_paged_attention_decode_with(
+    pkv_kernel kernel, void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t max_context_len, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, pkv_dtype dtype,
+    int32_t partition_size, float* max_logits, float* exp_sums, float* tmp_out,
+    void* stream);
+
+/* Merge split-context partitions: for each (i, h) with n = ceil(L_i / partition_size)
+ * partitions, M = max_p max_logits, w_p = exp_sums_p * exp(max_logits_p - M),
+ * out = sum_p w_p tmp_out_p / sum_p w_p (a zero row when n = 0). The merge is an exact
+ * rewriting of the softmax sum; the pages do not describe it.
+ * out: device [B, H, D] T; workspace as written by pkv_paged_attention_decode with the same
+ * partition_size and max_num_partitions = NPmax. */
+pkv_status pkv_paged_attention_reduce(void* out, const float* max_logits,
+                                      const float* exp_sums, const float* tmp_out,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_heads, int32_t head_dim,
+                                      int32_t partition_size, int32_t max_num_partitions,
+                                      pkv_dtype dtype, void* stream);
+
+/* Copy-on-write of shared blocks: for each layer l < num_layers and pair (src, dst) of
+ * block_mapping, block dst of k_caches[l] and v_caches[l] becomes a bit copy of block src
+ * (all Hkv * S * D elements of each). Source: prefix sharing (Hacker News discussion of
+ * PagedAttention, replies on shared prefixes).
+ * k_caches, v_caches: HOST arrays of num_layers device pool pointers (16-byte aligned);
+ * block_mapping: device int64 [num_pairs, 2]; pairs whose src or dst is outside
+ * [0, num_blocks) are skipped. */
+pkv_status pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                           const int64_t* block_mapping, int32_t num_pairs,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, pkv_dtype dtype, void* stream);
+
+/* Bytes of the split-context workspace: 4 * B * H * NPmax * (D + 2); 0 when
+ * partition_size <= 0. Carve it as max_logits | exp_sums | tmp_out in that order. */
+size_t pkv_partition_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                     int32_t max_context_len, int32_t partition_size);
+
+const char* pkv_status_string(pkv_status s);
+int pkv_last_hip_error(void);              /* hipError_t behind the last PKV_ERR_HIP */
+const char* pkv_last_error_message(void);  /* thread-local text of the last failure */
+int pkv_abi_version(void);                 /* 1 */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

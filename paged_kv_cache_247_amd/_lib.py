@@ -1,0 +1,239 @@
+"""ctypes binding of libpagedkv.so: argument marshalling only.
+
+Every function here takes torch tensors that live on the GPU, checks their dtype, shape and
+layout against the C header's contract, and passes raw device pointers, sizes and the current
+HIP stream to the C ABI. All computation happens in the HIP kernels. A non-zero status raises
+PagedKVError. If the library is not built, loading fails loudly: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpagedkv.so")
+
+PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
+_DTYPES = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+
+# Exported symbols and their C prototypes (pagedkv.h).
+_P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "pkv_reshape_and_cache": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "pkv_paged_attention_decode": (_I, [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I,
+                                        _F, _I, _I, _P, _P, _P, _P]),
+    "pkv_paged_attention_decode_with": (_I, [_I, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I,
+                                             _I, _I, _I, _F, _I, _I, _P, _P, _P, _P]),
+    "pkv_paged_attention_reduce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "pkv_copy_blocks": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "pkv_partition_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
+    "pkv_status_string": (ctypes.c_char_p, [_I]),
+    "pkv_last_hip_error": (ctypes.c_int, []),
+    "pkv_last_error_message": (ctypes.c_char_p, []),
+    "pkv_abi_version": (ctypes.c_int, []),
+}
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+_lib = None
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load the built library (once); raises if it is missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is not built: run `python -m paged_kv_cache_247_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load()
+        raise PagedKVError(status, lib.pkv_last_error_message().decode())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping):
+    """Write new K/V rows [T, Hkv, D] into their slots of the pools (pkv_reshape_and_cache)."""
+    _need(k_cache, "k_cache", ndim=4)
+    dt = k_cache.dtype
+    N, Hkv, S, D = k_cache.shape
+    _need(v_cache, "v_cache", dt, 4, k_cache.device)
+    if tuple(v_cache.shape) != (N, Hkv, D, S):
+        raise ValueError(f"v_cache must be [N, Hkv, D, S] = {(N, Hkv, D, S)}")
+    _need(key, "key", dt, 3, k_cache.device)
+    _need(value, "value", dt, 3, k_cache.device)
+    T = key.shape[0]
+    if tuple(key.shape) != (T, Hkv, D) or tuple(value.shape) != (T, Hkv, D):
+        raise ValueError("key/value must be [T, Hkv, D]")
+    _need(slot_mapping, "slot_mapping", torch.int64, 1, k_cache.device)
+    if slot_mapping.shape[0] != T:
+        raise ValueError("slot_mapping must have one slot per token")
+    _check(load().pkv_reshape_and_cache(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(slot_mapping), T, Hkv, D, S, N, _dt(k_cache),
+                                        _stream(k_cache)))
+
+
+def num_partitions(max_context_len: int, partition_size: int) -> int:
+    return -(-int(max_context_len) // int(partition_size)) if partition_size > 0 else 0
+
+
+def partition_workspace(num_seqs, num_heads, head_dim, max_context_len, partition_size,
+                        device):
+    """fp32 (max_logits [B,H,NP], exp_sums [B,H,NP], tmp_out [B,H,NP,D]) carved from one buffer
+    of pkv_partition_workspace_bytes bytes."""
+    NP = num_partitions(max_context_len, partition_size)
+    nbytes = load().pkv_partition_workspace_bytes(num_seqs, num_heads, head_dim,
+                                                  max_context_len, partition_size)
+    n = num_seqs * num_heads * NP
+    assert nbytes == 4 * n * (head_dim + 2)
+    buf = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=device)
+    # tmp_out first keeps it 16-byte aligned whatever n is.
+    tmp_out = buf[:n * head_dim].view(num_seqs, num_heads, NP, head_dim)
+    max_logits = buf[n * head_dim:n * (head_dim + 1)].view(num_seqs, num_heads, NP)
+    exp_sums = buf[n * (head_dim + 1):n * (head_dim + 2)].view(num_seqs, num_heads, NP)
+    return max_logits, exp_sums, tmp_out
+
+
+def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
+                           max_context_len, scale, partition_size=0, workspace=None,
+                           kernel="auto"):
+    """pkv_paged_attention_decode(_with). Single pass writes `out`; with partition_size > 0 it
+    writes only `workspace` = (max_logits, exp_sums, tmp_out)."""
+    _need(q, "q", ndim=3)
+    dt = q.dtype
+    B, H, D = q.shape
+    _need(k_cache, "k_cache", dt, 4, q.device)
+    N, Hkv, S, Dk = k_cache.shape
+    if Dk != D:
+        raise ValueError("head_dim of q and k_cache differ")
+    _need(v_cache, "v_cache", dt, 4, q.device)
+    if tuple(v_cache.shape) != (N, Hkv, D, S):
+        raise ValueError("v_cache must be [N, Hkv, D, S]")
+    _need(block_tables, "block_tables", torch.int32, 2, q.device)
+    _need(context_lens, "context_lens", torch.int32, 1, q.device)
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables/context_lens must have one row per sequence")
+    MB = block_tables.shape[1]
+    ml = es = to = None
+    if partition_size:
+        if workspace is None:
+            raise ValueError("split-context mode needs a workspace")
+        ml, es, to = workspace
+        NP = num_partitions(max_context_len, partition_size)
+        for t, shp in ((ml, (B, H, NP)), (es, (B, H, NP)), (to, (B, H, NP, D))):
+            _need(t, "workspace", torch.float32, len(shp), q.device)
+            if tuple(t.shape) != shp:
+                raise ValueError(f"workspace part must be {shp}, got {tuple(t.shape)}")
+    else:
+        _need(out, "out", dt, 3, q.device)
+        if tuple(out.shape) != (B, H, D):
+            raise ValueError("out must be [B, H, D]")
+    lib = load()
+    _check(lib.pkv_paged_attention_decode_with(
+        KERNELS[kernel], _ptr(out) if not partition_size else None, _ptr(q), _ptr(k_cache),
+        _ptr(v_cache), _ptr(block_tables), MB, _ptr(context_lens), int(max_context_len), B, H,
+        Hkv, D, S, N, float(scale), _dt(q), int(partition_size), _ptr(ml), _ptr(es), _ptr(to),
+        _stream(q)))
+
+
+def paged_attention_reduce(out, workspace, context_lens, partition_size):
+    """pkv_paged_attention_reduce: merge the partitions in `workspace` into `out`."""
+    ml, es, to = workspace
+    _need(out, "out", ndim=3)
+    B, H, D = out.shape
+    NP = ml.shape[2]
+    for t, shp in ((ml, (B, H, NP)), (es, (B, H, NP)), (to, (B, H, NP, D))):
+        _need(t, "workspace", torch.float32, len(shp), out.device)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"workspace part must be {shp}")
+    _need(context_lens, "context_lens", torch.int32, 1, out.device)
+    _check(load().pkv_paged_attention_reduce(_ptr(out), _ptr(ml), _ptr(es), _ptr(to),
+                                             _ptr(context_lens), B, H, D, int(partition_size),
+                                             NP, _dt(out), _stream(out)))
+
+
+def copy_blocks(k_caches, v_caches, block_mapping):
+    """pkv_copy_blocks over every layer: block dst := block src for each (src, dst) row."""
+    if len(k_caches) != len(v_caches) or not k_caches:
+        raise ValueError("need matching non-empty lists of K and V pools")
+    k0 = k_caches[0]
+    _need(k0, "k_caches[0]", ndim=4)
+    N, Hkv, S, D = k0.shape
+    for k, v in zip(k_caches, v_caches):
+        _need(k, "k_cache", k0.dtype, 4, k0.device)
+        _need(v, "v_cache", k0.dtype, 4, k0.device)
+        if tuple(k.shape) != (N, Hkv, S, D) or tuple(v.shape) != (N, Hkv, D, S):
+            raise ValueError("every layer's pools must have the same shape")
+    _need(block_mapping, "block_mapping", torch.int64, 2, k0.device)
+    if block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [M, 2]")
+    nl = len(k_caches)
+    karr = (ctypes.c_void_p * nl)(*[k.data_ptr() for k in k_caches])
+    varr = (ctypes.c_void_p * nl)(*[v.data_ptr() for v in v_caches])
+    _check(load().pkv_copy_blocks(karr, varr, nl, _ptr(block_mapping), block_mapping.shape[0],
+                                  Hkv, D, S, N, _dt(k0), _stream(k0)))
+
+
+def paged_attention(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                    scale, partition_size=0, workspace=None, kernel="auto"):
+    """The whole decode: single pass, or partitions then their merge, on the current stream."""
+    if partition_size:
+        B, H, D = q.shape
+        if workspace is None:
+            workspace = partition_workspace(B, H, D, max_context_len, partition_size, q.device)
+        paged_attention_decode(None, q, k_cache, v_cache, block_tables, context_lens,
+                               max_context_len, scale, partition_size, workspace, kernel)
+        paged_attention_reduce(out, workspace, context_lens, partition_size)
+    else:
+        paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
+                               max_context_len, scale, 0, None, kernel)
+    return out

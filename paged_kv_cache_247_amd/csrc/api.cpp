@@ -1,0 +1,283 @@
+// The C ABI of pagedkv.h: host-side validation of every scalar and pointer, kernel-family
+// choice, grid sizing and launch on the caller's stream. Nothing here allocates.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+#include "pagedkv.h"
+
+namespace {
+
+thread_local int t_last_hip = 0;
+thread_local char t_msg[256] = "";
+
+pkv_status fail(pkv_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(t_msg, sizeof t_msg, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+pkv_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PKV_OK;
+  if (e == hipErrorNotSupported)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: no kernel instantiation for this shape", what);
+  t_last_hip = (int)e;
+  return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return p && ((uintptr_t)p % a) == 0; }
+
+bool valid_dtype(pkv_dtype d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16; }
+
+pkv::Dt to_dt(pkv_dtype d) { return static_cast<pkv::Dt>((int)d); }
+
+// Shape checks shared by every entry point.
+pkv_status check_tile(const char* fn, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, pkv_dtype dtype) {
+  if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID_ARGUMENT, "%s: bad dtype %d", fn, (int)dtype);
+  if (num_kv_heads <= 0) return fail(PKV_ERR_INVALID_ARGUMENT, "%s: num_kv_heads %d", fn, num_kv_heads);
+  if (head_dim <= 0 || block_size <= 0)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: head_dim %d block_size %d", fn, head_dim, block_size);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: head_dim %d (supported: 64, 128)", fn, head_dim);
+  if (block_size != 16 && block_size != 32)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: block_size %d (supported: 16, 32)", fn, block_size);
+  return PKV_OK;
+}
+
+pkv_status decode_impl(pkv_kernel kernel, void* out, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t num_blocks, float scale, pkv_dtype dtype,
+                       int32_t partition_size, float* max_logits, float* exp_sums,
+                       float* tmp_out, void* stream) {
+  const char* fn = "pkv_paged_attention_decode";
+  pkv_status st = check_tile(fn, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARGUMENT, "%s: num_seqs %d", fn, num_seqs);
+  if (num_heads <= 0 || num_heads % num_kv_heads)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: num_heads %d not a positive multiple of num_kv_heads %d",
+                fn, num_heads, num_kv_heads);
+  const int G = num_heads / num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: query group %d (supported: 1, 2, 4, 8, 16)", fn, G);
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: num_blocks %d max_blocks_per_seq %d", fn,
+                num_blocks, max_blocks_per_seq);
+  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: max_context_len %d outside [0, %lld]", fn,
+                max_context_len, (long long)max_blocks_per_seq * block_size);
+  if (!isfinite(scale)) return fail(PKV_ERR_INVALID_ARGUMENT, "%s: scale is not finite", fn);
+  if (partition_size < 0 || (partition_size > 0 && partition_size % block_size))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: partition_size %d is not 0 or a multiple of %d",
+                fn, partition_size, block_size);
+  const bool partial = partition_size > 0;
+  if (partial) {
+    if (!aligned(max_logits, 4) || !aligned(exp_sums, 4) || !aligned(tmp_out, 16))
+      return fail(PKV_ERR_INVALID_ARGUMENT, "%s: partition workspace pointers null or misaligned", fn);
+  } else if (max_logits || exp_sums || tmp_out) {
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: workspace pointers must be NULL in single-pass mode", fn);
+  }
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      (!partial && !aligned(out, 16)) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: a tensor pointer is null or misaligned", fn);
+  bool mfma;
+  switch (kernel) {
+    case PKV_KERNEL_AUTO: mfma = dtype != PKV_F32 && G >= 4; break;
+    case PKV_KERNEL_VALU: mfma = false; break;
+    case PKV_KERNEL_MFMA: mfma = true; break;
+    default: return fail(PKV_ERR_INVALID_ARGUMENT, "%s: bad kernel family %d", fn, (int)kernel);
+  }
+  if (mfma && dtype == PKV_F32)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: the MFMA kernel takes fp16/bf16 only", fn);
+  if (!mfma && G > 8)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: the VALU kernel takes query groups up to 8", fn);
+
+  const int64_t ranges = partial ? ((int64_t)max_context_len + partition_size - 1) / partition_size : 1;
+  const int64_t grid = (int64_t)num_seqs * ranges * num_kv_heads;
+  if (grid > INT32_MAX) return fail(PKV_ERR_INVALID_ARGUMENT, "%s: grid of %lld workgroups", fn, (long long)grid);
+  if (grid == 0) return PKV_OK;
+
+  pkv::DecodeParams p;
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.max_logits = max_logits;
+  p.exp_sums = exp_sums;
+  p.tmp_out = tmp_out;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.range_tokens = partial ? partition_size : max_blocks_per_seq * block_size;
+  p.num_ranges = (int32_t)ranges;
+  p.scale_log2e = scale * pkv::kLog2e;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = mfma ? pkv::launch_decode_mfma(to_dt(dtype), head_dim, block_size, partial, p, s)
+                            : pkv::launch_decode_valu(to_dt(dtype), head_dim, block_size, G, partial, p, s);
+  return hip_status(e, fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cache,
+                                 void* v_cache, const int64_t* slot_mapping,
+                                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks, pkv_dtype dtype,
+                                 void* stream) {
+  const char* fn = "pkv_reshape_and_cache";
+  pkv_status st = check_tile(fn, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PKV_OK) return st;
+  if (num_tokens < 0 || num_blocks <= 0)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: num_tokens %d num_blocks %d", fn, num_tokens, num_blocks);
+  if (num_tokens == 0) return PKV_OK;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(slot_mapping, 8))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: a pointer is null or misaligned", fn);
+  pkv::CacheWriteParams p;
+  p.key = key;
+  p.value = value;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.slot_mapping = slot_mapping;
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = num_kv_heads;
+  p.num_blocks = num_blocks;
+  return hip_status(pkv::launch_reshape_and_cache(to_dt(dtype), head_dim, block_size, p,
+                                                  reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+pkv_status pkv_paged_attention_decode(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t max_context_len, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, pkv_dtype dtype,
+    int32_t partition_size, float* max_logits, float* exp_sums, float* tmp_out, void* stream) {
+  return decode_impl(PKV_KERNEL_AUTO, out, q, k_cache, v_cache, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                     partition_size, max_logits, exp_sums, tmp_out, stream);
+}
+
+pkv_status pkv_paged_attention_decode_with(
+    pkv_kernel kernel, void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t max_context_len, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, pkv_dtype dtype,
+    int32_t partition_size, float* max_logits, float* exp_sums, float* tmp_out,
+    void* stream) {
+  return decode_impl(kernel, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                     context_lens, max_context_len, num_seqs, num_heads, num_kv_heads,
+                     head_dim, block_size, num_blocks, scale, dtype, partition_size,
+                     max_logits, exp_sums, tmp_out, stream);
+}
+
+pkv_status pkv_paged_attention_reduce(void* out, const float* max_logits,
+                                      const float* exp_sums, const float* tmp_out,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_heads, int32_t head_dim,
+                                      int32_t partition_size, int32_t max_num_partitions,
+                                      pkv_dtype dtype, void* stream) {
+  const char* fn = "pkv_paged_attention_reduce";
+  if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID_ARGUMENT, "%s: bad dtype %d", fn, (int)dtype);
+  if (num_seqs < 0 || num_heads <= 0 || partition_size <= 0 || max_num_partitions < 0)
+    return fail(PKV_ERR_INVALID_ARGUMENT,
+                "%s: num_seqs %d num_heads %d partition_size %d max_num_partitions %d", fn,
+                num_seqs, num_heads, partition_size, max_num_partitions);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(head_dim > 0 ? PKV_ERR_UNSUPPORTED : PKV_ERR_INVALID_ARGUMENT,
+                "%s: head_dim %d (supported: 64, 128)", fn, head_dim);
+  if ((int64_t)num_seqs * num_heads > INT32_MAX)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: too many rows", fn);
+  if (num_seqs == 0) return PKV_OK;
+  if (!aligned(out, 16) || !aligned(context_lens, 4) ||
+      (max_num_partitions > 0 &&
+       (!aligned(max_logits, 4) || !aligned(exp_sums, 4) || !aligned(tmp_out, 16))))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: a pointer is null or misaligned", fn);
+  pkv::ReduceParams p;
+  p.out = out;
+  p.max_logits = max_logits;
+  p.exp_sums = exp_sums;
+  p.tmp_out = tmp_out;
+  p.context_lens = context_lens;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.partition_size = partition_size;
+  p.max_num_partitions = max_num_partitions;
+  return hip_status(pkv::launch_reduce(to_dt(dtype), head_dim, p, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+pkv_status pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                           const int64_t* block_mapping, int32_t num_pairs,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, pkv_dtype dtype, void* stream) {
+  const char* fn = "pkv_copy_blocks";
+  pkv_status st = check_tile(fn, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PKV_OK) return st;
+  if (num_layers < 0 || num_pairs < 0 || num_blocks <= 0)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: num_layers %d num_pairs %d num_blocks %d", fn,
+                num_layers, num_pairs, num_blocks);
+  if (num_layers == 0 || num_pairs == 0) return PKV_OK;
+  if (!k_caches || !v_caches || !aligned(block_mapping, 8))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: null pointer array or misaligned mapping", fn);
+  for (int l = 0; l < num_layers; ++l)
+    if (!aligned(k_caches[l], 16) || !aligned(v_caches[l], 16))
+      return fail(PKV_ERR_INVALID_ARGUMENT, "%s: layer %d pool pointer null or misaligned", fn, l);
+  static const int eb[3] = {4, 2, 2};
+  pkv::CopyParams p;
+  p.block_mapping = block_mapping;
+  p.num_pairs = num_pairs;
+  p.num_blocks = num_blocks;
+  p.tile_bytes = (int64_t)num_kv_heads * block_size * head_dim * eb[(int)dtype];
+  for (int l0 = 0; l0 < num_layers; l0 += pkv::kMaxLayersPerLaunch) {
+    const int n = num_layers - l0 < pkv::kMaxLayersPerLaunch ? num_layers - l0 : pkv::kMaxLayersPerLaunch;
+    for (int l = 0; l < n; ++l) {
+      p.k[l] = k_caches[l0 + l];
+      p.v[l] = v_caches[l0 + l];
+    }
+    st = hip_status(pkv::launch_copy_blocks(n, p, reinterpret_cast<hipStream_t>(stream)), fn);
+    if (st != PKV_OK) return st;
+  }
+  return PKV_OK;
+}
+
+size_t pkv_partition_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                     int32_t max_context_len, int32_t partition_size) {
+  if (partition_size <= 0 || num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 ||
+      max_context_len <= 0)
+    return 0;
+  const size_t np = ((size_t)max_context_len + partition_size - 1) / partition_size;
+  return 4 * (size_t)num_seqs * num_heads * np * ((size_t)head_dim + 2);
+}
+
+const char* pkv_status_string(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported shape";
+    case PKV_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int pkv_last_hip_error(void) { return t_last_hip; }
+
+const char* pkv_last_error_message(void) { return t_msg; }
+
+int pkv_abi_version(void) { return 1; }
+
+}  // extern "C"

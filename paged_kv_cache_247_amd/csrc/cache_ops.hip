@@ -1,0 +1,98 @@
+// Cache maintenance kernels: writing each step's new K/V rows into their slots, and
+// copy-on-write of whole blocks.
+//
+// A slot is block_id * S + position: the new token's K/V go to that position of that block
+// (the cache grows by one position per generated token; Qualiteg, "About PagedAttention for LLM
+// serving", the past_key_values loop of "Deepening Our Understanding ..." and item 1-2 on
+// blocks). Requests that share a prefix share its blocks (Hacker News discussion of
+// PagedAttention, replies on shared prefixes); a block is copied before a sequence writes into
+// a shared one.
+#include "kernels.hpp"
+
+namespace pkv {
+namespace {
+
+// One workgroup per new token. K rows are 16-byte vector stores into the [S][D] tile; V
+// elements go to column `pos` of the [D][S] tile.
+template <Dt DT, int D, int S>
+__global__ void __launch_bounds__(256) reshape_and_cache_kernel(const CacheWriteParams a) {
+  using T = typename Elt<DT>::T;
+  constexpr int EB = Elt<DT>::bytes;
+  constexpr int VEC = 16 / EB;
+  const int t = blockIdx.x;
+  const int64_t slot = a.slot_mapping[t];
+  if (slot < 0 || slot >= (int64_t)a.num_blocks * S) return;
+  const int64_t blk = slot / S;
+  const int pos = (int)(slot % S);
+  const int Hkv = a.num_kv_heads;
+
+  const char* key = reinterpret_cast<const char*>(a.key) + (size_t)t * Hkv * D * EB;
+  char* kc = reinterpret_cast<char*>(a.k_cache);
+  for (int v = threadIdx.x; v < Hkv * D / VEC; v += blockDim.x) {
+    const int h = (v * VEC) / D;
+    const int d = (v * VEC) % D;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(key + ((size_t)h * D + d) * EB);
+    *reinterpret_cast<u32x4*>(kc + ((((size_t)blk * Hkv + h) * S + pos) * D + d) * EB) = x;
+  }
+  const T* val = reinterpret_cast<const T*>(a.value) + (size_t)t * Hkv * D;
+  T* vc = reinterpret_cast<T*>(a.v_cache);
+  for (int e = threadIdx.x; e < Hkv * D; e += blockDim.x) {
+    const int h = e / D;
+    const int d = e % D;
+    vc[(((size_t)blk * Hkv + h) * D + d) * S + pos] = val[e];
+  }
+}
+
+// One workgroup per (pair, layer, pool): a block of one pool is one contiguous tile.
+__global__ void __launch_bounds__(256) copy_blocks_kernel(const CopyParams a) {
+  const int pair = blockIdx.x;
+  const int layer = blockIdx.y;
+  const int64_t src = a.block_mapping[2 * pair];
+  const int64_t dst = a.block_mapping[2 * pair + 1];
+  if (src < 0 || dst < 0 || src >= a.num_blocks || dst >= a.num_blocks || src == dst) return;
+  char* base = reinterpret_cast<char*>(blockIdx.z == 0 ? a.k[layer] : a.v[layer]);
+  const u32x4* s = reinterpret_cast<const u32x4*>(base + src * a.tile_bytes);
+  u32x4* d = reinterpret_cast<u32x4*>(base + dst * a.tile_bytes);
+  const int64_t n = a.tile_bytes / 16;
+  for (int64_t e = threadIdx.x; e < n; e += blockDim.x) d[e] = s[e];
+}
+
+template <Dt DT, int D>
+hipError_t write_d(int block_size, const CacheWriteParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)p.num_tokens);
+  switch (block_size) {
+    case 16: reshape_and_cache_kernel<DT, D, 16><<<grid, 256, 0, stream>>>(p); break;
+    case 32: reshape_and_cache_kernel<DT, D, 32><<<grid, 256, 0, stream>>>(p); break;
+    default: return hipErrorNotSupported;
+  }
+  return hipGetLastError();
+}
+
+template <Dt DT>
+hipError_t write_t(int head_dim, int block_size, const CacheWriteParams& p, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return write_d<DT, 64>(block_size, p, stream);
+    case 128: return write_d<DT, 128>(block_size, p, stream);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_reshape_and_cache(Dt dt, int head_dim, int block_size,
+                                    const CacheWriteParams& p, hipStream_t stream) {
+  switch (dt) {
+    case Dt::F32: return write_t<Dt::F32>(head_dim, block_size, p, stream);
+    case Dt::F16: return write_t<Dt::F16>(head_dim, block_size, p, stream);
+    case Dt::BF16: return write_t<Dt::BF16>(head_dim, block_size, p, stream);
+  }
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_copy_blocks(int num_layers, const CopyParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)p.num_pairs, (unsigned)num_layers, 2);
+  copy_blocks_kernel<<<grid, 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

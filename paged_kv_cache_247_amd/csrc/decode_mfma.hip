@@ -1,0 +1,298 @@
+// Paged decode attention with gfx950 matrix cores, for fp16/bf16 when a grouped-query group of
+// G >= 4 query heads shares each kv head: per 32-position chunk the logits are a dense
+// [32 x D] by [D x G] product and the output update a dense [D x 32] by [32 x G] product.
+// The G heads are the 16 columns of v_mfma_f32_16x16x32_{bf16,f16} (G <= 16; unused columns
+// hold zero queries and are never written).
+//
+// The operation is attention over non-contiguous KV-cache blocks (vAttention, section 3.1
+// "Requires re-writing the attention kernel"; grouped-query attention is the case that
+// section singles out), each block reached through the block table (Qualiteg, "About
+// PagedAttention for LLM serving", "There are logical blocks and physical blocks ...") and each
+// sequence using only its own length (same post, item 2-1).
+//
+// Register layouts (lane = 16 r + c, r in 0..3, c in 0..15). For a 16x16x32 product the A
+// operand gives lane (r, c) row c and eight consecutive k values of group r, the B operand
+// column c and the same eight k values, and the accumulator holds rows 4r..4r+3 of column c.
+// Only the pairing of A's and B's k values matters, so k is mapped freely:
+//   logits   S^T[t][h] = sum_d K[t][d] q[h][d]      A = K rows, B = q columns
+//     lane (r, c) loads K row tau = 8(c/4) + 4 gi + (c%4) (gi = 0, 1 picks one of two
+//     products) at d = 32 kk + 8r .. +8, so its accumulator holds positions 8r .. 8r+7 of
+//     head c, in order.
+//   output   O^T[d][h] = sum_t V^T[d][t] P^T[t][h]  A = V^T rows, B = softmax weights
+//     lane (r, c) loads V^T row d = 16 nt + c at positions 8r .. 8r+7 -- 16 contiguous bytes
+//     of the [D][S] tile -- and its B operand is exactly the eight weights it computed.
+//   The accumulator of tile nt holds O^T[16 nt + 4r + i][c]: the head is the lane's own
+//   column, so the online-softmax rescale uses the lane's own running max; no exchange.
+#include "kernels.hpp"
+
+namespace pkv {
+namespace {
+
+template <Dt DT> struct Mfma;
+template <> struct Mfma<Dt::BF16> {
+  using V8 = bf16x8;
+  static __device__ __forceinline__ f32x4 mac(V8 a, V8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ __bf16 narrow(float x) { return (__bf16)x; }
+};
+template <> struct Mfma<Dt::F16> {
+  using V8 = f16x8;
+  static __device__ __forceinline__ f32x4 mac(V8 a, V8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ _Float16 narrow(float x) { return (_Float16)x; }
+};
+
+template <Dt DT, int D, int S, int NW, bool PARTIAL>
+__global__ void __launch_bounds__(NW * 64)
+decode_mfma_kernel(const DecodeParams a) {
+  static_assert(DT == Dt::BF16 || DT == Dt::F16, "16-bit inputs only");
+  constexpr int EB = 2;
+  constexpr int CT = 32;        // positions per chunk
+  constexpr int BPC = CT / S;   // blocks per chunk
+  constexpr int KK = D / 32;    // k-steps of the logits product
+  constexpr int NT = D / 16;    // 16-row tiles of the output product
+  static_assert(BPC == 1 || BPC == 2, "block_size 16 or 32");
+  using M = Mfma<DT>;
+  using V8 = typename M::V8;
+  using T = typename Elt<DT>::T;
+
+  __shared__ float sh_m[NW][16];
+  __shared__ float sh_l[NW][16];
+  __shared__ float sh_acc[NW][16][D];
+
+  const int Hkv = a.num_kv_heads;
+  const int H = a.num_heads;
+  const int G = H / Hkv;
+  const int w = blockIdx.x;
+  const int g = w % Hkv;
+  const int rest = w / Hkv;
+  const int part = rest % a.num_ranges;
+  const int i = rest / a.num_ranges;
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int r = lane >> 4;
+  const int c = lane & 15;
+
+  int L = a.context_lens[i];
+  L = min(max(L, 0), a.max_blocks_per_seq * S);
+  const int start = part * a.range_tokens;
+  if (start >= L) {
+    if (!PARTIAL && part == 0) {
+      T* o = reinterpret_cast<T*>(a.out) + ((size_t)i * H + (size_t)g * G) * D;
+      for (int e = threadIdx.x; e < G * D; e += NW * 64) o[e] = from_f32<DT>(0.0f);
+    }
+    return;
+  }
+  const int end = min(start + a.range_tokens, L);
+  const int nch = (end - start + CT - 1) / CT;
+  const int per = (nch + NW - 1) / NW;
+  const int ch_lo = wave * per;
+  const int ch_hi = min(ch_lo + per, nch);
+  const int blk_end = (end + S - 1) / S;  // first logical block past the range
+
+  // q columns: lane (r, c) holds head c (zero beyond the group) at d = 32 kk + 8r .. +8.
+  V8 qb[KK];
+  {
+    const char* qp = reinterpret_cast<const char*>(a.q) +
+                     (((size_t)i * H + (size_t)g * G + c) * D + 8 * r) * EB;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (c < G) v = *reinterpret_cast<const u32x4*>(qp + kk * 64);
+      qb[kk] = __builtin_bit_cast(V8, v);
+    }
+  }
+
+  const int32_t* bt = a.block_tables + (size_t)i * a.max_blocks_per_seq;
+  const size_t tile_bytes = (size_t)S * D * EB;
+  const size_t id_stride = (size_t)Hkv * tile_bytes;
+  const char* kpool = reinterpret_cast<const char*>(a.k_cache) + (size_t)g * tile_bytes;
+  const char* vpool = reinterpret_cast<const char*>(a.v_cache) + (size_t)g * tile_bytes;
+  // K: row tau = 8(c/4) + (c%4) (+4 for the second product) of block tau / S.
+  const int k_tau = 8 * (c >> 2) + (c & 3);
+  const int k_blk = k_tau / S;
+  const int k_off = (k_tau % S) * D * EB + r * 16;  // + gi * 4 rows + kk * 64
+  // V^T: row d = 16 nt + c, positions 8r .. 8r+7 of block 8r / S.
+  const int v_blk = (8 * r) / S;
+  const int v_off = c * S * EB + ((8 * r) % S) * EB;  // + nt * 16 rows
+
+  struct Regs {
+    u32x4 k[2][KK];
+    u32x4 v[NT];
+  };
+
+  auto load = [&](int n, Regs& R) {
+    const int b0 = start / S + n * BPC;
+    int id0 = bt[b0];
+    id0 = min(max(id0, 0), a.num_blocks - 1);
+    int id1 = id0;
+    if constexpr (BPC == 2) {
+      if (b0 + 1 < blk_end) {
+        id1 = bt[b0 + 1];
+        id1 = min(max(id1, 0), a.num_blocks - 1);
+      }
+    }
+    const char* kt = kpool + (size_t)(k_blk ? id1 : id0) * id_stride + k_off;
+    const char* vt = vpool + (size_t)(v_blk ? id1 : id0) * id_stride + v_off;
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        R.k[gi][kk] = *reinterpret_cast<const u32x4*>(kt + gi * 4 * D * EB + kk * 64);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      R.v[nt] = *reinterpret_cast<const u32x4*>(vt + nt * 16 * S * EB);
+  };
+
+  float m = -INFINITY, l = 0.0f;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](int n, Regs& R) {
+    f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      s0 = M::mac(__builtin_bit_cast(V8, R.k[0][kk]), qb[kk], s0);
+      s1 = M::mac(__builtin_bit_cast(V8, R.k[1][kk]), qb[kk], s1);
+    }
+    const int pos0 = start + n * CT + 8 * r;  // position of this lane's first logit
+    float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      sv[j] = (pos0 + j < end) ? sv[j] * a.scale_log2e : -INFINITY;
+      mx = fmaxf(mx, sv[j]);
+    }
+    mx = across16(mx, OpMax());
+    mx = across32(mx, OpMax());
+    const float mnew = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    m = mnew;
+    V8 pb;
+    float psum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pb[j] = M::narrow(__builtin_amdgcn_exp2f(sv[j] - mnew));
+      psum += (float)pb[j];  // the sum matches the weights the product uses
+    }
+    l = fmaf(l, alpha, psum);
+    // Positions past the end may hold anything (even NaN): zero them, 0 * NaN is NaN.
+    const int nv = end - pos0;
+    if (nv < 8) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t keep = (2 * q + 1 < nv) ? 0xffffffffu : (2 * q < nv) ? 0x0000ffffu : 0u;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) R.v[nt][q] &= keep;
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      acc[nt] *= alpha;
+      acc[nt] = M::mac(__builtin_bit_cast(V8, R.v[nt]), pb, acc[nt]);
+    }
+  };
+
+  if (ch_lo < ch_hi) {
+    Regs A, B;
+    load(ch_lo, A);
+    int n = ch_lo;
+    while (true) {
+      if (n + 1 < ch_hi) load(n + 1, B);
+      compute(n, A);
+      if (++n >= ch_hi) break;
+      if (n + 1 < ch_hi) load(n + 1, A);
+      compute(n, B);
+      if (++n >= ch_hi) break;
+    }
+  }
+
+  l = across16(l, OpAdd());
+  l = across32(l, OpAdd());
+  if (c < G) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sh_acc[wave][c][16 * nt + 4 * r + e] = acc[nt][e];
+    if (r == 0) {
+      sh_m[wave][c] = m;
+      sh_l[wave][c] = l;
+    }
+  }
+  __syncthreads();
+
+  for (int e = threadIdx.x; e < G * D; e += NW * 64) {
+    const int h = e / D;
+    const int d = e % D;
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) Mx = fmaxf(Mx, sh_m[v][h]);
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const float f = __builtin_amdgcn_exp2f(sh_m[v][h] - Mx);
+      num = fmaf(f, sh_acc[v][h][d], num);
+      den = fmaf(f, sh_l[v][h], den);
+    }
+    const float o = num / den;
+    const size_t row = (size_t)i * H + (size_t)g * G + h;
+    if constexpr (PARTIAL) {
+      const size_t rec = row * a.num_ranges + part;
+      a.tmp_out[rec * D + d] = o;
+      if (d == 0) {
+        a.max_logits[rec] = Mx * kLn2;
+        a.exp_sums[rec] = den;
+      }
+    } else {
+      reinterpret_cast<T*>(a.out)[row * D + d] = from_f32<DT>(o);
+    }
+  }
+}
+
+constexpr int kMfmaWaves = 4;
+
+template <Dt DT, int D, int S>
+hipError_t launch_s(bool partial, const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)p.num_seqs * p.num_ranges * p.num_kv_heads);
+  const dim3 block(kMfmaWaves * 64);
+  if (partial)
+    decode_mfma_kernel<DT, D, S, kMfmaWaves, true><<<grid, block, 0, stream>>>(p);
+  else
+    decode_mfma_kernel<DT, D, S, kMfmaWaves, false><<<grid, block, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+template <Dt DT, int D>
+hipError_t launch_d(int block_size, bool partial, const DecodeParams& p, hipStream_t stream) {
+  switch (block_size) {
+    case 16: return launch_s<DT, D, 16>(partial, p, stream);
+    case 32: return launch_s<DT, D, 32>(partial, p, stream);
+    default: return hipErrorNotSupported;
+  }
+}
+
+template <Dt DT>
+hipError_t launch_t(int head_dim, int block_size, bool partial, const DecodeParams& p,
+                    hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_d<DT, 64>(block_size, partial, p, stream);
+    case 128: return launch_d<DT, 128>(block_size, partial, p, stream);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(Dt dt, int head_dim, int block_size, bool partial,
+                              const DecodeParams& p, hipStream_t stream) {
+  switch (dt) {
+    case Dt::F16: return launch_t<Dt::F16>(head_dim, block_size, partial, p, stream);
+    case Dt::BF16: return launch_t<Dt::BF16>(head_dim, block_size, partial, p, stream);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace pkv

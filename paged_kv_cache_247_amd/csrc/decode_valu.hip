@@ -1,0 +1,294 @@
+// Paged decode attention on the vector ALUs (fp32, and fp16/bf16 when the query group is too
+// small for a dense product). One workgroup of NW waves owns one (sequence, kv head, range)
+// unit; each wave walks a contiguous run of the range's blocks with an online softmax, and the
+// waves merge their (max, sum, accumulator) states through LDS at the end.
+//
+// The operation is attention over non-contiguous KV-cache blocks (vAttention, section 3.1
+// "Requires re-writing the attention kernel"): each block is found through the sequence's
+// block table (Qualiteg, "About PagedAttention for LLM serving", "There are logical blocks
+// and physical blocks, and the two are linked by a block table"), and each sequence uses
+// only its own length, with no padding (same post, item 2-1).
+//
+// Lane geometry for a K tile [S][D] of a (block, kv head): a token row is LPR lanes x 16
+// bytes, so one wave load covers ROWS = 64 / LPR rows; lane (r, c) with r = lane / LPR and
+// c = lane % LPR owns positions r*TPL .. r*TPL+TPL-1 of every block and the 16-byte column
+// piece c of the K row. For the V^T tile [D][S] the same lane reads, for each of its VEC
+// head-dim rows d = c + LPR*y, the TPL contiguous positions it owns; so the softmax weights a
+// lane needs for P.V are the ones it computed itself, with no exchange.
+#include "kernels.hpp"
+
+namespace pkv {
+namespace {
+
+template <Dt DT, int D, int S, int G, int NW, bool PARTIAL>
+__global__ void __launch_bounds__(NW * 64)
+decode_valu_kernel(const DecodeParams a) {
+  constexpr int EB = Elt<DT>::bytes;
+  constexpr int VEC = 16 / EB;   // elements per 16-byte piece
+  constexpr int LPR = D / VEC;   // lanes per K row
+  constexpr int ROWS = 64 / LPR; // K rows per wave load
+  constexpr int TPL = S / ROWS;  // positions per lane per block
+  constexpr int VB = TPL * EB;   // bytes per lane per V^T row
+  constexpr int VW = VB / 4;     // 32-bit words per lane per V^T row
+  static_assert(LPR >= 8 && LPR <= 32 && TPL >= 1, "unsupported head_dim/block_size/dtype");
+  using T = typename Elt<DT>::T;
+
+  __shared__ float sh_m[NW][G];
+  __shared__ float sh_l[NW][G];
+  __shared__ float sh_acc[NW][G][D];
+
+  const int Hkv = a.num_kv_heads;
+  const int H = a.num_heads;
+  const int w = blockIdx.x;
+  const int g = w % Hkv;  // consecutive workgroups take different kv heads (XCD round robin)
+  const int rest = w / Hkv;
+  const int part = rest % a.num_ranges;
+  const int i = rest / a.num_ranges;
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int r = lane / LPR;
+  const int c = lane % LPR;
+
+  int L = a.context_lens[i];
+  L = min(max(L, 0), a.max_blocks_per_seq * S);
+  const int start = part * a.range_tokens;
+  if (start >= L) {
+    if (!PARTIAL && part == 0) {
+      T* o = reinterpret_cast<T*>(a.out) + ((size_t)i * H + (size_t)g * G) * D;
+      for (int e = threadIdx.x; e < G * D; e += NW * 64) o[e] = from_f32<DT>(0.0f);
+    }
+    return;
+  }
+  const int end = min(start + a.range_tokens, L);
+  const int blk_lo = start / S;
+  const int blk_hi = (end + S - 1) / S;
+  const int per = (blk_hi - blk_lo + NW - 1) / NW;
+  const int my_lo = blk_lo + wave * per;
+  const int my_hi = min(my_lo + per, blk_hi);
+
+  // This lane's 16-byte piece of q for every head of the group, widened to fp32.
+  float qf[G][VEC];
+  {
+    const char* qb = reinterpret_cast<const char*>(a.q) +
+                     ((size_t)i * H + (size_t)g * G) * D * EB + (size_t)c * 16;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      uint32_t wq[4];
+      load_words<16>(qb + (size_t)h * D * EB, wq);
+      unpack_words<DT, 4>(wq, qf[h]);
+    }
+  }
+
+  float m[G], l[G], acc[G][VEC];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.0f;
+#pragma unroll
+    for (int y = 0; y < VEC; ++y) acc[h][y] = 0.0f;
+  }
+
+  const int32_t* bt = a.block_tables + (size_t)i * a.max_blocks_per_seq;
+  const size_t tile_bytes = (size_t)S * D * EB;
+  const size_t id_stride = (size_t)Hkv * tile_bytes;
+  const char* kpool = reinterpret_cast<const char*>(a.k_cache) + (size_t)g * tile_bytes;
+  const char* vpool = reinterpret_cast<const char*>(a.v_cache) + (size_t)g * tile_bytes;
+  const int k_off = (r * TPL) * D * EB + c * 16;   // + x * D * EB
+  const int v_off = c * S * EB + r * TPL * EB;     // + y * LPR * S * EB
+
+  struct Regs {
+    uint32_t k[TPL][4];
+    uint32_t v[VEC][VW];
+  };
+
+  auto load = [&](int b, Regs& R) {
+    int id = bt[b];
+    id = min(max(id, 0), a.num_blocks - 1);
+    const char* kt = kpool + (size_t)id * id_stride + k_off;
+    const char* vt = vpool + (size_t)id * id_stride + v_off;
+#pragma unroll
+    for (int x = 0; x < TPL; ++x) load_words<16>(kt + x * D * EB, R.k[x]);
+#pragma unroll
+    for (int y = 0; y < VEC; ++y) load_words<VB>(vt + y * LPR * S * EB, R.v[y]);
+  };
+
+  auto compute = [&](int b, const Regs& R) {
+    float s[TPL][G];
+#pragma unroll
+    for (int x = 0; x < TPL; ++x) {
+      float kf[VEC];
+      unpack_words<DT, 4>(R.k[x], kf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float t = 0.0f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) t = fmaf(qf[h][e], kf[e], t);
+        s[x][h] = t;
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < TPL; ++x)
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[x][h] = group_reduce<LPR>(s[x][h], OpAdd());
+
+    const int pos0 = b * S + r * TPL;
+    float mx[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      mx[h] = -INFINITY;
+#pragma unroll
+      for (int x = 0; x < TPL; ++x) {
+        s[x][h] = (pos0 + x < end) ? s[x][h] * a.scale_log2e : -INFINITY;
+        mx[h] = fmaxf(mx[h], s[x][h]);
+      }
+      mx[h] = cross_group_reduce<LPR>(mx[h], OpMax());
+      const float mnew = fmaxf(m[h], mx[h]);
+      const float alpha = __builtin_amdgcn_exp2f(m[h] - mnew);
+      m[h] = mnew;
+      l[h] *= alpha;
+#pragma unroll
+      for (int y = 0; y < VEC; ++y) acc[h][y] *= alpha;
+#pragma unroll
+      for (int x = 0; x < TPL; ++x) {
+        s[x][h] = __builtin_amdgcn_exp2f(s[x][h] - mnew);
+        l[h] += s[x][h];
+      }
+    }
+    const bool tail = (b + 1) * S > end;
+#pragma unroll
+    for (int y = 0; y < VEC; ++y) {
+      float vf[TPL];
+      unpack_words<DT, VW>(R.v[y], vf);
+      if (tail) {
+#pragma unroll
+        for (int x = 0; x < TPL; ++x) vf[x] = (pos0 + x < end) ? vf[x] : 0.0f;
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int x = 0; x < TPL; ++x) acc[h][y] = fmaf(s[x][h], vf[x], acc[h][y]);
+    }
+  };
+
+  if (my_lo < my_hi) {
+    Regs A, B;
+    load(my_lo, A);
+    int b = my_lo;
+    while (true) {
+      if (b + 1 < my_hi) load(b + 1, B);
+      compute(b, A);
+      if (++b >= my_hi) break;
+      if (b + 1 < my_hi) load(b + 1, A);
+      compute(b, B);
+      if (++b >= my_hi) break;
+    }
+  }
+
+  // Sum each lane's positions over the row groups (lanes that share c hold the same columns).
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    l[h] = cross_group_reduce<LPR>(l[h], OpAdd());
+#pragma unroll
+    for (int y = 0; y < VEC; ++y) acc[h][y] = cross_group_reduce<LPR>(acc[h][y], OpAdd());
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int y = 0; y < VEC; ++y) sh_acc[wave][h][c + LPR * y] = acc[h][y];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      sh_m[wave][h] = m[h];
+      sh_l[wave][h] = l[h];
+    }
+  }
+  __syncthreads();
+
+  // Merge the waves: M = max m_w, weights 2^(m_w - M) (a wave without blocks has m = -inf).
+  for (int e = threadIdx.x; e < G * D; e += NW * 64) {
+    const int h = e / D;
+    const int d = e % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) M = fmaxf(M, sh_m[v][h]);
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const float f = __builtin_amdgcn_exp2f(sh_m[v][h] - M);
+      num = fmaf(f, sh_acc[v][h][d], num);
+      den = fmaf(f, sh_l[v][h], den);
+    }
+    const float o = num / den;
+    const size_t row = (size_t)i * H + (size_t)g * G + h;
+    if constexpr (PARTIAL) {
+      const size_t rec = row * a.num_ranges + part;
+      a.tmp_out[rec * D + d] = o;
+      if (d == 0) {
+        a.max_logits[rec] = M * kLn2;
+        a.exp_sums[rec] = den;
+      }
+    } else {
+      reinterpret_cast<T*>(a.out)[row * D + d] = from_f32<DT>(o);
+    }
+  }
+}
+
+constexpr int kValuWaves = 4;
+
+template <Dt DT, int D, int S, int G>
+hipError_t launch_g(bool partial, const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)p.num_seqs * p.num_ranges * p.num_kv_heads);
+  const dim3 block(kValuWaves * 64);
+  if (partial)
+    decode_valu_kernel<DT, D, S, G, kValuWaves, true><<<grid, block, 0, stream>>>(p);
+  else
+    decode_valu_kernel<DT, D, S, G, kValuWaves, false><<<grid, block, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+template <Dt DT, int D, int S>
+hipError_t launch_s(int group, bool partial, const DecodeParams& p, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_g<DT, D, S, 1>(partial, p, stream);
+    case 2: return launch_g<DT, D, S, 2>(partial, p, stream);
+    case 4: return launch_g<DT, D, S, 4>(partial, p, stream);
+    case 8: return launch_g<DT, D, S, 8>(partial, p, stream);
+    default: return hipErrorNotSupported;
+  }
+}
+
+template <Dt DT, int D>
+hipError_t launch_d(int block_size, int group, bool partial, const DecodeParams& p,
+                    hipStream_t stream) {
+  switch (block_size) {
+    case 16: return launch_s<DT, D, 16>(group, partial, p, stream);
+    case 32: return launch_s<DT, D, 32>(group, partial, p, stream);
+    default: return hipErrorNotSupported;
+  }
+}
+
+template <Dt DT>
+hipError_t launch_t(int head_dim, int block_size, int group, bool partial,
+                    const DecodeParams& p, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_d<DT, 64>(block_size, group, partial, p, stream);
+    case 128: return launch_d<DT, 128>(block_size, group, partial, p, stream);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_valu(Dt dt, int head_dim, int block_size, int group, bool partial,
+                              const DecodeParams& p, hipStream_t stream) {
+  switch (dt) {
+    case Dt::F32: return launch_t<Dt::F32>(head_dim, block_size, group, partial, p, stream);
+    case Dt::F16: return launch_t<Dt::F16>(head_dim, block_size, group, partial, p, stream);
+    case Dt::BF16: return launch_t<Dt::BF16>(head_dim, block_size, group, partial, p, stream);
+  }
+  return hipErrorNotSupported;
+}
+
+}  // namespace pkv

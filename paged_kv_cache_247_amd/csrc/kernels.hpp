@@ -1,0 +1,79 @@
+// Internal launcher interface between the C ABI (api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace pkv {
+
+// Arguments of one decode launch. A work unit is (sequence i, kv head g, range p) where range
+// p covers positions [p * range_tokens, (p + 1) * range_tokens) of the sequence; single-pass
+// mode uses one range of max_blocks_per_seq * block_size positions.
+struct DecodeParams {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* max_logits;
+  float* exp_sums;
+  float* tmp_out;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks_per_seq;
+  int32_t num_blocks;
+  int32_t range_tokens;
+  int32_t num_ranges;
+  float scale_log2e;
+};
+
+struct ReduceParams {
+  void* out;
+  const float* max_logits;
+  const float* exp_sums;
+  const float* tmp_out;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t partition_size;
+  int32_t max_num_partitions;
+};
+
+constexpr int kMaxLayersPerLaunch = 32;
+
+struct CopyParams {
+  void* k[kMaxLayersPerLaunch];
+  void* v[kMaxLayersPerLaunch];
+  const int64_t* block_mapping;
+  int32_t num_pairs;
+  int32_t num_blocks;
+  int64_t tile_bytes;  // Hkv * S * D * elt: one block of one pool
+};
+
+struct CacheWriteParams {
+  const void* key;
+  const void* value;
+  void* k_cache;
+  void* v_cache;
+  const int64_t* slot_mapping;
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+};
+
+// Each returns hipSuccess or the launch error; hipErrorNotSupported if no instantiation
+// matches (the C ABI validates shapes before calling, so that is a library bug).
+hipError_t launch_decode_valu(Dt dt, int head_dim, int block_size, int group, bool partial,
+                              const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_mfma(Dt dt, int head_dim, int block_size, bool partial,
+                              const DecodeParams& p, hipStream_t stream);
+hipError_t launch_reduce(Dt dt, int head_dim, const ReduceParams& p, hipStream_t stream);
+hipError_t launch_reshape_and_cache(Dt dt, int head_dim, int block_size,
+                                    const CacheWriteParams& p, hipStream_t stream);
+hipError_t launch_copy_blocks(int num_layers, const CopyParams& p, hipStream_t stream);
+
+}  // namespace pkv

@@ -329,13 +329,16 @@ def generate(cfg: Config, poison: str = "nan", keep_logical: bool = False,
     k_cache[blk, :, slot_off, :] = ks[row_of[place]]
     v_cache[blk, :, :, slot_off] = vs[row_of[place]]
 
-    # Newest token of each sequence: written by reshape_and_cache during the step.
-    last_rows = row_of[newest]
-    key = np.ascontiguousarray(ks[last_rows])
-    value = np.ascontiguousarray(vs[last_rows])
-    lp = L.astype(np.int64) - 1
-    slot_mapping = (tables[np.arange(B), lp // S].astype(np.int64) * S + lp % S)
-    if prefix and np.any(lp < cfg.prefix_len):
+    # Newest token of each sequence: written by reshape_and_cache during the step. A sequence
+    # with an empty context has none: its slot is -1 (skipped) and its rows are zero.
+    has = L > 0
+    key = np.zeros((B, Hkv, D), dtype=ks.dtype)
+    value = np.zeros((B, Hkv, D), dtype=vs.dtype)
+    key[has] = ks[row_of[newest]]
+    value[has] = vs[row_of[newest]]
+    lp = np.maximum(L.astype(np.int64) - 1, 0)
+    slot_mapping = np.where(has, tables[np.arange(B), lp // S].astype(np.int64) * S + lp % S, -1)
+    if prefix and np.any(L.astype(np.int64) - 1 < cfg.prefix_len):
         raise ValueError("prefix configs need a non-empty suffix")
 
     wl = Workload(cfg=cfg, context_lens=L, block_tables=tables,

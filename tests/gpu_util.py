@@ -1,0 +1,92 @@
+"""Helpers for the GPU parity tests: move a workload to the device, run one step through the
+C ABI, and compute the oracle's expected values on the host."""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_cache_247_amd as pk
+
+TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2}  # max |gpu - oracle|, fp32 accumulation
+
+
+def to_dev(a: np.ndarray, dtype: str | None = None) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def to_host(x: torch.Tensor, dtype: str) -> np.ndarray:
+    x = x.detach().cpu().contiguous()
+    if dtype == "bf16":
+        return x.view(torch.int16).numpy().view(np.uint16)
+    return x.numpy()
+
+
+def bits(a: np.ndarray) -> np.ndarray:
+    """Raw bit pattern view for bit-exact comparisons (NaN payloads included)."""
+    return a.view({2: np.uint16, 4: np.uint32, 8: np.uint64}[a.dtype.itemsize])
+
+
+@dataclasses.dataclass
+class Dev:
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    bt: torch.Tensor
+    bt_before: torch.Tensor
+    lens: torch.Tensor
+    key: torch.Tensor
+    value: torch.Tensor
+    slots: torch.Tensor
+    mapping: torch.Tensor
+
+
+def upload(wl) -> Dev:
+    dt = wl.cfg.dtype
+    return Dev(q=to_dev(wl.q, dt), k=to_dev(wl.k_cache, dt), v=to_dev(wl.v_cache, dt),
+               bt=to_dev(wl.block_tables), bt_before=to_dev(wl.block_tables_before),
+               lens=to_dev(wl.context_lens), key=to_dev(wl.key, dt),
+               value=to_dev(wl.value, dt), slots=to_dev(wl.slot_mapping),
+               mapping=to_dev(wl.block_mapping.reshape(-1, 2)))
+
+
+def run_step(dev: Dev, wl, kernel="auto", partition_size=None, tables=None, copy=True):
+    """copy_blocks (if the workload has pairs) -> reshape_and_cache -> decode (+ reduce)."""
+    c = wl.cfg
+    P = c.partition_size if partition_size is None else partition_size
+    if copy and len(wl.block_mapping):
+        pk.copy_blocks([dev.k], [dev.v], dev.mapping)
+    pk.reshape_and_cache(dev.key, dev.value, dev.k, dev.v, dev.slots)
+    out = torch.full((c.num_seqs, c.num_heads, c.head_dim), float("nan"),
+                     dtype=TORCH_DT[c.dtype], device="cuda")
+    pk.paged_attention(out, dev.q, dev.k, dev.v, dev.bt if tables is None else tables, dev.lens,
+                       wl.max_context_len, c.scale, P, kernel=kernel)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_pools(wl, copy=True):
+    c = wl.cfg
+    kc, vc = oracle.write_cache(wl.k_cache, wl.v_cache, wl.key, wl.value, wl.slot_mapping,
+                                c.block_size)
+    if copy and len(wl.block_mapping):
+        (kc,), (vc,) = oracle.copy_blocks([kc], [vc], wl.block_mapping)
+    return kc, vc
+
+
+def oracle_out(wl, seqs=None, pools=None):
+    c = wl.cfg
+    kc, vc = pools if pools is not None else oracle_pools(wl)
+    idx = np.arange(c.num_seqs) if seqs is None else np.asarray(seqs)
+    return oracle.decode(wl.q[idx], kc, vc, wl.block_tables[idx], wl.context_lens[idx], c.scale,
+                         c.num_kv_heads, c.dtype)
+
+
+def out_f64(out: torch.Tensor) -> np.ndarray:
+    return out.detach().float().cpu().numpy().astype(np.float64)
