@@ -140,10 +140,9 @@ decode_mfma_kernel(const DecodeParams a) {
     for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        R.k[gi][kk] = *reinterpret_cast<const u32x4*>(kt + gi * 4 * D * EB + kk * 64);
+        R.k[gi][kk] = load_kv<u32x4>(kt + gi * 4 * D * EB + kk * 64);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      R.v[nt] = *reinterpret_cast<const u32x4*>(vt + nt * 16 * S * EB);
+    for (int nt = 0; nt < NT; ++nt) R.v[nt] = load_kv<u32x4>(vt + nt * 16 * S * EB);
   };
 
   float m = -INFINITY, l = 0.0f;

@@ -73,8 +73,8 @@ decode_valu_kernel(const DecodeParams a) {
                      ((size_t)i * H + (size_t)g * G) * D * EB + (size_t)c * 16;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      uint32_t wq[4];
-      load_words<16>(qb + (size_t)h * D * EB, wq);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qb + (size_t)h * D * EB);
+      const uint32_t wq[4] = {v.x, v.y, v.z, v.w};
       unpack_words<DT, 4>(wq, qf[h]);
     }
   }

@@ -13,7 +13,8 @@ namespace {
 template <Dt DT, int D>
 __global__ void __launch_bounds__(64) reduce_kernel(const ReduceParams a) {
   using T = typename Elt<DT>::T;
-  constexpr int PER = D / 64;
+  constexpr int PER = D / 64;  // output columns per lane
+  constexpr int U = 8;         // partition rows in flight
   const int H = a.num_heads;
   const int i = blockIdx.x / H;
   const int h = blockIdx.x % H;
@@ -31,8 +32,9 @@ __global__ void __launch_bounds__(64) reduce_kernel(const ReduceParams a) {
   const size_t rec0 = ((size_t)i * H + h) * a.max_num_partitions;
   const float* ml = a.max_logits + rec0;
   const float* es = a.exp_sums + rec0;
-  const float* to = a.tmp_out + rec0 * D;
+  const float* to = a.tmp_out + rec0 * D + lane;
 
+  // Lane p handles partition p (of each group of 64): M and the weight total first.
   float M = -INFINITY;
   for (int p = lane; p < n; p += 64) M = fmaxf(M, ml[p]);
   M = group_reduce<64>(M, OpMax());
@@ -43,10 +45,31 @@ __global__ void __launch_bounds__(64) reduce_kernel(const ReduceParams a) {
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
-  for (int p = 0; p < n; ++p) {
-    const float wp = es[p] * __builtin_amdgcn_exp2f((ml[p] - M) * kLog2e) / den;
+  for (int p0 = 0; p0 < n; p0 += 64) {
+    const int cnt = min(64, n - p0);
+    // Normalised weight of this lane's partition; w / den is exactly 1 for a lone partition.
+    float w = 0.0f;
+    if (lane < cnt) w = es[p0 + lane] * __builtin_amdgcn_exp2f((ml[p0 + lane] - M) * kLog2e) / den;
+    const float* row = to + (size_t)p0 * D;
+    int p = 0;
+    for (; p + U <= cnt; p += U) {
+      float t[U][PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = fmaf(wp, to[(size_t)p * D + lane + 64 * e], acc[e]);
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) t[u][e] = row[(size_t)(p + u) * D + 64 * e];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float wp = bits_f((uint32_t)__builtin_amdgcn_readlane((int)f_bits(w), p + u));
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(wp, t[u][e], acc[e]);
+      }
+    }
+    for (; p < cnt; ++p) {
+      const float wp = bits_f((uint32_t)__builtin_amdgcn_readlane((int)f_bits(w), p));
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = fmaf(wp, row[(size_t)p * D + 64 * e], acc[e]);
+    }
   }
 #pragma unroll
   for (int e = 0; e < PER; ++e) o[lane + 64 * e] = from_f32<DT>(acc[e]);
