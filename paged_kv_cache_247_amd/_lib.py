@@ -23,10 +23,10 @@ _DTYPES = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_B
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "pkv_reshape_and_cache": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
-    "pkv_paged_attention_decode": (_I, [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I,
-                                        _F, _I, _I, _P, _P, _P, _P]),
-    "pkv_paged_attention_decode_with": (_I, [_I, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I,
-                                             _I, _I, _I, _F, _I, _I, _P, _P, _P, _P]),
+    "pkv_paged_attention_decode": (_I, [_P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I,
+                                        _I, _F, _I, _I, _P, _P, _P, _P]),
+    "pkv_paged_attention_decode_with": (_I, [_I, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I,
+                                             _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P]),
     "pkv_paged_attention_reduce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pkv_copy_blocks": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pkv_partition_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
@@ -145,9 +145,10 @@ def partition_workspace(num_seqs, num_heads, head_dim, max_context_len, partitio
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
                            max_context_len, scale, partition_size=0, workspace=None,
-                           kernel="auto"):
+                           kernel="auto", work_order=None):
     """pkv_paged_attention_decode(_with). Single pass writes `out`; with partition_size > 0 it
-    writes only `workspace` = (max_logits, exp_sums, tmp_out)."""
+    writes only `workspace` = (max_logits, exp_sums, tmp_out). work_order: optional device int32
+    [B] dispatch order of the sequences (longest first shortens the tail)."""
     _need(q, "q", ndim=3)
     dt = q.dtype
     B, H, D = q.shape
@@ -162,6 +163,10 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     _need(context_lens, "context_lens", torch.int32, 1, q.device)
     if block_tables.shape[0] != B or context_lens.shape[0] != B:
         raise ValueError("block_tables/context_lens must have one row per sequence")
+    if work_order is not None:
+        _need(work_order, "work_order", torch.int32, 1, q.device)
+        if work_order.shape[0] != B:
+            raise ValueError("work_order must have one entry per sequence")
     MB = block_tables.shape[1]
     ml = es = to = None
     if partition_size:
@@ -180,7 +185,8 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     lib = load()
     _check(lib.pkv_paged_attention_decode_with(
         KERNELS[kernel], _ptr(out) if not partition_size else None, _ptr(q), _ptr(k_cache),
-        _ptr(v_cache), _ptr(block_tables), MB, _ptr(context_lens), int(max_context_len), B, H,
+        _ptr(v_cache), _ptr(block_tables), MB, _ptr(context_lens), _ptr(work_order),
+        int(max_context_len), B, H,
         Hkv, D, S, N, float(scale), _dt(q), int(partition_size), _ptr(ml), _ptr(es), _ptr(to),
         _stream(q)))
 
@@ -224,16 +230,17 @@ def copy_blocks(k_caches, v_caches, block_mapping):
 
 
 def paged_attention(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
-                    scale, partition_size=0, workspace=None, kernel="auto"):
+                    scale, partition_size=0, workspace=None, kernel="auto", work_order=None):
     """The whole decode: single pass, or partitions then their merge, on the current stream."""
     if partition_size:
         B, H, D = q.shape
         if workspace is None:
             workspace = partition_workspace(B, H, D, max_context_len, partition_size, q.device)
         paged_attention_decode(None, q, k_cache, v_cache, block_tables, context_lens,
-                               max_context_len, scale, partition_size, workspace, kernel)
+                               max_context_len, scale, partition_size, workspace, kernel,
+                               work_order)
         paged_attention_reduce(out, workspace, context_lens, partition_size)
     else:
         paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
-                               max_context_len, scale, 0, None, kernel)
+                               max_context_len, scale, 0, None, kernel, work_order)
     return out

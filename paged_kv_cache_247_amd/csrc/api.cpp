@@ -54,7 +54,7 @@ pkv_status check_tile(const char* fn, int32_t num_kv_heads, int32_t head_dim,
 pkv_status decode_impl(pkv_kernel kernel, void* out, const void* q, const void* k_cache,
                        const void* v_cache, const int32_t* block_tables,
                        int32_t max_blocks_per_seq, const int32_t* context_lens,
-                       int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                       const int32_t* work_order, int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                        int32_t num_blocks, float scale, pkv_dtype dtype,
                        int32_t partition_size, float* max_logits, float* exp_sums,
@@ -87,7 +87,8 @@ pkv_status decode_impl(pkv_kernel kernel, void* out, const void* q, const void* 
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: workspace pointers must be NULL in single-pass mode", fn);
   }
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-      (!partial && !aligned(out, 16)) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+      (!partial && !aligned(out, 16)) || !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
+      (work_order && !aligned(work_order, 4)))
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: a tensor pointer is null or misaligned", fn);
   bool mfma;
   switch (kernel) {
@@ -113,6 +114,7 @@ pkv_status decode_impl(pkv_kernel kernel, void* out, const void* q, const void* 
   p.v_cache = v_cache;
   p.block_tables = block_tables;
   p.context_lens = context_lens;
+  p.work_order = work_order;
   p.max_logits = max_logits;
   p.exp_sums = exp_sums;
   p.tmp_out = tmp_out;
@@ -164,11 +166,12 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cac
 pkv_status pkv_paged_attention_decode(
     void* out, const void* q, const void* k_cache, const void* v_cache,
     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-    int32_t max_context_len, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-    int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, pkv_dtype dtype,
-    int32_t partition_size, float* max_logits, float* exp_sums, float* tmp_out, void* stream) {
+    const int32_t* work_order, int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    pkv_dtype dtype, int32_t partition_size, float* max_logits, float* exp_sums,
+    float* tmp_out, void* stream) {
   return decode_impl(PKV_KERNEL_AUTO, out, q, k_cache, v_cache, block_tables,
-                     max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_heads,
+                     max_blocks_per_seq, context_lens, work_order, max_context_len, num_seqs, num_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
                      partition_size, max_logits, exp_sums, tmp_out, stream);
 }
@@ -176,12 +179,12 @@ pkv_status pkv_paged_attention_decode(
 pkv_status pkv_paged_attention_decode_with(
     pkv_kernel kernel, void* out, const void* q, const void* k_cache, const void* v_cache,
     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-    int32_t max_context_len, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-    int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, pkv_dtype dtype,
-    int32_t partition_size, float* max_logits, float* exp_sums, float* tmp_out,
-    void* stream) {
+    const int32_t* work_order, int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    pkv_dtype dtype, int32_t partition_size, float* max_logits, float* exp_sums,
+    float* tmp_out, void* stream) {
   return decode_impl(kernel, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
-                     context_lens, max_context_len, num_seqs, num_heads, num_kv_heads,
+                     context_lens, work_order, max_context_len, num_seqs, num_heads, num_kv_heads,
                      head_dim, block_size, num_blocks, scale, dtype, partition_size,
                      max_logits, exp_sums, tmp_out, stream);
 }

@@ -65,19 +65,29 @@ decode_mfma_kernel(const DecodeParams a) {
   const int Hkv = a.num_kv_heads;
   const int H = a.num_heads;
   const int G = H / Hkv;
+  const int MB = a.max_blocks_per_seq;
   const int w = blockIdx.x;
-  const int g = w % Hkv;
+  const int g = w % Hkv;  // consecutive workgroups take different kv heads (XCD round robin)
   const int rest = w / Hkv;
   const int part = rest % a.num_ranges;
-  const int i = rest / a.num_ranges;
+  const int slot = rest / a.num_ranges;
+  const int i = a.work_order ? min(max(a.work_order[slot], 0), a.num_seqs - 1) : slot;
   const int lane = lane_id();
   const int wave = wave_id();
   const int r = lane >> 4;
   const int c = lane & 15;
+  const int32_t* bt = a.block_tables + (size_t)i * MB;
+  const int start = part * a.range_tokens;
+
+  // Waves take chunks wave, wave + NW, ... of the range, so this wave's first chunk is known
+  // before the context length: its block ids are fetched now, in parallel with the length
+  // (any entry of the row may be read; ids are clamped into the pool before use).
+  const int b_first = start / S + wave * BPC;
+  int first0 = b_first < MB ? bt[b_first] : 0;
+  int first1 = (BPC == 2 && b_first + 1 < MB) ? bt[b_first + 1] : first0;
 
   int L = a.context_lens[i];
-  L = min(max(L, 0), a.max_blocks_per_seq * S);
-  const int start = part * a.range_tokens;
+  L = min(max(L, 0), MB * S);
   if (start >= L) {
     if (!PARTIAL && part == 0) {
       T* o = reinterpret_cast<T*>(a.out) + ((size_t)i * H + (size_t)g * G) * D;
@@ -87,9 +97,6 @@ decode_mfma_kernel(const DecodeParams a) {
   }
   const int end = min(start + a.range_tokens, L);
   const int nch = (end - start + CT - 1) / CT;
-  const int per = (nch + NW - 1) / NW;
-  const int ch_lo = wave * per;
-  const int ch_hi = min(ch_lo + per, nch);
   const int blk_end = (end + S - 1) / S;  // first logical block past the range
 
   // q columns: lane (r, c) holds head c (zero beyond the group) at d = 32 kk + 8r .. +8.
@@ -105,7 +112,6 @@ decode_mfma_kernel(const DecodeParams a) {
     }
   }
 
-  const int32_t* bt = a.block_tables + (size_t)i * a.max_blocks_per_seq;
   const size_t tile_bytes = (size_t)S * D * EB;
   const size_t id_stride = (size_t)Hkv * tile_bytes;
   const char* kpool = reinterpret_cast<const char*>(a.k_cache) + (size_t)g * tile_bytes;
@@ -118,24 +124,28 @@ decode_mfma_kernel(const DecodeParams a) {
   const int v_blk = (8 * r) / S;
   const int v_off = c * S * EB + ((8 * r) % S) * EB;  // + nt * 16 rows
 
+  struct Ids {
+    int b0, b1;
+  };
+  auto clamp_id = [&](int id) { return min(max(id, 0), a.num_blocks - 1); };
+  // Physical ids of chunk n's blocks; a second block past the range reuses the first (its
+  // positions are masked).
+  auto fetch_ids = [&](int n) {
+    const int b0 = start / S + n * BPC;
+    Ids ids;
+    ids.b0 = clamp_id(bt[b0]);
+    ids.b1 = (BPC == 2 && b0 + 1 < blk_end) ? clamp_id(bt[b0 + 1]) : ids.b0;
+    return ids;
+  };
+
   struct Regs {
     u32x4 k[2][KK];
     u32x4 v[NT];
   };
 
-  auto load = [&](int n, Regs& R) {
-    const int b0 = start / S + n * BPC;
-    int id0 = bt[b0];
-    id0 = min(max(id0, 0), a.num_blocks - 1);
-    int id1 = id0;
-    if constexpr (BPC == 2) {
-      if (b0 + 1 < blk_end) {
-        id1 = bt[b0 + 1];
-        id1 = min(max(id1, 0), a.num_blocks - 1);
-      }
-    }
-    const char* kt = kpool + (size_t)(k_blk ? id1 : id0) * id_stride + k_off;
-    const char* vt = vpool + (size_t)(v_blk ? id1 : id0) * id_stride + v_off;
+  auto load = [&](const Ids& ids, Regs& R) {
+    const char* kt = kpool + (size_t)(k_blk ? ids.b1 : ids.b0) * id_stride + k_off;
+    const char* vt = vpool + (size_t)(v_blk ? ids.b1 : ids.b0) * id_stride + v_off;
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
@@ -195,17 +205,31 @@ decode_mfma_kernel(const DecodeParams a) {
     }
   };
 
-  if (ch_lo < ch_hi) {
+  int n = wave;
+  if (n < nch) {
     Regs A, B;
-    load(ch_lo, A);
-    int n = ch_lo;
+    Ids ids;
+    ids.b0 = clamp_id(first0);
+    ids.b1 = (BPC == 2 && b_first + 1 < blk_end) ? clamp_id(first1) : ids.b0;
+    load(ids, A);
+    if (n + NW < nch) ids = fetch_ids(n + NW);
+    // Two register sets: chunk n + NW loads while chunk n computes; its block ids were
+    // fetched one step earlier still.
     while (true) {
-      if (n + 1 < ch_hi) load(n + 1, B);
+      if (n + NW < nch) {
+        load(ids, B);
+        if (n + 2 * NW < nch) ids = fetch_ids(n + 2 * NW);
+      }
       compute(n, A);
-      if (++n >= ch_hi) break;
-      if (n + 1 < ch_hi) load(n + 1, A);
+      n += NW;
+      if (n >= nch) break;
+      if (n + NW < nch) {
+        load(ids, A);
+        if (n + 2 * NW < nch) ids = fetch_ids(n + 2 * NW);
+      }
       compute(n, B);
-      if (++n >= ch_hi) break;
+      n += NW;
+      if (n >= nch) break;
     }
   }
 

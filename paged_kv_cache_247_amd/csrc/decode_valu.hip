@@ -39,19 +39,27 @@ decode_valu_kernel(const DecodeParams a) {
 
   const int Hkv = a.num_kv_heads;
   const int H = a.num_heads;
+  const int MB = a.max_blocks_per_seq;
   const int w = blockIdx.x;
   const int g = w % Hkv;  // consecutive workgroups take different kv heads (XCD round robin)
   const int rest = w / Hkv;
   const int part = rest % a.num_ranges;
-  const int i = rest / a.num_ranges;
+  const int slot = rest / a.num_ranges;
+  const int i = a.work_order ? min(max(a.work_order[slot], 0), a.num_seqs - 1) : slot;
   const int lane = lane_id();
   const int wave = wave_id();
   const int r = lane / LPR;
   const int c = lane % LPR;
+  const int32_t* bt = a.block_tables + (size_t)i * MB;
+  const int start = part * a.range_tokens;
+
+  // Waves take blocks start/S + wave, + NW, ...; the first one's id is fetched before the
+  // context length arrives (any entry of the row may be read; ids are clamped before use).
+  const int b_first = start / S + wave;
+  const int first_id = b_first < MB ? bt[b_first] : 0;
 
   int L = a.context_lens[i];
-  L = min(max(L, 0), a.max_blocks_per_seq * S);
-  const int start = part * a.range_tokens;
+  L = min(max(L, 0), MB * S);
   if (start >= L) {
     if (!PARTIAL && part == 0) {
       T* o = reinterpret_cast<T*>(a.out) + ((size_t)i * H + (size_t)g * G) * D;
@@ -60,11 +68,7 @@ decode_valu_kernel(const DecodeParams a) {
     return;
   }
   const int end = min(start + a.range_tokens, L);
-  const int blk_lo = start / S;
   const int blk_hi = (end + S - 1) / S;
-  const int per = (blk_hi - blk_lo + NW - 1) / NW;
-  const int my_lo = blk_lo + wave * per;
-  const int my_hi = min(my_lo + per, blk_hi);
 
   // This lane's 16-byte piece of q for every head of the group, widened to fp32.
   float qf[G][VEC];
@@ -88,7 +92,6 @@ decode_valu_kernel(const DecodeParams a) {
     for (int y = 0; y < VEC; ++y) acc[h][y] = 0.0f;
   }
 
-  const int32_t* bt = a.block_tables + (size_t)i * a.max_blocks_per_seq;
   const size_t tile_bytes = (size_t)S * D * EB;
   const size_t id_stride = (size_t)Hkv * tile_bytes;
   const char* kpool = reinterpret_cast<const char*>(a.k_cache) + (size_t)g * tile_bytes;
@@ -101,9 +104,8 @@ decode_valu_kernel(const DecodeParams a) {
     uint32_t v[VEC][VW];
   };
 
-  auto load = [&](int b, Regs& R) {
-    int id = bt[b];
-    id = min(max(id, 0), a.num_blocks - 1);
+  auto clamp_id = [&](int id) { return min(max(id, 0), a.num_blocks - 1); };
+  auto load = [&](int id, Regs& R) {
     const char* kt = kpool + (size_t)id * id_stride + k_off;
     const char* vt = vpool + (size_t)id * id_stride + v_off;
 #pragma unroll
@@ -170,17 +172,28 @@ decode_valu_kernel(const DecodeParams a) {
     }
   };
 
-  if (my_lo < my_hi) {
+  int b = b_first;
+  if (b < blk_hi) {
     Regs A, B;
-    load(my_lo, A);
-    int b = my_lo;
+    load(clamp_id(first_id), A);
+    int id = b + NW < blk_hi ? clamp_id(bt[b + NW]) : 0;
+    // Two register sets: block b + NW loads while block b computes; its id was fetched one
+    // step earlier still.
     while (true) {
-      if (b + 1 < my_hi) load(b + 1, B);
+      if (b + NW < blk_hi) {
+        load(id, B);
+        if (b + 2 * NW < blk_hi) id = clamp_id(bt[b + 2 * NW]);
+      }
       compute(b, A);
-      if (++b >= my_hi) break;
-      if (b + 1 < my_hi) load(b + 1, A);
+      b += NW;
+      if (b >= blk_hi) break;
+      if (b + NW < blk_hi) {
+        load(id, A);
+        if (b + 2 * NW < blk_hi) id = clamp_id(bt[b + 2 * NW]);
+      }
       compute(b, B);
-      if (++b >= my_hi) break;
+      b += NW;
+      if (b >= blk_hi) break;
     }
   }
 

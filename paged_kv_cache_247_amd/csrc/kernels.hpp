@@ -18,6 +18,7 @@ struct DecodeParams {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const int32_t* work_order;  // NULL = sequence order
   float* max_logits;
   float* exp_sums;
   float* tmp_out;

@@ -180,6 +180,12 @@ class Workload:
     def total_tokens(self) -> int:
         return int(self.context_lens.astype(np.int64).sum())
 
+    def longest_first(self) -> np.ndarray:
+        """Host-side dispatch order for decode: sequence indices by decreasing context length
+        (ties in index order). Any permutation gives the same result; this one lets short
+        sequences fill in behind long ones."""
+        return np.argsort(-self.context_lens.astype(np.int64), kind="stable").astype(np.int32)
+
     def kv_bytes(self) -> int:
         """Algorithmic KV bytes one decode call reads: sum_i L_i * Hkv * D * elt * 2."""
         c = self.cfg

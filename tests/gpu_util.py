@@ -56,8 +56,10 @@ def upload(wl) -> Dev:
                mapping=to_dev(wl.block_mapping.reshape(-1, 2)))
 
 
-def run_step(dev: Dev, wl, kernel="auto", partition_size=None, tables=None, copy=True):
-    """copy_blocks (if the workload has pairs) -> reshape_and_cache -> decode (+ reduce)."""
+def run_step(dev: Dev, wl, kernel="auto", partition_size=None, tables=None, copy=True,
+             order=None):
+    """copy_blocks (if the workload has pairs) -> reshape_and_cache -> decode (+ reduce).
+    order: optional host int32 dispatch order of the sequences."""
     c = wl.cfg
     P = c.partition_size if partition_size is None else partition_size
     if copy and len(wl.block_mapping):
@@ -66,7 +68,8 @@ def run_step(dev: Dev, wl, kernel="auto", partition_size=None, tables=None, copy
     out = torch.full((c.num_seqs, c.num_heads, c.head_dim), float("nan"),
                      dtype=TORCH_DT[c.dtype], device="cuda")
     pk.paged_attention(out, dev.q, dev.k, dev.v, dev.bt if tables is None else tables, dev.lens,
-                       wl.max_context_len, c.scale, P, kernel=kernel)
+                       wl.max_context_len, c.scale, P, kernel=kernel,
+                       work_order=None if order is None else to_dev(np.asarray(order, np.int32)))
     torch.cuda.synchronize()
     return out
 

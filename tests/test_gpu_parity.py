@@ -166,6 +166,18 @@ def test_shared_prefix_equals_private_copy_bit_identical(kernel):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("name,kernel,P", [("c3", "auto", 0), ("c3", "auto", 64),
+                                           ("c5", "auto", 64), ("c2", "auto", 0),
+                                           ("c3", "valu", 32), ("c1", "auto", 0)])
+def test_work_order_does_not_change_the_result(name, kernel, P):
+    wl = W.generate(_cfg(name))
+    base = run_step(upload(wl), wl, kernel=kernel, partition_size=P)
+    for order in (wl.longest_first(),
+                  np.random.default_rng(3).permutation(wl.cfg.num_seqs).astype(np.int32)):
+        got = run_step(upload(wl), wl, kernel=kernel, partition_size=P, order=order)
+        assert torch.equal(got.view(torch.uint8), base.view(torch.uint8))
+
+
 @pytest.mark.parametrize("name", ["c3", "c5"])
 def test_repeated_runs_are_bit_identical(name):
     wl = W.generate(_cfg(name))
@@ -203,21 +215,15 @@ def test_partials_match_oracle(name, kernel, P):
 
 # ------------------------------------------------------------------ full-size workloads
 
-FULL = {  # workload -> (kernel, partition size) the benchmark launches it with
-    "c2": ("auto", 0),
-    "c3": ("auto", 512),
-    "c4": ("auto", 512),
-    "c5": ("auto", 512),
-}
-
-
-@pytest.mark.parametrize("name", list(FULL))
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
 def test_full_size_sampled_against_oracle(name):
-    kernel, P = FULL[name]
+    """The full workload in the launch configuration the benchmark times."""
+    from bench import LAUNCH
+    kernel, P = LAUNCH[name]
     cfg = W.CONFIGS[name]
     wl = W.generate(cfg)
     dev = upload(wl)
-    out = out_f64(run_step(dev, wl, kernel=kernel, partition_size=P))
+    out = out_f64(run_step(dev, wl, kernel=kernel, partition_size=P, order=wl.longest_first()))
     assert np.isfinite(out).all()
     L = wl.context_lens
     rng = np.random.default_rng(0)
