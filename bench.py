@@ -44,40 +44,61 @@ def parse():
     ap.add_argument("--kernel", default=None, choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU time to spend timing the oracle")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     return ap.parse_args()
 
 
 def cpu_baseline(wl, target_s: float):
-    """Oracle decode (fp64 numpy, one thread) on the first sequences of the workload."""
+    """The oracle's decode (fp64 numpy, one thread) over whole passes of the workload, repeated
+    until about target_s seconds of CPU time have run."""
     from threadpoolctl import threadpool_limits
 
     import oracle
     c = wl.cfg
-    order = np.arange(c.num_seqs)
+    passes, toks, dt = 0, 0, 0.0
     with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        oracle.decode(wl.q[:1], wl.k_cache, wl.v_cache, wl.block_tables[:1],
-                      wl.context_lens[:1], c.scale, c.num_kv_heads, c.dtype)
-        per_tok = (time.perf_counter() - t0) / max(int(wl.context_lens[0]), 1)
-        budget = target_s / max(per_tok, 1e-9)
-        cum = np.cumsum(wl.context_lens[order].astype(np.int64))
-        n = int(min(max(np.searchsorted(cum, budget) + 1, 1), c.num_seqs))
-        idx = order[:n]
-        t0 = time.perf_counter()
-        oracle.decode(wl.q[idx], wl.k_cache, wl.v_cache, wl.block_tables[idx],
-                      wl.context_lens[idx], c.scale, c.num_kv_heads, c.dtype)
-        dt = time.perf_counter() - t0
-    toks = int(wl.context_lens[idx].astype(np.int64).sum())
+        while dt < target_s:
+            t0 = time.perf_counter()
+            oracle.decode(wl.q, wl.k_cache, wl.v_cache, wl.block_tables, wl.context_lens,
+                          c.scale, c.num_kv_heads, c.dtype)
+            dt += time.perf_counter() - t0
+            passes += 1
+            toks += wl.total_tokens
     kvb = toks * c.num_kv_heads * c.head_dim * (4 if c.dtype == "f32" else 2) * 2
-    return {"value": kvb / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} of {c.num_seqs} sequences ({toks} context tokens), "
-                      f"fp64 numpy decode, one thread, {dt:.1f} s",
-            "attended_tokens_per_s": toks / dt,
+    return {"value": round(kvb / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} whole passes over all {c.num_seqs} sequences ({toks} context "
+                      f"tokens), fp64 numpy decode on one thread, {dt:.1f} s",
+            "attended_tokens_per_s": round(toks / dt, 1),
             "cpu": platform.processor() or platform.machine()}
+
+
+def counter_traffic(kernel_sources, workload):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if the summary
+    was taken on the kernel sources as they are now (else None)."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", f"decode_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for src in kernel_sources:
+        h.update(open(os.path.join(root, "paged_kv_cache_247_amd", "csrc", src), "rb").read())
+    if vals.get("source_sha256") != h.hexdigest():
+        return None
+    return int(float(vals["traffic_bytes_per_launch"]))
+
+
+# Sources the decode kernels are built from (a change to any invalidates counter figures).
+KERNEL_SOURCES = {"mfma": ["decode_mfma.hip", "common.hpp", "kernels.hpp"],
+                  "valu": ["decode_valu.hip", "common.hpp", "kernels.hpp"]}
 
 
 def main():
@@ -155,6 +176,9 @@ def main():
           file=sys.stderr, flush=True)
 
     kvb = wl.kv_bytes()
+    family = "mfma" if (kernel == "mfma" or (kernel == "auto" and cfg.dtype != "f32"
+                                             and cfg.group >= 4)) else "valu"
+    traffic = counter_traffic(KERNEL_SOURCES[family], name)
     value = kvb / (ms_step * 1e-3) / 1e9
     achieved = kvb / (dec_ms * 1e-3) / 1e9
     ukvb = wl.unique_kv_bytes() if has_copy else kvb
@@ -182,7 +206,7 @@ def main():
         "attended_tokens_per_s": round(wl.total_tokens / (ms_step * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "kernel": "paged_attention_decode",
+                     "traffic": traffic, "kernel": f"paged_attention_decode ({family})",
                      "ms_per_launch": round(dec_ms, 5), "bytes_per_launch": kvb},
     }
     if args.copy_calibration_gib > 0:
