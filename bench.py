@@ -1,11 +1,13 @@
 """Paged decode benchmark on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3] [--kernel auto]
-                    [--partition-size P] [--no-cpu-baseline]
+                    [--partition-size P] [--unfused] [--no-cpu-baseline]
 
 One step is one pass of the whole hot path over one batch: copy-on-write block copies (when
 the workload has them), the cache write of each sequence's newest token, paged decode, and the
-partition merge when the context is split. Inputs are resident in HBM before timing starts.
+partition merge when the context is split. By default the cache write is fused into the decode
+launch (--unfused writes with a separate reshape_and_cache launch). Inputs are resident in HBM
+before timing starts.
 Prints one JSON line: KV-read GB/s over the step (value), attended tokens/s, the decode
 kernel's roofline figures (timed per launch with HIP events on the launch stream) and the
 oracle's CPU throughput on a bounded sample of the same workload.
@@ -23,15 +25,16 @@ import numpy as np
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published peak
 
-# Launch configuration the benchmark uses for each workload: (kernel family, partition size).
-# With longest-first dispatch, single-pass decode is fastest up to 4k-token contexts; the
-# lognormal long-context batch (up to ~31k tokens) splits into 1024-token partitions.
+# Launch configuration the benchmark uses for each workload: (kernel family, partition size,
+# cached K/V loads). With longest-first dispatch, single-pass decode is fastest up to 4k-token
+# contexts; the lognormal long-context batch (up to ~31k tokens) splits into 1024-token
+# partitions; the prefix-shared batch keeps K/V in cache so the shared prefix is reused.
 LAUNCH = {
-    "c1": ("auto", 0),
-    "c2": ("auto", 0),
-    "c3": ("auto", 0),
-    "c4": ("auto", 0),
-    "c5": ("auto", 1024),
+    "c1": ("auto", 0, False),
+    "c2": ("auto", 0, False),
+    "c3": ("auto", 0, False),
+    "c4": ("auto", 0, True),
+    "c5": ("auto", 1024, False),
 }
 
 
@@ -43,6 +46,8 @@ def parse():
     ap.add_argument("--config", default="c3", choices=sorted(LAUNCH))
     ap.add_argument("--kernel", default=None, choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--unfused", action="store_true",
+                    help="write new tokens with a separate reshape_and_cache launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time to spend timing the oracle")
@@ -118,7 +123,7 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     name = args.config
-    kernel, P = LAUNCH[name]
+    kernel, P, cached = LAUNCH[name]
     kernel = args.kernel or kernel
     P = P if args.partition_size is None else args.partition_size
     cfg = W.CONFIGS[name]
@@ -147,15 +152,21 @@ def main():
     has_copy = len(wl.block_mapping) > 0
     ev = []
 
+    fused = not args.unfused
+
     def step(record):
         if has_copy:
             pk.copy_blocks([kc], [vc], mapping)
-        pk.reshape_and_cache(key, value, kc, vc, slots)
+        if not fused:
+            pk.reshape_and_cache(key, value, kc, vc, slots)
         if record:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
+        # With fused=True the decode launch also writes each sequence's newest K/V to its slot.
         pk.paged_attention_decode(None if P else out, q, kc, vc, bt, lens, maxlen, cfg.scale,
-                                  P, ws, kernel=kernel, work_order=order)
+                                  P, ws, kernel=kernel, work_order=order, cached_kv=cached,
+                                  new_key=key if fused else None,
+                                  new_value=value if fused else None)
         if record:
             e1.record()
             ev.append((e0, e1))
@@ -200,7 +211,8 @@ def main():
                    "head_dim": cfg.head_dim, "block_size": cfg.block_size,
                    "num_blocks": cfg.num_blocks, "seed": cfg.seed,
                    "context_tokens": wl.total_tokens, "max_context_len": maxlen,
-                   "kernel": kernel, "partition_size": P, "kv_bytes": kvb,
+                   "kernel": kernel, "partition_size": P, "cached_kv": cached,
+                   "fused_cache_write": fused, "kv_bytes": kvb,
                    "unique_kv_bytes": ukvb},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "attended_tokens_per_s": round(wl.total_tokens / (ms_step * 1e-3), 1),

@@ -120,15 +120,35 @@ pkv_status pkv_paged_attention_decode(
     int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, pkv_dtype dtype,
     int32_t partition_size, float* max_logits, float* exp_sums, float* tmp_out, void* stream);
 
-/* The same operation with an explicit kernel family (for measurement and testing).
- * PKV_KERNEL_MFMA needs fp16/bf16; PKV_KERNEL_VALU needs G <= 8. */
-pkv_status pkv_paged_attention_decode_with(
-    pkv_kernel kernel, void* out, const void* q, const void* k_cache, const void* v_cache,
+/* Options of pkv_paged_attention_decode_ex (a NULL options pointer means all defaults). */
+enum {
+  /* Load K/V with ordinary cached loads instead of the default non-temporal (streaming) ones.
+   * Set it when block tables share physical blocks between sequences (a common prefix, Hacker
+   * News discussion of PagedAttention, replies on shared prefixes): the shared tiles are then
+   * served from the caches. */
+  PKV_DECODE_CACHED_KV = 1u << 0
+};
+typedef struct {
+  pkv_kernel kernel;     /* kernel family; PKV_KERNEL_MFMA needs fp16/bf16, VALU needs G <= 8 */
+  uint32_t flags;        /* PKV_DECODE_* bits */
+  /* NULL, or device [B, Hkv, D] T rows of each sequence's newest token (logical position
+   * L_i - 1), 16-byte aligned: the call then also does the cache write of
+   * pkv_reshape_and_cache for that token -- K row and V column stored at the slot
+   * block_tables maps position L_i - 1 to -- and attends to it from these rows, reading the
+   * pool only up to position L_i - 2. new_key and new_value are both NULL or both set. */
+  const void* new_key;
+  const void* new_value;
+} pkv_decode_options;
+
+/* pkv_paged_attention_decode with options (see pkv_decode_options). k_cache and v_cache are
+ * written only when options->new_key is set. */
+pkv_status pkv_paged_attention_decode_ex(
+    const pkv_decode_options* options, void* out, const void* q, void* k_cache, void* v_cache,
     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-    const int32_t* work_order, int32_t max_context_len, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-    int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, pkv_dtype dtype,
-    int32_t partition_size, float* max_logits, float* exp_sums, float* tmp_out,
-    void* stream);
+    const int32_t* work_order, int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    pkv_dtype dtype, int32_t partition_size, float* max_logits, float* exp_sums,
+    float* tmp_out, void* stream);
 
 /* Merge split-context partitions: for each (i, h) with n = ceil(L_i / partition_size)
  * partitions, M = max_p max_logits, w_p = exp_sums_p * exp(max_logits_p - M),

@@ -19,14 +19,24 @@ PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
 _DTYPES = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
 
+PKV_DECODE_CACHED_KV = 1
+
+
+class DecodeOptions(ctypes.Structure):
+    """pkv_decode_options."""
+    _fields_ = [("kernel", ctypes.c_int), ("flags", ctypes.c_uint32),
+                ("new_key", ctypes.c_void_p), ("new_value", ctypes.c_void_p)]
+
+
 # Exported symbols and their C prototypes (pagedkv.h).
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+_OPT = ctypes.POINTER(DecodeOptions)
 SIGNATURES = {
     "pkv_reshape_and_cache": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pkv_paged_attention_decode": (_I, [_P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I,
                                         _I, _F, _I, _I, _P, _P, _P, _P]),
-    "pkv_paged_attention_decode_with": (_I, [_I, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I,
-                                             _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P]),
+    "pkv_paged_attention_decode_ex": (_I, [_OPT, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I,
+                                           _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P]),
     "pkv_paged_attention_reduce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pkv_copy_blocks": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pkv_partition_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
@@ -145,10 +155,13 @@ def partition_workspace(num_seqs, num_heads, head_dim, max_context_len, partitio
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
                            max_context_len, scale, partition_size=0, workspace=None,
-                           kernel="auto", work_order=None):
-    """pkv_paged_attention_decode(_with). Single pass writes `out`; with partition_size > 0 it
+                           kernel="auto", work_order=None, cached_kv=False, new_key=None,
+                           new_value=None):
+    """pkv_paged_attention_decode_ex. Single pass writes `out`; with partition_size > 0 it
     writes only `workspace` = (max_logits, exp_sums, tmp_out). work_order: optional device int32
-    [B] dispatch order of the sequences (longest first shortens the tail)."""
+    [B] dispatch order of the sequences (longest first shortens the tail). cached_kv: ordinary
+    cached K/V loads (for block tables that share blocks). new_key/new_value: optional
+    [B, Hkv, D] newest-token rows, written to the cache and attended to in the same launch."""
     _need(q, "q", ndim=3)
     dt = q.dtype
     B, H, D = q.shape
@@ -167,6 +180,13 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         _need(work_order, "work_order", torch.int32, 1, q.device)
         if work_order.shape[0] != B:
             raise ValueError("work_order must have one entry per sequence")
+    if (new_key is None) != (new_value is None):
+        raise ValueError("new_key and new_value go together")
+    if new_key is not None:
+        for t, nm in ((new_key, "new_key"), (new_value, "new_value")):
+            _need(t, nm, dt, 3, q.device)
+            if tuple(t.shape) != (B, Hkv, D):
+                raise ValueError(f"{nm} must be [B, Hkv, D]")
     MB = block_tables.shape[1]
     ml = es = to = None
     if partition_size:
@@ -183,8 +203,11 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         if tuple(out.shape) != (B, H, D):
             raise ValueError("out must be [B, H, D]")
     lib = load()
-    _check(lib.pkv_paged_attention_decode_with(
-        KERNELS[kernel], _ptr(out) if not partition_size else None, _ptr(q), _ptr(k_cache),
+    opts = DecodeOptions(KERNELS[kernel], PKV_DECODE_CACHED_KV if cached_kv else 0,
+                         None if new_key is None else new_key.data_ptr(),
+                         None if new_value is None else new_value.data_ptr())
+    _check(lib.pkv_paged_attention_decode_ex(
+        ctypes.byref(opts), _ptr(out) if not partition_size else None, _ptr(q), _ptr(k_cache),
         _ptr(v_cache), _ptr(block_tables), MB, _ptr(context_lens), _ptr(work_order),
         int(max_context_len), B, H,
         Hkv, D, S, N, float(scale), _dt(q), int(partition_size), _ptr(ml), _ptr(es), _ptr(to),
@@ -230,17 +253,19 @@ def copy_blocks(k_caches, v_caches, block_mapping):
 
 
 def paged_attention(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
-                    scale, partition_size=0, workspace=None, kernel="auto", work_order=None):
+                    scale, partition_size=0, workspace=None, kernel="auto", work_order=None,
+                    cached_kv=False, new_key=None, new_value=None):
     """The whole decode: single pass, or partitions then their merge, on the current stream."""
+    kw = dict(kernel=kernel, work_order=work_order, cached_kv=cached_kv, new_key=new_key,
+              new_value=new_value)
     if partition_size:
         B, H, D = q.shape
         if workspace is None:
             workspace = partition_workspace(B, H, D, max_context_len, partition_size, q.device)
         paged_attention_decode(None, q, k_cache, v_cache, block_tables, context_lens,
-                               max_context_len, scale, partition_size, workspace, kernel,
-                               work_order)
+                               max_context_len, scale, partition_size, workspace, **kw)
         paged_attention_reduce(out, workspace, context_lens, partition_size)
     else:
         paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
-                               max_context_len, scale, 0, None, kernel, work_order)
+                               max_context_len, scale, 0, None, **kw)
     return out

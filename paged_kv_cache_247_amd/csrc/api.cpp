@@ -51,8 +51,8 @@ pkv_status check_tile(const char* fn, int32_t num_kv_heads, int32_t head_dim,
   return PKV_OK;
 }
 
-pkv_status decode_impl(pkv_kernel kernel, void* out, const void* q, const void* k_cache,
-                       const void* v_cache, const int32_t* block_tables,
+pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, void* k_cache,
+                       void* v_cache, const int32_t* block_tables,
                        int32_t max_blocks_per_seq, const int32_t* context_lens,
                        const int32_t* work_order, int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
@@ -90,12 +90,20 @@ pkv_status decode_impl(pkv_kernel kernel, void* out, const void* q, const void* 
       (!partial && !aligned(out, 16)) || !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
       (work_order && !aligned(work_order, 4)))
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: a tensor pointer is null or misaligned", fn);
+  static const pkv_decode_options defaults = {PKV_KERNEL_AUTO, 0u, nullptr, nullptr};
+  if (!opt) opt = &defaults;
+  if (opt->flags & ~(uint32_t)PKV_DECODE_CACHED_KV)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: unknown option flags 0x%x", fn, opt->flags);
+  if ((opt->new_key == nullptr) != (opt->new_value == nullptr) ||
+      (opt->new_key && (!aligned(opt->new_key, 16) || !aligned(opt->new_value, 16))))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: new_key/new_value must both be NULL or both set "
+                "and 16-byte aligned", fn);
   bool mfma;
-  switch (kernel) {
+  switch (opt->kernel) {
     case PKV_KERNEL_AUTO: mfma = dtype != PKV_F32 && G >= 4; break;
     case PKV_KERNEL_VALU: mfma = false; break;
     case PKV_KERNEL_MFMA: mfma = true; break;
-    default: return fail(PKV_ERR_INVALID_ARGUMENT, "%s: bad kernel family %d", fn, (int)kernel);
+    default: return fail(PKV_ERR_INVALID_ARGUMENT, "%s: bad kernel family %d", fn, (int)opt->kernel);
   }
   if (mfma && dtype == PKV_F32)
     return fail(PKV_ERR_UNSUPPORTED, "%s: the MFMA kernel takes fp16/bf16 only", fn);
@@ -115,6 +123,8 @@ pkv_status decode_impl(pkv_kernel kernel, void* out, const void* q, const void* 
   p.block_tables = block_tables;
   p.context_lens = context_lens;
   p.work_order = work_order;
+  p.new_key = opt->new_key;
+  p.new_value = opt->new_value;
   p.max_logits = max_logits;
   p.exp_sums = exp_sums;
   p.tmp_out = tmp_out;
@@ -127,8 +137,10 @@ pkv_status decode_impl(pkv_kernel kernel, void* out, const void* q, const void* 
   p.num_ranges = (int32_t)ranges;
   p.scale_log2e = scale * pkv::kLog2e;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const hipError_t e = mfma ? pkv::launch_decode_mfma(to_dt(dtype), head_dim, block_size, partial, p, s)
-                            : pkv::launch_decode_valu(to_dt(dtype), head_dim, block_size, G, partial, p, s);
+  const bool nt = !(opt->flags & PKV_DECODE_CACHED_KV);
+  const hipError_t e =
+      mfma ? pkv::launch_decode_mfma(to_dt(dtype), head_dim, block_size, partial, nt, p, s)
+           : pkv::launch_decode_valu(to_dt(dtype), head_dim, block_size, G, partial, nt, p, s);
   return hip_status(e, fn);
 }
 
@@ -170,23 +182,25 @@ pkv_status pkv_paged_attention_decode(
     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
     pkv_dtype dtype, int32_t partition_size, float* max_logits, float* exp_sums,
     float* tmp_out, void* stream) {
-  return decode_impl(PKV_KERNEL_AUTO, out, q, k_cache, v_cache, block_tables,
-                     max_blocks_per_seq, context_lens, work_order, max_context_len, num_seqs, num_heads,
-                     num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
-                     partition_size, max_logits, exp_sums, tmp_out, stream);
+  // Without new rows the kernels never write the pools.
+  return decode_impl(nullptr, out, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
+                     block_tables, max_blocks_per_seq, context_lens, work_order,
+                     max_context_len, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, scale, dtype, partition_size, max_logits, exp_sums, tmp_out,
+                     stream);
 }
 
-pkv_status pkv_paged_attention_decode_with(
-    pkv_kernel kernel, void* out, const void* q, const void* k_cache, const void* v_cache,
+pkv_status pkv_paged_attention_decode_ex(
+    const pkv_decode_options* options, void* out, const void* q, void* k_cache, void* v_cache,
     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
     const int32_t* work_order, int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
     pkv_dtype dtype, int32_t partition_size, float* max_logits, float* exp_sums,
     float* tmp_out, void* stream) {
-  return decode_impl(kernel, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
-                     context_lens, work_order, max_context_len, num_seqs, num_heads, num_kv_heads,
-                     head_dim, block_size, num_blocks, scale, dtype, partition_size,
-                     max_logits, exp_sums, tmp_out, stream);
+  return decode_impl(options, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                     context_lens, work_order, max_context_len, num_seqs, num_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                     partition_size, max_logits, exp_sums, tmp_out, stream);
 }
 
 pkv_status pkv_paged_attention_reduce(void* out, const float* max_logits,

@@ -44,7 +44,7 @@ template <> struct Mfma<Dt::F16> {
   static __device__ __forceinline__ _Float16 narrow(float x) { return (_Float16)x; }
 };
 
-template <Dt DT, int D, int S, int NW, bool PARTIAL>
+template <Dt DT, int D, int S, int NW, bool PARTIAL, bool NTL>
 __global__ void __launch_bounds__(NW * 64)
 decode_mfma_kernel(const DecodeParams a) {
   static_assert(DT == Dt::BF16 || DT == Dt::F16, "16-bit inputs only");
@@ -61,6 +61,8 @@ decode_mfma_kernel(const DecodeParams a) {
   __shared__ float sh_m[NW][16];
   __shared__ float sh_l[NW][16];
   __shared__ float sh_acc[NW][16][D];
+  __shared__ float sh_new[16];
+  __shared__ float sh_vnew[D];
 
   const int Hkv = a.num_kv_heads;
   const int H = a.num_heads;
@@ -95,9 +97,12 @@ decode_mfma_kernel(const DecodeParams a) {
     }
     return;
   }
-  const int end = min(start + a.range_tokens, L);
-  const int nch = (end - start + CT - 1) / CT;
-  const int blk_end = (end + S - 1) / S;  // first logical block past the range
+  // With a fused write, position L-1 comes from new_key/new_value (this is then the sequence's
+  // last range) and the cache is read only up to L-2.
+  const bool fused = a.new_key != nullptr && start + a.range_tokens >= L;
+  const int end = min(start + a.range_tokens, L) - (fused ? 1 : 0);
+  const int nch = max(end - start + CT - 1, 0) / CT;
+  const int blk_end = (end + S - 1) / S;  // first logical block past the cached range
 
   // q columns: lane (r, c) holds head c (zero beyond the group) at d = 32 kk + 8r .. +8.
   V8 qb[KK];
@@ -150,9 +155,9 @@ decode_mfma_kernel(const DecodeParams a) {
     for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        R.k[gi][kk] = load_kv<u32x4>(kt + gi * 4 * D * EB + kk * 64);
+        R.k[gi][kk] = load_kv<NTL, u32x4>(kt + gi * 4 * D * EB + kk * 64);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) R.v[nt] = load_kv<u32x4>(vt + nt * 16 * S * EB);
+    for (int nt = 0; nt < NT; ++nt) R.v[nt] = load_kv<NTL, u32x4>(vt + nt * 16 * S * EB);
   };
 
   float m = -INFINITY, l = 0.0f;
@@ -205,6 +210,55 @@ decode_mfma_kernel(const DecodeParams a) {
     }
   };
 
+  // Position L-1 joins the merge below as one more partial state (m = its logit, l = 1,
+  // acc = its V row). Its rows are loaded before the first chunk (vector loads return in
+  // order, so waiting for them below does not wait for the chunk).
+  const char* kn = reinterpret_cast<const char*>(a.new_key) + ((size_t)i * Hkv + g) * D * EB;
+  const T* vn = reinterpret_cast<const T*>(a.new_value) + ((size_t)i * Hkv + g) * D;
+  u32x4 kpiece[KK];
+  u32x4 krow = {0u, 0u, 0u, 0u};
+  T vrow[D / 64];
+  int slot_blk = 0;
+  if (fused) {
+    if (wave == NW - 1) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        kpiece[kk] = *reinterpret_cast<const u32x4*>(kn + (32 * kk + 8 * r) * EB);
+    }
+    if (wave == 0) {
+      slot_blk = bt[(L - 1) / S];
+      if (lane < D * EB / 16) krow = reinterpret_cast<const u32x4*>(kn)[lane];
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e) vrow[e] = vn[lane + 64 * e];
+    }
+  }
+
+  // Consumes the new rows loaded above (after this wave's first loads are in flight): the
+  // last wave's logits and wave 0's LDS copy of the V row.
+  auto use_new_rows = [&]() {
+    if (wave == NW - 1) {
+      // Logit of head c: fp32 dot over the d pieces this lane holds of q, summed over rows.
+      float part_dot = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const V8 kv = __builtin_bit_cast(V8, kpiece[kk]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) part_dot = fmaf((float)qb[kk][j], (float)kv[j], part_dot);
+      }
+      part_dot = across16(part_dot, OpAdd());
+      part_dot = across32(part_dot, OpAdd());
+      if (r == 0 && c < G) sh_new[c] = part_dot * a.scale_log2e;
+    }
+    if (wave == 0) {
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e) {
+        const int d = lane + 64 * e;
+        if constexpr (DT == Dt::BF16) sh_vnew[d] = bits_f((uint32_t)vrow[e] << 16);
+        else sh_vnew[d] = (float)vrow[e];
+      }
+    }
+  };
+
   int n = wave;
   if (n < nch) {
     Regs A, B;
@@ -213,6 +267,7 @@ decode_mfma_kernel(const DecodeParams a) {
     ids.b1 = (BPC == 2 && b_first + 1 < blk_end) ? clamp_id(first1) : ids.b0;
     load(ids, A);
     if (n + NW < nch) ids = fetch_ids(n + NW);
+    if (fused) use_new_rows();
     // Two register sets: chunk n + NW loads while chunk n computes; its block ids were
     // fetched one step earlier still.
     while (true) {
@@ -231,10 +286,26 @@ decode_mfma_kernel(const DecodeParams a) {
       n += NW;
       if (n >= nch) break;
     }
+  } else if (fused) {
+    use_new_rows();
+  }
+
+  // The new rows go to the slot the table maps position L-1 to. The stores come after every
+  // block-table read so the table can stay in the scalar cache (a store that might alias it
+  // would force those reads through the vector memory path).
+  if (fused && wave == 0) {
+    const int p = L - 1;
+    const size_t tile = ((size_t)clamp_id(slot_blk) * Hkv + g) * S * D;
+    T* kc = reinterpret_cast<T*>(a.k_cache) + tile + (size_t)(p % S) * D;
+    T* vc = reinterpret_cast<T*>(a.v_cache) + tile + (p % S);
+    if (lane < D * EB / 16) reinterpret_cast<u32x4*>(kc)[lane] = krow;
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) vc[(size_t)(lane + 64 * e) * S] = vrow[e];
   }
 
   l = across16(l, OpAdd());
   l = across32(l, OpAdd());
+
   if (c < G) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -250,7 +321,7 @@ decode_mfma_kernel(const DecodeParams a) {
   for (int e = threadIdx.x; e < G * D; e += NW * 64) {
     const int h = e / D;
     const int d = e % D;
-    float Mx = -INFINITY;
+    float Mx = fused ? sh_new[h] : -INFINITY;
 #pragma unroll
     for (int v = 0; v < NW; ++v) Mx = fmaxf(Mx, sh_m[v][h]);
     float num = 0.0f, den = 0.0f;
@@ -259,6 +330,11 @@ decode_mfma_kernel(const DecodeParams a) {
       const float f = __builtin_amdgcn_exp2f(sh_m[v][h] - Mx);
       num = fmaf(f, sh_acc[v][h][d], num);
       den = fmaf(f, sh_l[v][h], den);
+    }
+    if (fused) {
+      const float f = __builtin_amdgcn_exp2f(sh_new[h] - Mx);
+      num = fmaf(f, sh_vnew[d], num);
+      den += f;
     }
     const float o = num / den;
     const size_t row = (size_t)i * H + (size_t)g * G + h;
@@ -278,42 +354,46 @@ decode_mfma_kernel(const DecodeParams a) {
 constexpr int kMfmaWaves = 4;
 
 template <Dt DT, int D, int S>
-hipError_t launch_s(bool partial, const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_s(bool partial, bool nt, const DecodeParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)p.num_seqs * p.num_ranges * p.num_kv_heads);
   const dim3 block(kMfmaWaves * 64);
-  if (partial)
-    decode_mfma_kernel<DT, D, S, kMfmaWaves, true><<<grid, block, 0, stream>>>(p);
-  else
-    decode_mfma_kernel<DT, D, S, kMfmaWaves, false><<<grid, block, 0, stream>>>(p);
+  if (partial) {
+    if (nt) decode_mfma_kernel<DT, D, S, kMfmaWaves, true, true><<<grid, block, 0, stream>>>(p);
+    else decode_mfma_kernel<DT, D, S, kMfmaWaves, true, false><<<grid, block, 0, stream>>>(p);
+  } else {
+    if (nt) decode_mfma_kernel<DT, D, S, kMfmaWaves, false, true><<<grid, block, 0, stream>>>(p);
+    else decode_mfma_kernel<DT, D, S, kMfmaWaves, false, false><<<grid, block, 0, stream>>>(p);
+  }
   return hipGetLastError();
 }
 
 template <Dt DT, int D>
-hipError_t launch_d(int block_size, bool partial, const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_d(int block_size, bool partial, bool nt, const DecodeParams& p,
+                    hipStream_t stream) {
   switch (block_size) {
-    case 16: return launch_s<DT, D, 16>(partial, p, stream);
-    case 32: return launch_s<DT, D, 32>(partial, p, stream);
+    case 16: return launch_s<DT, D, 16>(partial, nt, p, stream);
+    case 32: return launch_s<DT, D, 32>(partial, nt, p, stream);
     default: return hipErrorNotSupported;
   }
 }
 
 template <Dt DT>
-hipError_t launch_t(int head_dim, int block_size, bool partial, const DecodeParams& p,
+hipError_t launch_t(int head_dim, int block_size, bool partial, bool nt, const DecodeParams& p,
                     hipStream_t stream) {
   switch (head_dim) {
-    case 64: return launch_d<DT, 64>(block_size, partial, p, stream);
-    case 128: return launch_d<DT, 128>(block_size, partial, p, stream);
+    case 64: return launch_d<DT, 64>(block_size, partial, nt, p, stream);
+    case 128: return launch_d<DT, 128>(block_size, partial, nt, p, stream);
     default: return hipErrorNotSupported;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_mfma(Dt dt, int head_dim, int block_size, bool partial,
+hipError_t launch_decode_mfma(Dt dt, int head_dim, int block_size, bool partial, bool nt,
                               const DecodeParams& p, hipStream_t stream) {
   switch (dt) {
-    case Dt::F16: return launch_t<Dt::F16>(head_dim, block_size, partial, p, stream);
-    case Dt::BF16: return launch_t<Dt::BF16>(head_dim, block_size, partial, p, stream);
+    case Dt::F16: return launch_t<Dt::F16>(head_dim, block_size, partial, nt, p, stream);
+    case Dt::BF16: return launch_t<Dt::BF16>(head_dim, block_size, partial, nt, p, stream);
     default: return hipErrorNotSupported;
   }
 }

@@ -20,7 +20,7 @@
 namespace pkv {
 namespace {
 
-template <Dt DT, int D, int S, int G, int NW, bool PARTIAL>
+template <Dt DT, int D, int S, int G, int NW, bool PARTIAL, bool NTL>
 __global__ void __launch_bounds__(NW * 64)
 decode_valu_kernel(const DecodeParams a) {
   constexpr int EB = Elt<DT>::bytes;
@@ -36,6 +36,8 @@ decode_valu_kernel(const DecodeParams a) {
   __shared__ float sh_m[NW][G];
   __shared__ float sh_l[NW][G];
   __shared__ float sh_acc[NW][G][D];
+  __shared__ float sh_new[G];
+  __shared__ float sh_vnew[D];
 
   const int Hkv = a.num_kv_heads;
   const int H = a.num_heads;
@@ -67,7 +69,10 @@ decode_valu_kernel(const DecodeParams a) {
     }
     return;
   }
-  const int end = min(start + a.range_tokens, L);
+  // With a fused write, position L-1 comes from new_key/new_value (this is then the sequence's
+  // last range) and the cache is read only up to L-2.
+  const bool fused = a.new_key != nullptr && start + a.range_tokens >= L;
+  const int end = min(start + a.range_tokens, L) - (fused ? 1 : 0);
   const int blk_hi = (end + S - 1) / S;
 
   // This lane's 16-byte piece of q for every head of the group, widened to fp32.
@@ -109,9 +114,9 @@ decode_valu_kernel(const DecodeParams a) {
     const char* kt = kpool + (size_t)id * id_stride + k_off;
     const char* vt = vpool + (size_t)id * id_stride + v_off;
 #pragma unroll
-    for (int x = 0; x < TPL; ++x) load_words<16>(kt + x * D * EB, R.k[x]);
+    for (int x = 0; x < TPL; ++x) load_words<16, NTL>(kt + x * D * EB, R.k[x]);
 #pragma unroll
-    for (int y = 0; y < VEC; ++y) load_words<VB>(vt + y * LPR * S * EB, R.v[y]);
+    for (int y = 0; y < VEC; ++y) load_words<VB, NTL>(vt + y * LPR * S * EB, R.v[y]);
   };
 
   auto compute = [&](int b, const Regs& R) {
@@ -172,11 +177,58 @@ decode_valu_kernel(const DecodeParams a) {
     }
   };
 
+  // Position L-1 joins the merge below as one more partial state (m = its logit, l = 1,
+  // acc = its V row). Its rows are loaded before the first block (vector loads return in
+  // order, so waiting for them below does not wait for the block).
+  const char* kn = reinterpret_cast<const char*>(a.new_key) + ((size_t)i * Hkv + g) * D * EB;
+  const T* vn = reinterpret_cast<const T*>(a.new_value) + ((size_t)i * Hkv + g) * D;
+  u32x4 kpiece = {0u, 0u, 0u, 0u};
+  u32x4 krow = {0u, 0u, 0u, 0u};
+  T vrow[D / 64];
+  int slot_blk = 0;
+  if (fused) {
+    if (wave == NW - 1) kpiece = *reinterpret_cast<const u32x4*>(kn + (size_t)c * 16);
+    if (wave == 0) {
+      slot_blk = bt[(L - 1) / S];
+      if (lane < D * EB / 16) krow = reinterpret_cast<const u32x4*>(kn)[lane];
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e) vrow[e] = vn[lane + 64 * e];
+    }
+  }
+
+  // Consumes the new rows loaded above (after this wave's first loads are in flight): the
+  // last wave's logits and wave 0's LDS copy of the V row.
+  auto use_new_rows = [&]() {
+    if (wave == NW - 1) {
+      const uint32_t kw4[4] = {kpiece.x, kpiece.y, kpiece.z, kpiece.w};
+      float kf[VEC];
+      unpack_words<DT, 4>(kw4, kf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float t = 0.0f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) t = fmaf(qf[h][e], kf[e], t);
+        t = group_reduce<LPR>(t, OpAdd());
+        if (lane == 0) sh_new[h] = t * a.scale_log2e;
+      }
+    }
+    if (wave == 0) {
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e) {
+        const int d = lane + 64 * e;
+        if constexpr (DT == Dt::F32) sh_vnew[d] = vrow[e];
+        else if constexpr (DT == Dt::BF16) sh_vnew[d] = bits_f((uint32_t)vrow[e] << 16);
+        else sh_vnew[d] = (float)vrow[e];
+      }
+    }
+  };
+
   int b = b_first;
   if (b < blk_hi) {
     Regs A, B;
     load(clamp_id(first_id), A);
     int id = b + NW < blk_hi ? clamp_id(bt[b + NW]) : 0;
+    if (fused) use_new_rows();
     // Two register sets: block b + NW loads while block b computes; its id was fetched one
     // step earlier still.
     while (true) {
@@ -195,6 +247,21 @@ decode_valu_kernel(const DecodeParams a) {
       b += NW;
       if (b >= blk_hi) break;
     }
+  } else if (fused) {
+    use_new_rows();
+  }
+
+  // The new rows go to the slot the table maps position L-1 to. The stores come after every
+  // block-table read so the table can stay in the scalar cache (a store that might alias it
+  // would force those reads through the vector memory path).
+  if (fused && wave == 0) {
+    const int p = L - 1;
+    const size_t tile = ((size_t)clamp_id(slot_blk) * Hkv + g) * S * D;
+    T* kc = reinterpret_cast<T*>(a.k_cache) + tile + (size_t)(p % S) * D;
+    T* vc = reinterpret_cast<T*>(a.v_cache) + tile + (p % S);
+    if (lane < D * EB / 16) reinterpret_cast<u32x4*>(kc)[lane] = krow;
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) vc[(size_t)(lane + 64 * e) * S] = vrow[e];
   }
 
   // Sum each lane's positions over the row groups (lanes that share c hold the same columns).
@@ -223,7 +290,7 @@ decode_valu_kernel(const DecodeParams a) {
   for (int e = threadIdx.x; e < G * D; e += NW * 64) {
     const int h = e / D;
     const int d = e % D;
-    float M = -INFINITY;
+    float M = fused ? sh_new[h] : -INFINITY;
 #pragma unroll
     for (int v = 0; v < NW; ++v) M = fmaxf(M, sh_m[v][h]);
     float num = 0.0f, den = 0.0f;
@@ -232,6 +299,11 @@ decode_valu_kernel(const DecodeParams a) {
       const float f = __builtin_amdgcn_exp2f(sh_m[v][h] - M);
       num = fmaf(f, sh_acc[v][h][d], num);
       den = fmaf(f, sh_l[v][h], den);
+    }
+    if (fused) {
+      const float f = __builtin_amdgcn_exp2f(sh_new[h] - M);
+      num = fmaf(f, sh_vnew[d], num);
+      den += f;
     }
     const float o = num / den;
     const size_t row = (size_t)i * H + (size_t)g * G + h;
@@ -251,43 +323,47 @@ decode_valu_kernel(const DecodeParams a) {
 constexpr int kValuWaves = 4;
 
 template <Dt DT, int D, int S, int G>
-hipError_t launch_g(bool partial, const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_g(bool partial, bool nt, const DecodeParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)p.num_seqs * p.num_ranges * p.num_kv_heads);
   const dim3 block(kValuWaves * 64);
-  if (partial)
-    decode_valu_kernel<DT, D, S, G, kValuWaves, true><<<grid, block, 0, stream>>>(p);
-  else
-    decode_valu_kernel<DT, D, S, G, kValuWaves, false><<<grid, block, 0, stream>>>(p);
+  if (partial) {
+    if (nt) decode_valu_kernel<DT, D, S, G, kValuWaves, true, true><<<grid, block, 0, stream>>>(p);
+    else decode_valu_kernel<DT, D, S, G, kValuWaves, true, false><<<grid, block, 0, stream>>>(p);
+  } else {
+    if (nt) decode_valu_kernel<DT, D, S, G, kValuWaves, false, true><<<grid, block, 0, stream>>>(p);
+    else decode_valu_kernel<DT, D, S, G, kValuWaves, false, false><<<grid, block, 0, stream>>>(p);
+  }
   return hipGetLastError();
 }
 
 template <Dt DT, int D, int S>
-hipError_t launch_s(int group, bool partial, const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_s(int group, bool partial, bool nt, const DecodeParams& p,
+                    hipStream_t stream) {
   switch (group) {
-    case 1: return launch_g<DT, D, S, 1>(partial, p, stream);
-    case 2: return launch_g<DT, D, S, 2>(partial, p, stream);
-    case 4: return launch_g<DT, D, S, 4>(partial, p, stream);
-    case 8: return launch_g<DT, D, S, 8>(partial, p, stream);
+    case 1: return launch_g<DT, D, S, 1>(partial, nt, p, stream);
+    case 2: return launch_g<DT, D, S, 2>(partial, nt, p, stream);
+    case 4: return launch_g<DT, D, S, 4>(partial, nt, p, stream);
+    case 8: return launch_g<DT, D, S, 8>(partial, nt, p, stream);
     default: return hipErrorNotSupported;
   }
 }
 
 template <Dt DT, int D>
-hipError_t launch_d(int block_size, int group, bool partial, const DecodeParams& p,
+hipError_t launch_d(int block_size, int group, bool partial, bool nt, const DecodeParams& p,
                     hipStream_t stream) {
   switch (block_size) {
-    case 16: return launch_s<DT, D, 16>(group, partial, p, stream);
-    case 32: return launch_s<DT, D, 32>(group, partial, p, stream);
+    case 16: return launch_s<DT, D, 16>(group, partial, nt, p, stream);
+    case 32: return launch_s<DT, D, 32>(group, partial, nt, p, stream);
     default: return hipErrorNotSupported;
   }
 }
 
 template <Dt DT>
-hipError_t launch_t(int head_dim, int block_size, int group, bool partial,
+hipError_t launch_t(int head_dim, int block_size, int group, bool partial, bool nt,
                     const DecodeParams& p, hipStream_t stream) {
   switch (head_dim) {
-    case 64: return launch_d<DT, 64>(block_size, group, partial, p, stream);
-    case 128: return launch_d<DT, 128>(block_size, group, partial, p, stream);
+    case 64: return launch_d<DT, 64>(block_size, group, partial, nt, p, stream);
+    case 128: return launch_d<DT, 128>(block_size, group, partial, nt, p, stream);
     default: return hipErrorNotSupported;
   }
 }
@@ -295,11 +371,11 @@ hipError_t launch_t(int head_dim, int block_size, int group, bool partial,
 }  // namespace
 
 hipError_t launch_decode_valu(Dt dt, int head_dim, int block_size, int group, bool partial,
-                              const DecodeParams& p, hipStream_t stream) {
+                              bool nt, const DecodeParams& p, hipStream_t stream) {
   switch (dt) {
-    case Dt::F32: return launch_t<Dt::F32>(head_dim, block_size, group, partial, p, stream);
-    case Dt::F16: return launch_t<Dt::F16>(head_dim, block_size, group, partial, p, stream);
-    case Dt::BF16: return launch_t<Dt::BF16>(head_dim, block_size, group, partial, p, stream);
+    case Dt::F32: return launch_t<Dt::F32>(head_dim, block_size, group, partial, nt, p, stream);
+    case Dt::F16: return launch_t<Dt::F16>(head_dim, block_size, group, partial, nt, p, stream);
+    case Dt::BF16: return launch_t<Dt::BF16>(head_dim, block_size, group, partial, nt, p, stream);
   }
   return hipErrorNotSupported;
 }

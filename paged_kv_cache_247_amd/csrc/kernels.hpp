@@ -14,11 +14,13 @@ namespace pkv {
 struct DecodeParams {
   void* out;
   const void* q;
-  const void* k_cache;
-  const void* v_cache;
+  void* k_cache;  // written only by the fused newest-token write
+  void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
   const int32_t* work_order;  // NULL = sequence order
+  const void* new_key;        // NULL, or [B, Hkv, D]: position L-1 of each sequence, fused write
+  const void* new_value;
   float* max_logits;
   float* exp_sums;
   float* tmp_out;
@@ -68,9 +70,10 @@ struct CacheWriteParams {
 
 // Each returns hipSuccess or the launch error; hipErrorNotSupported if no instantiation
 // matches (the C ABI validates shapes before calling, so that is a library bug).
+// nt: non-temporal K/V loads (else cached loads, for shared prefixes).
 hipError_t launch_decode_valu(Dt dt, int head_dim, int block_size, int group, bool partial,
-                              const DecodeParams& p, hipStream_t stream);
-hipError_t launch_decode_mfma(Dt dt, int head_dim, int block_size, bool partial,
+                              bool nt, const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_mfma(Dt dt, int head_dim, int block_size, bool partial, bool nt,
                               const DecodeParams& p, hipStream_t stream);
 hipError_t launch_reduce(Dt dt, int head_dim, const ReduceParams& p, hipStream_t stream);
 hipError_t launch_reshape_and_cache(Dt dt, int head_dim, int block_size,

@@ -56,11 +56,12 @@ def test_workspace_bytes(lib):
 def decode(lib, **kw):
     a = dict(kernel=0, out=A16, q=A16, k=A16, v=A16, bt=A16, MB=4, lens=A16, maxlen=64, B=2,
              H=8, Hkv=2, D=128, S=16, N=32, scale=0.125, dtype=2, P=0, ml=None, es=None, to=None,
-             order=None)
+             order=None, flags=0, nk=None, nv=None)
     a.update(kw)
-    return lib.pkv_paged_attention_decode_with(
-        a["kernel"], a["out"], a["q"], a["k"], a["v"], a["bt"], a["MB"], a["lens"], a["order"],
-        a["maxlen"],
+    opts = _lib.DecodeOptions(a["kernel"], a["flags"], a["nk"], a["nv"])
+    return lib.pkv_paged_attention_decode_ex(
+        ctypes.byref(opts), a["out"], a["q"], a["k"], a["v"], a["bt"], a["MB"], a["lens"],
+        a["order"], a["maxlen"],
         a["B"], a["H"], a["Hkv"], a["D"], a["S"], a["N"], a["scale"], a["dtype"], a["P"],
         a["ml"], a["es"], a["to"], None)
 
@@ -89,6 +90,9 @@ def decode(lib, **kw):
     (dict(kernel=2, dtype=0), UNSUPPORTED),  # MFMA needs 16-bit inputs
     (dict(kernel=1, H=32, Hkv=2), UNSUPPORTED),  # VALU kernel: group <= 8
     (dict(kernel=9), INVALID),
+    (dict(flags=4), INVALID),  # unknown option bit
+    (dict(nk=A16), INVALID),  # new_key without new_value
+    (dict(nk=A16, nv=A16 + 8), INVALID),  # misaligned new_value
     (dict(B=0), OK),  # nothing to do, nothing enqueued
 ])
 def test_decode_validation(lib, kw, status):

@@ -178,6 +178,60 @@ def test_work_order_does_not_change_the_result(name, kernel, P):
         assert torch.equal(got.view(torch.uint8), base.view(torch.uint8))
 
 
+FUSED = [("c1", {}, "auto", (0, 16)), ("c2", {}, "auto", (0, 64)), ("c3", {}, "auto", (0, 32)),
+         ("c3", {}, "valu", (0, 48)), ("c3", {"dtype": "f16", "head_dim": 64}, "auto", (0,)),
+         ("c3", {"dtype": "f32"}, "auto", (0, 16)), ("c4", {}, "auto", (0, 32)),
+         ("c5", {}, "auto", (64, 0)), ("c5", {"num_heads": 4}, "auto", (64,))]
+
+
+@pytest.mark.parametrize("name,over,kernel,parts", FUSED,
+                         ids=[f"{c[0]}-{'-'.join(f'{k}{v}' for k, v in c[1].items()) or 'base'}"
+                              f"-{c[2]}" for c in FUSED])
+def test_fused_cache_write_matches_oracle(name, over, kernel, parts):
+    """Decode that writes each newest token itself: same output tolerance, and the pools end
+    bit-identical to the oracle's cache write (and copies)."""
+    wl = W.generate(_cfg(name, **over))
+    dt = wl.cfg.dtype
+    kc, vc = oracle_pools(wl)
+    ref = oracle_out(wl, pools=(kc, vc))
+    for P in parts:
+        dev = upload(wl)
+        out = run_step(dev, wl, kernel=kernel, partition_size=P, fused=True)
+        err = oracle.max_abs_err(out_f64(out), ref)
+        assert err <= TOL[dt], f"P={P}: {err}"
+        assert np.array_equal(bits(to_host(dev.k, dt)), bits(kc))
+        assert np.array_equal(bits(to_host(dev.v, dt)), bits(vc))
+
+
+@pytest.mark.parametrize("kernel,dtype,S", [("auto", "bf16", 16), ("valu", "bf16", 32),
+                                            ("auto", "f32", 16)])
+def test_fused_edge_lengths(kernel, dtype, S):
+    lens = np.array([1, 2, S - 1, S, S + 1, 32, 33, 64, 65, 0, 97], dtype=np.int32)
+    cfg = _cfg("c3", dtype=dtype, block_size=S, num_seqs=len(lens), num_blocks=300, len_hi=100)
+    wl = W.generate(cfg, lens=lens)
+    kc, vc = oracle_pools(wl)
+    ref = oracle_out(wl, pools=(kc, vc))
+    for P in (0, S, 32):
+        dev = upload(wl)
+        o = out_f64(run_step(dev, wl, kernel=kernel, partition_size=P, fused=True))
+        assert oracle.max_abs_err(o, ref) <= TOL[dtype], f"P={P}"
+        assert not o[9].any()
+        assert np.array_equal(bits(to_host(dev.k, dtype)), bits(kc))
+        assert np.array_equal(bits(to_host(dev.v, dtype)), bits(vc))
+    # a one-position context is exactly its value row
+    one = run_step(upload(wl), wl, kernel=kernel, fused=True)
+    assert np.array_equal(bits(to_host(one, dtype)[0]), bits(np.repeat(wl.value[0], cfg.group, 0)))
+
+
+@pytest.mark.parametrize("name,kernel,P", [("c4", "auto", 0), ("c3", "auto", 64),
+                                           ("c3", "valu", 0), ("c5", "auto", 64)])
+def test_cached_loads_give_the_same_bits(name, kernel, P):
+    wl = W.generate(_cfg(name))
+    a = run_step(upload(wl), wl, kernel=kernel, partition_size=P)
+    b = run_step(upload(wl), wl, kernel=kernel, partition_size=P, cached_kv=True)
+    assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
 @pytest.mark.parametrize("name", ["c3", "c5"])
 def test_repeated_runs_are_bit_identical(name):
     wl = W.generate(_cfg(name))
@@ -219,11 +273,12 @@ def test_partials_match_oracle(name, kernel, P):
 def test_full_size_sampled_against_oracle(name):
     """The full workload in the launch configuration the benchmark times."""
     from bench import LAUNCH
-    kernel, P = LAUNCH[name]
+    kernel, P, cached = LAUNCH[name]
     cfg = W.CONFIGS[name]
     wl = W.generate(cfg)
     dev = upload(wl)
-    out = out_f64(run_step(dev, wl, kernel=kernel, partition_size=P, order=wl.longest_first()))
+    out = out_f64(run_step(dev, wl, kernel=kernel, partition_size=P, order=wl.longest_first(),
+                           fused=True, cached_kv=cached))
     assert np.isfinite(out).all()
     L = wl.context_lens
     rng = np.random.default_rng(0)
