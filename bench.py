@@ -27,14 +27,14 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published peak
 
 # Launch configuration the benchmark uses for each workload: (kernel family, partition size,
 # cached K/V loads). With longest-first dispatch, single-pass decode is fastest up to 4k-token
-# contexts; the lognormal long-context batch (up to ~31k tokens) splits into 1024-token
+# contexts; the lognormal long-context batch (up to ~31k tokens) splits into 2048-token
 # partitions; the prefix-shared batch keeps K/V in cache so the shared prefix is reused.
 LAUNCH = {
     "c1": ("auto", 0, False),
     "c2": ("auto", 0, False),
     "c3": ("auto", 0, False),
     "c4": ("auto", 0, True),
-    "c5": ("auto", 1024, False),
+    "c5": ("auto", 2048, False),
 }
 
 
@@ -143,8 +143,8 @@ def main():
     key, value = dev(wl.key, bf), dev(wl.value, bf)
     slots, bt, lens = dev(wl.slot_mapping), dev(wl.block_tables), dev(wl.context_lens)
     mapping = dev(wl.block_mapping.reshape(-1, 2))
-    # Host-side scheduler input: dispatch the longest contexts first.
-    order = dev(wl.longest_first())
+    # Host-side scheduler input: the units with work, largest first.
+    order = dev(wl.work_items(P))
     out = torch.empty((cfg.num_seqs, cfg.num_heads, cfg.head_dim), dtype=dt, device="cuda")
     ws = pk.partition_workspace(cfg.num_seqs, cfg.num_heads, cfg.head_dim, wl.max_context_len,
                                 P, q.device) if P else None
@@ -164,7 +164,7 @@ def main():
             e0.record()
         # With fused=True the decode launch also writes each sequence's newest K/V to its slot.
         pk.paged_attention_decode(None if P else out, q, kc, vc, bt, lens, maxlen, cfg.scale,
-                                  P, ws, kernel=kernel, work_order=order, cached_kv=cached,
+                                  P, ws, kernel=kernel, work_items=order, cached_kv=cached,
                                   new_key=key if fused else None,
                                   new_value=value if fused else None)
         if record:

@@ -51,10 +51,10 @@
  *
  * Caller contract that is not checked (it would need a device-to-host copy): block ids are in
  * [0, N); L_i <= MB * S and L_i <= max_context_len; slots are distinct; copy pairs have
- * distinct destinations and no destination is also a source; work_order is a permutation. So
- * that a broken contract can
+ * distinct destinations and no destination is also a source; the work list is as described
+ * at pkv_paged_attention_decode. So that a broken contract can
  * never make a kernel touch memory outside the buffers: kernels clamp block ids into [0, N),
- * work_order entries into [0, B), L_i into [0, MB * S] (and the partition count into
+ * work items into [0, B * NP), L_i into [0, MB * S] (and the partition count into
  * [0, NPmax]) and skip slots outside [0, N * S); the results for the affected sequences are
  * then undefined.
  *
@@ -105,18 +105,22 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cac
  * Source: vAttention section 3.1 (attention over non-contiguous KV-cache blocks); Qualiteg
  * post items 1-2 and 2-1 (blocks, block table, no padding).
  * out, q: device [B, H, D]; k_cache, v_cache: device pools of num_blocks blocks;
- * block_tables: device int32 [B, MB]; context_lens: device int32 [B]; work_order: NULL or a
- * device int32 [B] permutation of 0..B-1 -- workgroups of sequence work_order[0] are
- * dispatched first, then work_order[1], ...; passing the sequences longest first lets short
- * contexts fill in behind long ones instead of leaving a tail of long ones running alone
- * (longest-processing-time-first scheduling). The result does not depend on the order.
+ * block_tables: device int32 [B, MB]; context_lens: device int32 [B].
+ * work_items / num_work_items: NULL (all B * NP units in index order), or a device int32 list of
+ * num_work_items units u = i * NP + p (sequence i, range p; NP = 1 in single-pass mode, else
+ * ceil(max_context_len / partition_size)) in the order they are to be dispatched. The list
+ * must hold every unit that has work -- each sequence in single-pass mode, each (i, p) with
+ * p < ceil(L_i / partition_size) in split mode -- exactly once; units left out are not
+ * computed. Listing the largest units first (longest-processing-time-first) lets small units
+ * fill in behind large ones instead of leaving a tail, and leaving out empty partitions keeps
+ * them from occupying workgroup slots; the result does not depend on the order.
  * max_context_len: a host-side upper bound of every L_i (sizes the partition grid); scale:
  * the logit scale (usually 1/sqrt(D)). L_i = 0 gives a zero output row (single pass) or no
  * partials. */
 pkv_status pkv_paged_attention_decode(
     void* out, const void* q, const void* k_cache, const void* v_cache,
     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-    const int32_t* work_order, int32_t max_context_len, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    const int32_t* work_items, int32_t num_work_items, int32_t max_context_len, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
     int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, pkv_dtype dtype,
     int32_t partition_size, float* max_logits, float* exp_sums, float* tmp_out, void* stream);
 
@@ -145,7 +149,7 @@ typedef struct {
 pkv_status pkv_paged_attention_decode_ex(
     const pkv_decode_options* options, void* out, const void* q, void* k_cache, void* v_cache,
     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-    const int32_t* work_order, int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+    const int32_t* work_items, int32_t num_work_items, int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
     pkv_dtype dtype, int32_t partition_size, float* max_logits, float* exp_sums,
     float* tmp_out, void* stream);

@@ -34,9 +34,9 @@ _OPT = ctypes.POINTER(DecodeOptions)
 SIGNATURES = {
     "pkv_reshape_and_cache": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pkv_paged_attention_decode": (_I, [_P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I,
-                                        _I, _F, _I, _I, _P, _P, _P, _P]),
+                                        _I, _I, _F, _I, _I, _P, _P, _P, _P]),
     "pkv_paged_attention_decode_ex": (_I, [_OPT, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I,
-                                           _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P]),
+                                           _I, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P]),
     "pkv_paged_attention_reduce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pkv_copy_blocks": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pkv_partition_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
@@ -155,11 +155,12 @@ def partition_workspace(num_seqs, num_heads, head_dim, max_context_len, partitio
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
                            max_context_len, scale, partition_size=0, workspace=None,
-                           kernel="auto", work_order=None, cached_kv=False, new_key=None,
+                           kernel="auto", work_items=None, cached_kv=False, new_key=None,
                            new_value=None):
     """pkv_paged_attention_decode_ex. Single pass writes `out`; with partition_size > 0 it
-    writes only `workspace` = (max_logits, exp_sums, tmp_out). work_order: optional device int32
-    [B] dispatch order of the sequences (longest first shortens the tail). cached_kv: ordinary
+    writes only `workspace` = (max_logits, exp_sums, tmp_out). work_items: optional device int32
+    list of units i * NP + p in dispatch order (largest first shortens the tail; see
+    workload.Workload.work_items). cached_kv: ordinary
     cached K/V loads (for block tables that share blocks). new_key/new_value: optional
     [B, Hkv, D] newest-token rows, written to the cache and attended to in the same launch."""
     _need(q, "q", ndim=3)
@@ -176,10 +177,8 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     _need(context_lens, "context_lens", torch.int32, 1, q.device)
     if block_tables.shape[0] != B or context_lens.shape[0] != B:
         raise ValueError("block_tables/context_lens must have one row per sequence")
-    if work_order is not None:
-        _need(work_order, "work_order", torch.int32, 1, q.device)
-        if work_order.shape[0] != B:
-            raise ValueError("work_order must have one entry per sequence")
+    if work_items is not None:
+        _need(work_items, "work_items", torch.int32, 1, q.device)
     if (new_key is None) != (new_value is None):
         raise ValueError("new_key and new_value go together")
     if new_key is not None:
@@ -208,8 +207,8 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
                          None if new_value is None else new_value.data_ptr())
     _check(lib.pkv_paged_attention_decode_ex(
         ctypes.byref(opts), _ptr(out) if not partition_size else None, _ptr(q), _ptr(k_cache),
-        _ptr(v_cache), _ptr(block_tables), MB, _ptr(context_lens), _ptr(work_order),
-        int(max_context_len), B, H,
+        _ptr(v_cache), _ptr(block_tables), MB, _ptr(context_lens), _ptr(work_items),
+        0 if work_items is None else work_items.shape[0], int(max_context_len), B, H,
         Hkv, D, S, N, float(scale), _dt(q), int(partition_size), _ptr(ml), _ptr(es), _ptr(to),
         _stream(q)))
 
@@ -253,10 +252,10 @@ def copy_blocks(k_caches, v_caches, block_mapping):
 
 
 def paged_attention(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
-                    scale, partition_size=0, workspace=None, kernel="auto", work_order=None,
+                    scale, partition_size=0, workspace=None, kernel="auto", work_items=None,
                     cached_kv=False, new_key=None, new_value=None):
     """The whole decode: single pass, or partitions then their merge, on the current stream."""
-    kw = dict(kernel=kernel, work_order=work_order, cached_kv=cached_kv, new_key=new_key,
+    kw = dict(kernel=kernel, work_items=work_items, cached_kv=cached_kv, new_key=new_key,
               new_value=new_value)
     if partition_size:
         B, H, D = q.shape

@@ -54,7 +54,8 @@ pkv_status check_tile(const char* fn, int32_t num_kv_heads, int32_t head_dim,
 pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, void* k_cache,
                        void* v_cache, const int32_t* block_tables,
                        int32_t max_blocks_per_seq, const int32_t* context_lens,
-                       const int32_t* work_order, int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                       const int32_t* work_items, int32_t num_work_items,
+                       int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                        int32_t num_blocks, float scale, pkv_dtype dtype,
                        int32_t partition_size, float* max_logits, float* exp_sums,
@@ -88,7 +89,7 @@ pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, 
   }
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       (!partial && !aligned(out, 16)) || !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
-      (work_order && !aligned(work_order, 4)))
+      (work_items && !aligned(work_items, 4)))
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: a tensor pointer is null or misaligned", fn);
   static const pkv_decode_options defaults = {PKV_KERNEL_AUTO, 0u, nullptr, nullptr};
   if (!opt) opt = &defaults;
@@ -111,7 +112,12 @@ pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, 
     return fail(PKV_ERR_UNSUPPORTED, "%s: the VALU kernel takes query groups up to 8", fn);
 
   const int64_t ranges = partial ? ((int64_t)max_context_len + partition_size - 1) / partition_size : 1;
-  const int64_t grid = (int64_t)num_seqs * ranges * num_kv_heads;
+  if (work_items && num_work_items < 0)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: num_work_items %d", fn, num_work_items);
+  const int64_t units = work_items ? (int64_t)num_work_items : (int64_t)num_seqs * ranges;
+  if ((int64_t)num_seqs * ranges > INT32_MAX)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: %lld units", fn, (long long)num_seqs * ranges);
+  const int64_t grid = units * num_kv_heads;
   if (grid > INT32_MAX) return fail(PKV_ERR_INVALID_ARGUMENT, "%s: grid of %lld workgroups", fn, (long long)grid);
   if (grid == 0) return PKV_OK;
 
@@ -122,7 +128,8 @@ pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, 
   p.v_cache = v_cache;
   p.block_tables = block_tables;
   p.context_lens = context_lens;
-  p.work_order = work_order;
+  p.work_items = work_items;
+  p.num_units = (int32_t)units;
   p.new_key = opt->new_key;
   p.new_value = opt->new_value;
   p.max_logits = max_logits;
@@ -178,14 +185,14 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cac
 pkv_status pkv_paged_attention_decode(
     void* out, const void* q, const void* k_cache, const void* v_cache,
     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-    const int32_t* work_order, int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+    const int32_t* work_items, int32_t num_work_items, int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
     pkv_dtype dtype, int32_t partition_size, float* max_logits, float* exp_sums,
     float* tmp_out, void* stream) {
   // Without new rows the kernels never write the pools.
   return decode_impl(nullptr, out, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
-                     block_tables, max_blocks_per_seq, context_lens, work_order,
-                     max_context_len, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                     block_tables, max_blocks_per_seq, context_lens, work_items,
+                     num_work_items, max_context_len, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                      num_blocks, scale, dtype, partition_size, max_logits, exp_sums, tmp_out,
                      stream);
 }
@@ -193,12 +200,13 @@ pkv_status pkv_paged_attention_decode(
 pkv_status pkv_paged_attention_decode_ex(
     const pkv_decode_options* options, void* out, const void* q, void* k_cache, void* v_cache,
     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-    const int32_t* work_order, int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+    const int32_t* work_items, int32_t num_work_items, int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
     pkv_dtype dtype, int32_t partition_size, float* max_logits, float* exp_sums,
     float* tmp_out, void* stream) {
   return decode_impl(options, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
-                     context_lens, work_order, max_context_len, num_seqs, num_heads,
+                     context_lens, work_items, num_work_items, max_context_len, num_seqs,
+                     num_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
                      partition_size, max_logits, exp_sums, tmp_out, stream);
 }

@@ -44,6 +44,14 @@ template <> struct Mfma<Dt::F16> {
   static __device__ __forceinline__ _Float16 narrow(float x) { return (_Float16)x; }
 };
 
+// Waits until at most N vector memory operations of this wave are outstanding (and keeps the
+// compiler from moving memory accesses across the wait).
+template <int N>
+__device__ __forceinline__ void wait_vm_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 template <Dt DT, int D, int S, int NW, bool PARTIAL, bool NTL>
 __global__ void __launch_bounds__(NW * 64)
 decode_mfma_kernel(const DecodeParams a) {
@@ -58,11 +66,20 @@ decode_mfma_kernel(const DecodeParams a) {
   using V8 = typename M::V8;
   using T = typename Elt<DT>::T;
 
-  __shared__ float sh_m[NW][16];
-  __shared__ float sh_l[NW][16];
-  __shared__ float sh_acc[NW][16][D];
+  // K of a chunk is staged in LDS: each wave owns two slots of CT rows; a row's sixteen-byte
+  // pieces are rotated by rot(t) so that the operand reads below hit distinct banks. After the
+  // chunk loop the same space holds the merge buffers.
+  constexpr int RB = D * EB;        // bytes of one K row
+  constexpr int NPC = RB / 16;      // sixteen-byte pieces per K row
+  constexpr int SLOT = CT * RB;     // one chunk of K
+  constexpr int KLD = SLOT / 1024;  // 1 KiB direct-to-LDS loads per chunk
+  static_assert((NW * 16 * D + 2 * NW * 16) * 4 <= NW * 2 * SLOT, "merge fits the staging area");
+  __shared__ __attribute__((aligned(16))) char smem[NW * 2 * SLOT];
   __shared__ float sh_new[16];
   __shared__ float sh_vnew[D];
+  auto sh_acc = reinterpret_cast<float (*)[16][D]>(smem);
+  auto sh_m = reinterpret_cast<float (*)[16]>(smem + NW * 16 * D * 4);
+  auto sh_l = reinterpret_cast<float (*)[16]>(smem + (NW * 16 * D + NW * 16) * 4);
 
   const int Hkv = a.num_kv_heads;
   const int H = a.num_heads;
@@ -70,10 +87,11 @@ decode_mfma_kernel(const DecodeParams a) {
   const int MB = a.max_blocks_per_seq;
   const int w = blockIdx.x;
   const int g = w % Hkv;  // consecutive workgroups take different kv heads (XCD round robin)
-  const int rest = w / Hkv;
-  const int part = rest % a.num_ranges;
-  const int slot = rest / a.num_ranges;
-  const int i = a.work_order ? min(max(a.work_order[slot], 0), a.num_seqs - 1) : slot;
+  const int slot = w / Hkv;
+  int unit = a.work_items ? a.work_items[slot] : slot;
+  unit = min(max(unit, 0), a.num_seqs * a.num_ranges - 1);
+  const int part = unit % a.num_ranges;
+  const int i = unit / a.num_ranges;
   const int lane = lane_id();
   const int wave = wave_id();
   const int r = lane >> 4;
@@ -121,10 +139,9 @@ decode_mfma_kernel(const DecodeParams a) {
   const size_t id_stride = (size_t)Hkv * tile_bytes;
   const char* kpool = reinterpret_cast<const char*>(a.k_cache) + (size_t)g * tile_bytes;
   const char* vpool = reinterpret_cast<const char*>(a.v_cache) + (size_t)g * tile_bytes;
-  // K: row tau = 8(c/4) + (c%4) (+4 for the second product) of block tau / S.
+  // K: this lane's operand rows are chunk positions t = 8(c/4) + (c%4) (+4 for the second
+  // product), pieces 4 kk + r.
   const int k_tau = 8 * (c >> 2) + (c & 3);
-  const int k_blk = k_tau / S;
-  const int k_off = (k_tau % S) * D * EB + r * 16;  // + gi * 4 rows + kk * 64
   // V^T: row d = 16 nt + c, positions 8r .. 8r+7 of block 8r / S.
   const int v_blk = (8 * r) / S;
   const int v_off = c * S * EB + ((8 * r) % S) * EB;  // + nt * 16 rows
@@ -144,20 +161,38 @@ decode_mfma_kernel(const DecodeParams a) {
   };
 
   struct Regs {
-    u32x4 k[2][KK];
     u32x4 v[NT];
   };
+  auto rot = [](int t) { return t + 4 * (t >> 4); };
 
-  auto load = [&](const Ids& ids, Regs& R) {
-    const char* kt = kpool + (size_t)(k_blk ? ids.b1 : ids.b0) * id_stride + k_off;
+  // Chunk loads: K with KLD coalesced 1 KiB direct-to-LDS loads into the wave's slot (lane l of
+  // load x fills row t = x * (1024 / RB) + l / NPC, rotated piece l % NPC), V^T straight into
+  // registers (16 contiguous bytes per lane).
+  auto load = [&](const Ids& ids, Regs& R, int slot) {
+    char* dst = smem + (wave * 2 + slot) * SLOT;
+#pragma unroll
+    for (int x = 0; x < KLD; ++x) {
+      const int t = x * (1024 / RB) + lane / NPC;
+      const int jt = (lane % NPC - rot(t)) & (NPC - 1);
+      const int blk = (BPC == 2 && t >= S) ? ids.b1 : ids.b0;
+      const char* src = kpool + (size_t)blk * id_stride + (t % S) * RB + jt * 16;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + x * 1024),
+                                       16, 0, NTL ? 2 : 0);
+    }
     const char* vt = vpool + (size_t)(v_blk ? ids.b1 : ids.b0) * id_stride + v_off;
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi)
+    for (int nt = 0; nt < NT; ++nt) R.v[nt] = load_kv<NTL, u32x4>(vt + nt * 16 * S * EB);
+  };
+  // Operand pieces of chunk K from the wave's slot.
+  auto read_k = [&](int slot, u32x4 (&kr)[2][KK]) {
+    const char* src = smem + (wave * 2 + slot) * SLOT;
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int t = k_tau + 4 * gi;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        R.k[gi][kk] = load_kv<NTL, u32x4>(kt + gi * 4 * D * EB + kk * 64);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) R.v[nt] = load_kv<NTL, u32x4>(vt + nt * 16 * S * EB);
+        kr[gi][kk] = *reinterpret_cast<const u32x4*>(src + t * RB + ((4 * kk + r + rot(t)) & (NPC - 1)) * 16);
+    }
   };
 
   float m = -INFINITY, l = 0.0f;
@@ -165,12 +200,14 @@ decode_mfma_kernel(const DecodeParams a) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto compute = [&](int n, Regs& R) {
+  auto compute = [&](int n, Regs& R, int slot) {
+    u32x4 kr[2][KK];
+    read_k(slot, kr);
     f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      s0 = M::mac(__builtin_bit_cast(V8, R.k[0][kk]), qb[kk], s0);
-      s1 = M::mac(__builtin_bit_cast(V8, R.k[1][kk]), qb[kk], s1);
+      s0 = M::mac(__builtin_bit_cast(V8, kr[0][kk]), qb[kk], s0);
+      s1 = M::mac(__builtin_bit_cast(V8, kr[1][kk]), qb[kk], s1);
     }
     const int pos0 = start + n * CT + 8 * r;  // position of this lane's first logit
     float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
@@ -265,24 +302,32 @@ decode_mfma_kernel(const DecodeParams a) {
     Ids ids;
     ids.b0 = clamp_id(first0);
     ids.b1 = (BPC == 2 && b_first + 1 < blk_end) ? clamp_id(first1) : ids.b0;
-    load(ids, A);
+    load(ids, A, 0);
     if (n + NW < nch) ids = fetch_ids(n + NW);
     if (fused) use_new_rows();
-    // Two register sets: chunk n + NW loads while chunk n computes; its block ids were
-    // fetched one step earlier still.
+    // Two stages: chunk n + NW loads while chunk n computes; its block ids were fetched one
+    // step earlier still. The LDS half of a chunk is not tracked by the compiler, so each
+    // step waits explicitly: vector memory operations complete in order, and exactly
+    // KLD + NT of them (the next chunk's) may still be in flight when chunk n is read.
     while (true) {
       if (n + NW < nch) {
-        load(ids, B);
+        load(ids, B, 1);
         if (n + 2 * NW < nch) ids = fetch_ids(n + 2 * NW);
+        wait_vm_le<KLD + NT>();
+      } else {
+        wait_vm_le<0>();
       }
-      compute(n, A);
+      compute(n, A, 0);
       n += NW;
       if (n >= nch) break;
       if (n + NW < nch) {
-        load(ids, A);
+        load(ids, A, 0);
         if (n + 2 * NW < nch) ids = fetch_ids(n + 2 * NW);
+        wait_vm_le<KLD + NT>();
+      } else {
+        wait_vm_le<0>();
       }
-      compute(n, B);
+      compute(n, B, 1);
       n += NW;
       if (n >= nch) break;
     }
@@ -306,6 +351,7 @@ decode_mfma_kernel(const DecodeParams a) {
   l = across16(l, OpAdd());
   l = across32(l, OpAdd());
 
+  __syncthreads();  // every wave is done with its staging slots: the merge buffers reuse them
   if (c < G) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -355,7 +401,7 @@ constexpr int kMfmaWaves = 4;
 
 template <Dt DT, int D, int S>
 hipError_t launch_s(bool partial, bool nt, const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)p.num_seqs * p.num_ranges * p.num_kv_heads);
+  const dim3 grid((unsigned)p.num_units * p.num_kv_heads);
   const dim3 block(kMfmaWaves * 64);
   if (partial) {
     if (nt) decode_mfma_kernel<DT, D, S, kMfmaWaves, true, true><<<grid, block, 0, stream>>>(p);

@@ -44,10 +44,11 @@ decode_valu_kernel(const DecodeParams a) {
   const int MB = a.max_blocks_per_seq;
   const int w = blockIdx.x;
   const int g = w % Hkv;  // consecutive workgroups take different kv heads (XCD round robin)
-  const int rest = w / Hkv;
-  const int part = rest % a.num_ranges;
-  const int slot = rest / a.num_ranges;
-  const int i = a.work_order ? min(max(a.work_order[slot], 0), a.num_seqs - 1) : slot;
+  const int slot = w / Hkv;
+  int unit = a.work_items ? a.work_items[slot] : slot;
+  unit = min(max(unit, 0), a.num_seqs * a.num_ranges - 1);
+  const int part = unit % a.num_ranges;
+  const int i = unit / a.num_ranges;
   const int lane = lane_id();
   const int wave = wave_id();
   const int r = lane / LPR;
@@ -324,7 +325,7 @@ constexpr int kValuWaves = 4;
 
 template <Dt DT, int D, int S, int G>
 hipError_t launch_g(bool partial, bool nt, const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)p.num_seqs * p.num_ranges * p.num_kv_heads);
+  const dim3 grid((unsigned)p.num_units * p.num_kv_heads);
   const dim3 block(kValuWaves * 64);
   if (partial) {
     if (nt) decode_valu_kernel<DT, D, S, G, kValuWaves, true, true><<<grid, block, 0, stream>>>(p);

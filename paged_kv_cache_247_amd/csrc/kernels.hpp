@@ -18,7 +18,7 @@ struct DecodeParams {
   void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  const int32_t* work_order;  // NULL = sequence order
+  const int32_t* work_items;  // NULL = all units in index order; else unit = i * num_ranges + p
   const void* new_key;        // NULL, or [B, Hkv, D]: position L-1 of each sequence, fused write
   const void* new_value;
   float* max_logits;
@@ -31,6 +31,7 @@ struct DecodeParams {
   int32_t num_blocks;
   int32_t range_tokens;
   int32_t num_ranges;
+  int32_t num_units;  // grid units (work items, or num_seqs * num_ranges)
   float scale_log2e;
 };
 

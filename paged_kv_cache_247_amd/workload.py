@@ -180,11 +180,27 @@ class Workload:
     def total_tokens(self) -> int:
         return int(self.context_lens.astype(np.int64).sum())
 
-    def longest_first(self) -> np.ndarray:
-        """Host-side dispatch order for decode: sequence indices by decreasing context length
-        (ties in index order). Any permutation gives the same result; this one lets short
-        sequences fill in behind long ones."""
-        return np.argsort(-self.context_lens.astype(np.int64), kind="stable").astype(np.int32)
+    def work_items(self, partition_size: int = 0) -> np.ndarray:
+        """Host-side decode schedule: the units that have work, largest first.
+
+        A unit is i * NP + p (sequence i, range p) with NP = 1 in single-pass mode (every
+        sequence is listed, empty ones too: they get a zero row) and NP = ceil(max_context_len
+        / partition_size) in split mode (only p < ceil(L_i / partition_size)). Ties keep index
+        order. Any order gives the same result; largest-first lets small units fill in behind
+        large ones."""
+        L = self.context_lens.astype(np.int64)
+        if partition_size <= 0:
+            return np.argsort(-L, kind="stable").astype(np.int32)
+        P = int(partition_size)
+        NP = max(-(-self.max_context_len // P), 1)
+        units, sizes = [], []
+        for i, Li in enumerate(L):
+            for p in range(-(-int(Li) // P)):
+                units.append(i * NP + p)
+                sizes.append(min(P, int(Li) - p * P))
+        units = np.asarray(units, dtype=np.int64)
+        order = np.argsort(-np.asarray(sizes, dtype=np.int64), kind="stable")
+        return units[order].astype(np.int32)
 
     def kv_bytes(self) -> int:
         """Algorithmic KV bytes one decode call reads: sum_i L_i * Hkv * D * elt * 2."""

@@ -59,7 +59,8 @@ def upload(wl) -> Dev:
 def run_step(dev: Dev, wl, kernel="auto", partition_size=None, tables=None, copy=True,
              order=None, fused=False, cached_kv=False):
     """copy_blocks (if the workload has pairs) -> reshape_and_cache -> decode (+ reduce).
-    order: optional host int32 dispatch order of the sequences. fused: the decode call writes
+    order: optional host int32 work list (units i * NP + p, see Workload.work_items). fused:
+    the decode call writes
     the newest tokens itself (no reshape_and_cache). cached_kv: cached K/V loads."""
     c = wl.cfg
     P = c.partition_size if partition_size is None else partition_size
@@ -71,7 +72,7 @@ def run_step(dev: Dev, wl, kernel="auto", partition_size=None, tables=None, copy
                      dtype=TORCH_DT[c.dtype], device="cuda")
     pk.paged_attention(out, dev.q, dev.k, dev.v, dev.bt if tables is None else tables, dev.lens,
                        wl.max_context_len, c.scale, P, kernel=kernel,
-                       work_order=None if order is None else to_dev(np.asarray(order, np.int32)),
+                       work_items=None if order is None else to_dev(np.asarray(order, np.int32)),
                        cached_kv=cached_kv, new_key=dev.key if fused else None,
                        new_value=dev.value if fused else None)
     torch.cuda.synchronize()

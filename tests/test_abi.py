@@ -56,12 +56,12 @@ def test_workspace_bytes(lib):
 def decode(lib, **kw):
     a = dict(kernel=0, out=A16, q=A16, k=A16, v=A16, bt=A16, MB=4, lens=A16, maxlen=64, B=2,
              H=8, Hkv=2, D=128, S=16, N=32, scale=0.125, dtype=2, P=0, ml=None, es=None, to=None,
-             order=None, flags=0, nk=None, nv=None)
+             order=None, nitems=0, flags=0, nk=None, nv=None)
     a.update(kw)
     opts = _lib.DecodeOptions(a["kernel"], a["flags"], a["nk"], a["nv"])
     return lib.pkv_paged_attention_decode_ex(
         ctypes.byref(opts), a["out"], a["q"], a["k"], a["v"], a["bt"], a["MB"], a["lens"],
-        a["order"], a["maxlen"],
+        a["order"], a["nitems"], a["maxlen"],
         a["B"], a["H"], a["Hkv"], a["D"], a["S"], a["N"], a["scale"], a["dtype"], a["P"],
         a["ml"], a["es"], a["to"], None)
 
@@ -80,6 +80,8 @@ def decode(lib, **kw):
     (dict(k=A16 + 8), INVALID),
     (dict(bt=A16 + 2), INVALID),
     (dict(order=A16 + 2), INVALID),
+    (dict(order=A16, nitems=-1), INVALID),
+    (dict(order=A16, nitems=0), OK),  # an empty work list: nothing enqueued
     (dict(maxlen=65), INVALID),  # above MB * S
     (dict(maxlen=-1), INVALID),
     (dict(N=0), INVALID),

@@ -168,14 +168,30 @@ def test_shared_prefix_equals_private_copy_bit_identical(kernel):
 
 @pytest.mark.parametrize("name,kernel,P", [("c3", "auto", 0), ("c3", "auto", 64),
                                            ("c5", "auto", 64), ("c2", "auto", 0),
-                                           ("c3", "valu", 32), ("c1", "auto", 0)])
-def test_work_order_does_not_change_the_result(name, kernel, P):
+                                           ("c3", "valu", 32), ("c1", "auto", 0),
+                                           ("c1", "auto", 16)])
+def test_work_list_does_not_change_the_result(name, kernel, P):
+    """Largest-first, reversed and shuffled work lists give bit-identical output."""
     wl = W.generate(_cfg(name))
     base = run_step(upload(wl), wl, kernel=kernel, partition_size=P)
-    for order in (wl.longest_first(),
-                  np.random.default_rng(3).permutation(wl.cfg.num_seqs).astype(np.int32)):
+    items = wl.work_items(P)
+    rng = np.random.default_rng(3)
+    for order in (items, items[::-1].copy(), rng.permutation(items)):
         got = run_step(upload(wl), wl, kernel=kernel, partition_size=P, order=order)
         assert torch.equal(got.view(torch.uint8), base.view(torch.uint8))
+
+
+def test_work_list_skips_empty_partitions():
+    """Split mode with only the non-empty units listed: empty contexts still read as zeros."""
+    cfg = _cfg("c3")
+    lens = np.array([0, 5, 130, 0, 64, 400], dtype=np.int32)
+    wl = W.generate(cfg, lens=lens)
+    items = wl.work_items(64)
+    assert len(items) == 1 + 3 + 1 + 7
+    out = run_step(upload(wl), wl, partition_size=64, order=items)
+    ref = oracle_out(wl)
+    assert oracle.max_abs_err(out_f64(out), ref) <= TOL["bf16"]
+    assert not out_f64(out)[[0, 3]].any()
 
 
 FUSED = [("c1", {}, "auto", (0, 16)), ("c2", {}, "auto", (0, 64)), ("c3", {}, "auto", (0, 32)),
@@ -277,7 +293,7 @@ def test_full_size_sampled_against_oracle(name):
     cfg = W.CONFIGS[name]
     wl = W.generate(cfg)
     dev = upload(wl)
-    out = out_f64(run_step(dev, wl, kernel=kernel, partition_size=P, order=wl.longest_first(),
+    out = out_f64(run_step(dev, wl, kernel=kernel, partition_size=P, order=wl.work_items(P),
                            fused=True, cached_kv=cached))
     assert np.isfinite(out).all()
     L = wl.context_lens
