@@ -73,13 +73,16 @@ decode_mfma_kernel(const DecodeParams a) {
   constexpr int NPC = RB / 16;      // sixteen-byte pieces per K row
   constexpr int SLOT = CT * RB;     // one chunk of K
   constexpr int KLD = SLOT / 1024;  // 1 KiB direct-to-LDS loads per chunk
-  static_assert((NW * 16 * D + 2 * NW * 16) * 4 <= NW * 2 * SLOT, "merge fits the staging area");
+  // Accumulator rows are padded by 16 bytes: lanes of one row group write the same columns of
+  // sixteen different head rows, which must not share banks.
+  constexpr int DP = D + 4;
+  static_assert((NW * 16 * DP + 2 * NW * 16) * 4 <= NW * 2 * SLOT, "merge fits the staging area");
   __shared__ __attribute__((aligned(16))) char smem[NW * 2 * SLOT];
   __shared__ float sh_new[16];
   __shared__ float sh_vnew[D];
-  auto sh_acc = reinterpret_cast<float (*)[16][D]>(smem);
-  auto sh_m = reinterpret_cast<float (*)[16]>(smem + NW * 16 * D * 4);
-  auto sh_l = reinterpret_cast<float (*)[16]>(smem + (NW * 16 * D + NW * 16) * 4);
+  auto sh_acc = reinterpret_cast<float (*)[16][DP]>(smem);
+  auto sh_m = reinterpret_cast<float (*)[16]>(smem + NW * 16 * DP * 4);
+  auto sh_l = reinterpret_cast<float (*)[16]>(smem + (NW * 16 * DP + NW * 16) * 4);
 
   const int Hkv = a.num_kv_heads;
   const int H = a.num_heads;
