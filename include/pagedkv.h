@@ -105,7 +105,10 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cac
  * Source: vAttention section 3.1 (attention over non-contiguous KV-cache blocks); Qualiteg
  * post items 1-2 and 2-1 (blocks, block table, no padding).
  * out, q: device [B, H, D]; k_cache, v_cache: device pools of num_blocks blocks;
- * block_tables: device int32 [B, MB]; context_lens: device int32 [B].
+ * block_tables: device int32 [B, MB], or NULL for the conventional contiguous reservation
+ * (sequence i owns pool blocks i * MB .. i * MB + MB - 1, addressed without a table; needs
+ * num_blocks >= B * MB) -- the layout paging replaces, kept to measure what the block table
+ * costs the kernel; MFMA kernel only); context_lens: device int32 [B].
  * work_items / num_work_items: NULL (all B * NP units in index order), or a device int32 list of
  * num_work_items units u = i * NP + p (sequence i, range p; NP = 1 in single-pass mode, else
  * ceil(max_context_len / partition_size)) in the order they are to be dispatched. The list

@@ -156,13 +156,15 @@ def partition_workspace(num_seqs, num_heads, head_dim, max_context_len, partitio
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
                            max_context_len, scale, partition_size=0, workspace=None,
                            kernel="auto", work_items=None, cached_kv=False, new_key=None,
-                           new_value=None):
+                           new_value=None, max_blocks_per_seq=None):
     """pkv_paged_attention_decode_ex. Single pass writes `out`; with partition_size > 0 it
     writes only `workspace` = (max_logits, exp_sums, tmp_out). work_items: optional device int32
     list of units i * NP + p in dispatch order (largest first shortens the tail; see
     workload.Workload.work_items). cached_kv: ordinary
     cached K/V loads (for block tables that share blocks). new_key/new_value: optional
-    [B, Hkv, D] newest-token rows, written to the cache and attended to in the same launch."""
+    [B, Hkv, D] newest-token rows, written to the cache and attended to in the same launch.
+    block_tables=None selects the contiguous reservation (sequence i owns pool blocks
+    i * max_blocks_per_seq onwards; max_blocks_per_seq is then required)."""
     _need(q, "q", ndim=3)
     dt = q.dtype
     B, H, D = q.shape
@@ -173,10 +175,18 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     _need(v_cache, "v_cache", dt, 4, q.device)
     if tuple(v_cache.shape) != (N, Hkv, D, S):
         raise ValueError("v_cache must be [N, Hkv, D, S]")
-    _need(block_tables, "block_tables", torch.int32, 2, q.device)
     _need(context_lens, "context_lens", torch.int32, 1, q.device)
-    if block_tables.shape[0] != B or context_lens.shape[0] != B:
-        raise ValueError("block_tables/context_lens must have one row per sequence")
+    if block_tables is None:  # contiguous reservation: max_blocks_per_seq blocks per sequence
+        if max_blocks_per_seq is None:
+            raise ValueError("max_blocks_per_seq is required without block tables")
+        MB = int(max_blocks_per_seq)
+    else:
+        _need(block_tables, "block_tables", torch.int32, 2, q.device)
+        MB = block_tables.shape[1]
+        if block_tables.shape[0] != B:
+            raise ValueError("block_tables must have one row per sequence")
+    if context_lens.shape[0] != B:
+        raise ValueError("context_lens must have one entry per sequence")
     if work_items is not None:
         _need(work_items, "work_items", torch.int32, 1, q.device)
     if (new_key is None) != (new_value is None):
@@ -186,7 +196,6 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
             _need(t, nm, dt, 3, q.device)
             if tuple(t.shape) != (B, Hkv, D):
                 raise ValueError(f"{nm} must be [B, Hkv, D]")
-    MB = block_tables.shape[1]
     ml = es = to = None
     if partition_size:
         if workspace is None:
@@ -253,10 +262,10 @@ def copy_blocks(k_caches, v_caches, block_mapping):
 
 def paged_attention(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
                     scale, partition_size=0, workspace=None, kernel="auto", work_items=None,
-                    cached_kv=False, new_key=None, new_value=None):
+                    cached_kv=False, new_key=None, new_value=None, max_blocks_per_seq=None):
     """The whole decode: single pass, or partitions then their merge, on the current stream."""
     kw = dict(kernel=kernel, work_items=work_items, cached_kv=cached_kv, new_key=new_key,
-              new_value=new_value)
+              new_value=new_value, max_blocks_per_seq=max_blocks_per_seq)
     if partition_size:
         B, H, D = q.shape
         if workspace is None:

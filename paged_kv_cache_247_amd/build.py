@@ -23,6 +23,11 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 SOURCES = ["api.cpp", "cache_ops.hip", "decode_valu.hip", "decode_mfma.hip", "reduce.hip"]
 ARCH = "gfx950"
+# Per-source extra flags. The decode MFMA kernel keeps its accumulators in ordinary VGPRs:
+# with the default heuristic the compiler puts them in AGPRs and copies them back and forth for
+# the per-chunk rescale, which costs instructions and pushes the 128-wide head past the
+# register budget of two waves per SIMD.
+EXTRA_FLAGS = {"decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -40,7 +45,8 @@ def common_flags():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), "-x", "hip", *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), "-x", "hip", *common_flags(), *EXTRA_FLAGS.get(src, []), "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

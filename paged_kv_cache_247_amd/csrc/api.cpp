@@ -88,9 +88,13 @@ pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, 
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: workspace pointers must be NULL in single-pass mode", fn);
   }
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-      (!partial && !aligned(out, 16)) || !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
-      (work_items && !aligned(work_items, 4)))
+      (!partial && !aligned(out, 16)) || (block_tables && !aligned(block_tables, 4)) ||
+      !aligned(context_lens, 4) || (work_items && !aligned(work_items, 4)))
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: a tensor pointer is null or misaligned", fn);
+  if (!block_tables && (int64_t)num_seqs * max_blocks_per_seq > num_blocks)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: without block tables the pool needs num_seqs * "
+                "max_blocks_per_seq = %lld blocks, it has %d", fn,
+                (long long)num_seqs * max_blocks_per_seq, num_blocks);
   static const pkv_decode_options defaults = {PKV_KERNEL_AUTO, 0u, nullptr, nullptr};
   if (!opt) opt = &defaults;
   if (opt->flags & ~(uint32_t)PKV_DECODE_CACHED_KV)
@@ -110,6 +114,8 @@ pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, 
     return fail(PKV_ERR_UNSUPPORTED, "%s: the MFMA kernel takes fp16/bf16 only", fn);
   if (!mfma && G > 8)
     return fail(PKV_ERR_UNSUPPORTED, "%s: the VALU kernel takes query groups up to 8", fn);
+  if (!mfma && !block_tables)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: the table-free contiguous layout runs on the MFMA kernel only", fn);
 
   const int64_t ranges = partial ? ((int64_t)max_context_len + partition_size - 1) / partition_size : 1;
   if (work_items && num_work_items < 0)

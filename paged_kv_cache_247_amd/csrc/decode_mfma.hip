@@ -23,6 +23,8 @@
 //     of the [D][S] tile -- and its B operand is exactly the eight weights it computed.
 //   The accumulator of tile nt holds O^T[16 nt + 4r + i][c]: the head is the lane's own
 //   column, so the online-softmax rescale uses the lane's own running max; no exchange.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace pkv {
@@ -44,15 +46,26 @@ template <> struct Mfma<Dt::F16> {
   static __device__ __forceinline__ _Float16 narrow(float x) { return (_Float16)x; }
 };
 
-// Waits until at most N vector memory operations of this wave are outstanding (and keeps the
-// compiler from moving memory accesses across the wait).
+// Waits until at most N vector memory operations of this wave are outstanding. The waitcnt
+// intrinsic touches no memory, so it does not count as a store that could alias the block
+// table (which keeps the table reads scalar); the scheduling barriers keep the LDS reads that
+// depend on the wait below it.
 template <int N>
 __device__ __forceinline__ void wait_vm_le() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  // s_waitcnt fields (gfx9): vmcnt[3:0] and [15:14], expcnt[6:4] (7 = no wait), lgkmcnt[11:8]
+  // (15 = no wait).
+  constexpr int kEnc = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(kEnc);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-template <Dt DT, int D, int S, int NW, bool PARTIAL, bool NTL>
+// Dword 3 of a raw buffer descriptor on gfx9-family chips: 32-bit data format, no swizzle,
+// no index stride.
+constexpr int kBufferFlags = 0x00020000;
+
+template <Dt DT, int D, int S, int NW, bool PARTIAL, bool NTL, bool TBL>
 __global__ void __launch_bounds__(NW * 64)
 decode_mfma_kernel(const DecodeParams a) {
   static_assert(DT == Dt::BF16 || DT == Dt::F16, "16-bit inputs only");
@@ -99,15 +112,27 @@ decode_mfma_kernel(const DecodeParams a) {
   const int wave = wave_id();
   const int r = lane >> 4;
   const int c = lane & 15;
+  // Physical block of logical block j: the sequence's table entry (TBL), or without tables the
+  // contiguous reservation of MB blocks per sequence (block i * MB + j).
   const int32_t* bt = a.block_tables + (size_t)i * MB;
+  const int contig0 = i * MB;
   const int start = part * a.range_tokens;
 
-  // Waves take chunks wave, wave + NW, ... of the range, so this wave's first chunk is known
-  // before the context length: its block ids are fetched now, in parallel with the length
-  // (any entry of the row may be read; ids are clamped into the pool before use).
-  const int b_first = start / S + wave * BPC;
-  int first0 = b_first < MB ? bt[b_first] : 0;
-  int first1 = (BPC == 2 && b_first + 1 < MB) ? bt[b_first + 1] : first0;
+  // Waves take chunks wave, wave + NW, ... of the range: local chunk m of this wave covers
+  // logical blocks start / S + (wave + NW m) BPC + e, e < BPC. The wave keeps the ids of CPB
+  // consecutive local chunks in one register, lane BPC (m % CPB) + e holding block e of local
+  // chunk m, and picks them out with readlane. One coalesced vector load fills it every CPB
+  // chunks. (The block table cannot be read through the scalar cache inside the loop: the
+  // direct-to-LDS loads count as writes to unknown memory, which rules scalar loads out.)
+  // The first batch is loaded now, in parallel with the context length; any entry of the row
+  // may be read and ids are clamped into the pool before use.
+  constexpr int CPB = 64 / BPC;
+  auto load_id_batch = [&](int kb) {
+    const int blk = start / S + (wave + NW * (kb * CPB + lane / BPC)) * BPC + lane % BPC;
+    return blk < MB ? bt[blk] : 0;
+  };
+  int id_batch = 0;
+  if constexpr (TBL) id_batch = load_id_batch(0);
 
   int L = a.context_lens[i];
   L = min(max(L, 0), MB * S);
@@ -151,15 +176,35 @@ decode_mfma_kernel(const DecodeParams a) {
 
   struct Ids {
     int b0, b1;
+    // This lane's V^T pieces of the chunk, formed with the ids a step early; pieces 4 KiB and
+    // more past vt are addressed from vt4 (= vt + 4 KiB, the reach of an immediate offset).
+    const char* vt;
+    const char* vt4;
   };
   auto clamp_id = [&](int id) { return min(max(id, 0), a.num_blocks - 1); };
-  // Physical ids of chunk n's blocks; a second block past the range reuses the first (its
-  // positions are masked).
-  auto fetch_ids = [&](int n) {
-    const int b0 = start / S + n * BPC;
+  // Physical ids of local chunk m's blocks; a second block past the range reuses the first (its
+  // positions are masked). Called for m = 0, 1, 2, ... in order.
+  auto fetch_ids = [&](int m) {
+    const int b0 = start / S + (wave + NW * m) * BPC;
     Ids ids;
-    ids.b0 = clamp_id(bt[b0]);
-    ids.b1 = (BPC == 2 && b0 + 1 < blk_end) ? clamp_id(bt[b0 + 1]) : ids.b0;
+    if constexpr (TBL) {
+      if (m > 0 && m % CPB == 0) {
+        id_batch = load_id_batch(m / CPB);
+        // Wait for the refill inside this rarely taken branch: a use here makes the compiler
+        // place its vmcnt wait now instead of before every readlane after the branches merge.
+        asm volatile("" : "+v"(id_batch));
+      }
+      const int sel = (m % CPB) * BPC;
+      ids.b0 = clamp_id(__builtin_amdgcn_readlane(id_batch, sel));
+      ids.b1 = (BPC == 2 && b0 + 1 < blk_end)
+                   ? clamp_id(__builtin_amdgcn_readlane(id_batch, sel + 1))
+                   : ids.b0;
+    } else {
+      ids.b0 = clamp_id(contig0 + b0);
+      ids.b1 = (BPC == 2 && b0 + 1 < blk_end) ? clamp_id(contig0 + b0 + 1) : ids.b0;
+    }
+    ids.vt = vpool + (size_t)(v_blk ? ids.b1 : ids.b0) * id_stride + v_off;
+    ids.vt4 = ids.vt + 4096;
     return ids;
   };
 
@@ -168,34 +213,59 @@ decode_mfma_kernel(const DecodeParams a) {
   };
   auto rot = [](int t) { return t + 4 * (t >> 4); };
 
-  // Chunk loads: K with KLD coalesced 1 KiB direct-to-LDS loads into the wave's slot (lane l of
-  // load x fills row t = x * (1024 / RB) + l / NPC, rotated piece l % NPC), V^T straight into
-  // registers (16 contiguous bytes per lane).
+  // Chunk loads: K with KLD coalesced 1 KiB buffer loads straight into the wave's LDS slot
+  // (lane l of load x fills row t = x * (1024 / RB) + l / NPC, rotated piece l % NPC), V^T
+  // straight into registers (16 contiguous bytes per lane). Each K block tile gets its own
+  // buffer descriptor (uniform, built with scalar arithmetic), so 32-bit offsets reach any
+  // pool size. The buffer form (rather than the global one) matters: the compiler counts it
+  // as an in-order vector memory operation, while a global load into LDS makes it flush the
+  // whole counter at every later wait.
+  static_assert(S % (1024 / RB) == 0, "a 1 KiB load stays within one block");
+  auto tile_rsrc = [&](int id) {
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(kpool + (size_t)id * id_stride), 0, (int)tile_bytes, kBufferFlags);
+  };
   auto load = [&](const Ids& ids, Regs& R, int slot) {
     char* dst = smem + (wave * 2 + slot) * SLOT;
+    const __amdgpu_buffer_rsrc_t r0 = tile_rsrc(ids.b0);
+    const __amdgpu_buffer_rsrc_t r1 = BPC == 2 ? tile_rsrc(ids.b1) : r0;
 #pragma unroll
     for (int x = 0; x < KLD; ++x) {
       const int t = x * (1024 / RB) + lane / NPC;
       const int jt = (lane % NPC - rot(t)) & (NPC - 1);
-      const int blk = (BPC == 2 && t >= S) ? ids.b1 : ids.b0;
-      const char* src = kpool + (size_t)blk * id_stride + (t % S) * RB + jt * 16;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + x * 1024),
-                                       16, 0, NTL ? 2 : 0);
+      const bool second = BPC == 2 && x * (1024 / RB) >= S;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          second ? r1 : r0, (__attribute__((address_space(3))) void*)(dst + x * 1024), 16,
+          (t % S) * RB + jt * 16, 0, 0, NTL ? 2 : 0);
     }
-    const char* vt = vpool + (size_t)(v_blk ? ids.b1 : ids.b0) * id_stride + v_off;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) R.v[nt] = load_kv<NTL, u32x4>(vt + nt * 16 * S * EB);
+    for (int nt = 0; nt < NT; ++nt) {
+      constexpr int kStep = 16 * S * EB;
+      const int off = nt * kStep;
+      R.v[nt] = load_kv<NTL, u32x4>(off < 4096 ? ids.vt + off : ids.vt4 + (off - 4096));
+    }
   };
-  // Operand pieces of chunk K from the wave's slot.
+  // Operand pieces of chunk K from the wave's slot. The reads are issued as inline LDS
+  // instructions that the compiler does not see as LDS reads, so it adds no waits of its own
+  // for the loads in flight into the other slot; the caller's vmcnt wait has made this slot's
+  // data visible, and the lgkmcnt wait below completes the reads before their results are used.
   auto read_k = [&](int slot, u32x4 (&kr)[2][KK]) {
     const char* src = smem + (wave * 2 + slot) * SLOT;
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
       const int t = k_tau + 4 * gi;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        kr[gi][kk] = *reinterpret_cast<const u32x4*>(src + t * RB + ((4 * kk + r + rot(t)) & (NPC - 1)) * 16);
+      for (int kk = 0; kk < KK; ++kk) {
+        const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(
+            src + t * RB + ((4 * kk + r + rot(t)) & (NPC - 1)) * 16);
+        asm volatile("ds_read_b128 %0, %1" : "=v"(kr[gi][kk]) : "v"(addr) : "memory");
+      }
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(kr[gi][kk]));
   };
 
   float m = -INFINITY, l = 0.0f;
@@ -203,7 +273,10 @@ decode_mfma_kernel(const DecodeParams a) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto compute = [&](int n, Regs& R, int slot) {
+  // Chunk n from the registers R and LDS slot. Only a wave's last chunk can reach past the end
+  // of the range (chunks are dealt round robin), so only that one (last = true) masks.
+  auto compute = [&](int n, Regs& R, int slot, auto last) {
+    constexpr bool MASK = decltype(last)::value;
     u32x4 kr[2][KK];
     read_k(slot, kr);
     f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -217,7 +290,7 @@ decode_mfma_kernel(const DecodeParams a) {
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      sv[j] = (pos0 + j < end) ? sv[j] * a.scale_log2e : -INFINITY;
+      sv[j] = (!MASK || pos0 + j < end) ? sv[j] * a.scale_log2e : -INFINITY;
       mx = fmaxf(mx, sv[j]);
     }
     mx = across16(mx, OpMax());
@@ -235,7 +308,7 @@ decode_mfma_kernel(const DecodeParams a) {
     l = fmaf(l, alpha, psum);
     // Positions past the end may hold anything (even NaN): zero them, 0 * NaN is NaN.
     const int nv = end - pos0;
-    if (nv < 8) {
+    if (MASK && nv < 8) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint32_t keep = (2 * q + 1 < nv) ? 0xffffffffu : (2 * q < nv) ? 0x0000ffffu : 0u;
@@ -266,7 +339,7 @@ decode_mfma_kernel(const DecodeParams a) {
         kpiece[kk] = *reinterpret_cast<const u32x4*>(kn + (32 * kk + 8 * r) * EB);
     }
     if (wave == 0) {
-      slot_blk = bt[(L - 1) / S];
+      slot_blk = TBL ? bt[(L - 1) / S] : contig0 + (L - 1) / S;
       if (lane < D * EB / 16) krow = reinterpret_cast<const u32x4*>(kn)[lane];
 #pragma unroll
       for (int e = 0; e < D / 64; ++e) vrow[e] = vn[lane + 64 * e];
@@ -302,37 +375,41 @@ decode_mfma_kernel(const DecodeParams a) {
   int n = wave;
   if (n < nch) {
     Regs A, B;
-    Ids ids;
-    ids.b0 = clamp_id(first0);
-    ids.b1 = (BPC == 2 && b_first + 1 < blk_end) ? clamp_id(first1) : ids.b0;
+    Ids ids = fetch_ids(0);
+    int m_next = 1;  // local index of the chunk whose ids are fetched next
     load(ids, A, 0);
-    if (n + NW < nch) ids = fetch_ids(n + NW);
+    if (n + NW < nch) ids = fetch_ids(m_next++);
     if (fused) use_new_rows();
     // Two stages: chunk n + NW loads while chunk n computes; its block ids were fetched one
     // step earlier still. The LDS half of a chunk is not tracked by the compiler, so each
     // step waits explicitly: vector memory operations complete in order, and exactly
-    // KLD + NT of them (the next chunk's) may still be in flight when chunk n is read.
+    // KLD + NT of them (the next chunk's) may still be in flight when chunk n is read. Each
+    // steady-state compute is reached only through the next chunk's loads and that wait, so
+    // the compiler's own waits for the V registers count the same KLD + NT operations; the
+    // last chunk is computed after a full wait.
+    const std::false_type mid;
+    const std::true_type last;
     while (true) {
-      if (n + NW < nch) {
-        load(ids, B, 1);
-        if (n + 2 * NW < nch) ids = fetch_ids(n + 2 * NW);
-        wait_vm_le<KLD + NT>();
-      } else {
+      if (n + NW >= nch) {
         wait_vm_le<0>();
+        compute(n, A, 0, last);
+        break;
       }
-      compute(n, A, 0);
+      load(ids, B, 1);
+      if (n + 2 * NW < nch) ids = fetch_ids(m_next++);
+      wait_vm_le<KLD + NT>();
+      compute(n, A, 0, mid);
       n += NW;
-      if (n >= nch) break;
-      if (n + NW < nch) {
-        load(ids, A, 0);
-        if (n + 2 * NW < nch) ids = fetch_ids(n + 2 * NW);
-        wait_vm_le<KLD + NT>();
-      } else {
+      if (n + NW >= nch) {
         wait_vm_le<0>();
+        compute(n, B, 1, last);
+        break;
       }
-      compute(n, B, 1);
+      load(ids, A, 0);
+      if (n + 2 * NW < nch) ids = fetch_ids(m_next++);
+      wait_vm_le<KLD + NT>();
+      compute(n, B, 1, mid);
       n += NW;
-      if (n >= nch) break;
     }
   } else if (fused) {
     use_new_rows();
@@ -402,18 +479,21 @@ decode_mfma_kernel(const DecodeParams a) {
 
 constexpr int kMfmaWaves = 4;
 
-template <Dt DT, int D, int S>
-hipError_t launch_s(bool partial, bool nt, const DecodeParams& p, hipStream_t stream) {
+template <Dt DT, int D, int S, bool PARTIAL, bool NTL>
+hipError_t launch_p(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)p.num_units * p.num_kv_heads);
   const dim3 block(kMfmaWaves * 64);
-  if (partial) {
-    if (nt) decode_mfma_kernel<DT, D, S, kMfmaWaves, true, true><<<grid, block, 0, stream>>>(p);
-    else decode_mfma_kernel<DT, D, S, kMfmaWaves, true, false><<<grid, block, 0, stream>>>(p);
-  } else {
-    if (nt) decode_mfma_kernel<DT, D, S, kMfmaWaves, false, true><<<grid, block, 0, stream>>>(p);
-    else decode_mfma_kernel<DT, D, S, kMfmaWaves, false, false><<<grid, block, 0, stream>>>(p);
-  }
+  if (p.block_tables)
+    decode_mfma_kernel<DT, D, S, kMfmaWaves, PARTIAL, NTL, true><<<grid, block, 0, stream>>>(p);
+  else
+    decode_mfma_kernel<DT, D, S, kMfmaWaves, PARTIAL, NTL, false><<<grid, block, 0, stream>>>(p);
   return hipGetLastError();
+}
+
+template <Dt DT, int D, int S>
+hipError_t launch_s(bool partial, bool nt, const DecodeParams& p, hipStream_t stream) {
+  if (partial) return nt ? launch_p<DT, D, S, true, true>(p, stream) : launch_p<DT, D, S, true, false>(p, stream);
+  return nt ? launch_p<DT, D, S, false, true>(p, stream) : launch_p<DT, D, S, false, false>(p, stream);
 }
 
 template <Dt DT, int D>

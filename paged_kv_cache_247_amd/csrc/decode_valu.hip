@@ -54,12 +54,13 @@ decode_valu_kernel(const DecodeParams a) {
   const int r = lane / LPR;
   const int c = lane % LPR;
   const int32_t* bt = a.block_tables + (size_t)i * MB;
+  auto table = [&](int j) { return bt[j]; };
   const int start = part * a.range_tokens;
 
   // Waves take blocks start/S + wave, + NW, ...; the first one's id is fetched before the
   // context length arrives (any entry of the row may be read; ids are clamped before use).
   const int b_first = start / S + wave;
-  const int first_id = b_first < MB ? bt[b_first] : 0;
+  const int first_id = b_first < MB ? table(b_first) : 0;
 
   int L = a.context_lens[i];
   L = min(max(L, 0), MB * S);
@@ -190,7 +191,7 @@ decode_valu_kernel(const DecodeParams a) {
   if (fused) {
     if (wave == NW - 1) kpiece = *reinterpret_cast<const u32x4*>(kn + (size_t)c * 16);
     if (wave == 0) {
-      slot_blk = bt[(L - 1) / S];
+      slot_blk = table((L - 1) / S);
       if (lane < D * EB / 16) krow = reinterpret_cast<const u32x4*>(kn)[lane];
 #pragma unroll
       for (int e = 0; e < D / 64; ++e) vrow[e] = vn[lane + 64 * e];
@@ -228,21 +229,21 @@ decode_valu_kernel(const DecodeParams a) {
   if (b < blk_hi) {
     Regs A, B;
     load(clamp_id(first_id), A);
-    int id = b + NW < blk_hi ? clamp_id(bt[b + NW]) : 0;
+    int id = b + NW < blk_hi ? clamp_id(table(b + NW)) : 0;
     if (fused) use_new_rows();
     // Two register sets: block b + NW loads while block b computes; its id was fetched one
     // step earlier still.
     while (true) {
       if (b + NW < blk_hi) {
         load(id, B);
-        if (b + 2 * NW < blk_hi) id = clamp_id(bt[b + 2 * NW]);
+        if (b + 2 * NW < blk_hi) id = clamp_id(table(b + 2 * NW));
       }
       compute(b, A);
       b += NW;
       if (b >= blk_hi) break;
       if (b + NW < blk_hi) {
         load(id, A);
-        if (b + 2 * NW < blk_hi) id = clamp_id(bt[b + 2 * NW]);
+        if (b + 2 * NW < blk_hi) id = clamp_id(table(b + 2 * NW));
       }
       compute(b, B);
       b += NW;

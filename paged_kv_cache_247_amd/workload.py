@@ -401,3 +401,32 @@ def permute_pool(wl: Workload, seed: int) -> Workload:
         block_tables_before=remap(wl.block_tables_before),
         block_mapping=pi[wl.block_mapping].astype(np.int64) if len(wl.block_mapping)
         else wl.block_mapping, slot_mapping=new_slots.astype(np.int64), meta=dict(wl.meta))
+
+
+def contiguous_layout(wl: Workload) -> Workload:
+    """The same workload in the conventional contiguous reservation: sequence i owns pool
+    blocks i * MB .. i * MB + MB - 1 in order (the per-request maximum-length reservation that
+    paging replaces). Tables are rewritten to that identity mapping, so decode can run either
+    through them or table-free; prefix sharing and copy-on-write do not exist in this layout."""
+    cfg = wl.cfg
+    if len(wl.block_mapping):
+        raise ValueError("a contiguous reservation has no shared blocks")
+    B, MB, S = cfg.num_seqs, wl.block_tables.shape[1], cfg.block_size
+    N = B * MB
+    k = np.zeros((N,) + wl.k_cache.shape[1:], dtype=wl.k_cache.dtype)
+    v = np.zeros((N,) + wl.v_cache.shape[1:], dtype=wl.v_cache.dtype)
+    tables = np.full_like(wl.block_tables, -1)
+    for i in range(B):
+        nb = -(-int(wl.context_lens[i]) // S)
+        old = wl.block_tables[i, :nb]
+        k[i * MB:i * MB + nb] = wl.k_cache[old]
+        v[i * MB:i * MB + nb] = wl.v_cache[old]
+        tables[i, :nb] = i * MB + np.arange(nb)
+    slots = wl.slot_mapping.copy()
+    for i, s_ in enumerate(slots):
+        if s_ >= 0:
+            j = int(wl.context_lens[i] - 1) // S
+            slots[i] = (i * MB + j) * S + s_ % S
+    return dataclasses.replace(wl, cfg=cfg.replace(num_blocks=N), k_cache=k, v_cache=v,
+                               block_tables=tables, block_tables_before=tables.copy(),
+                               slot_mapping=slots, meta=dict(wl.meta))

@@ -57,11 +57,11 @@ def upload(wl) -> Dev:
 
 
 def run_step(dev: Dev, wl, kernel="auto", partition_size=None, tables=None, copy=True,
-             order=None, fused=False, cached_kv=False):
+             order=None, fused=False, cached_kv=False, table_free=False):
     """copy_blocks (if the workload has pairs) -> reshape_and_cache -> decode (+ reduce).
     order: optional host int32 work list (units i * NP + p, see Workload.work_items). fused:
-    the decode call writes
-    the newest tokens itself (no reshape_and_cache). cached_kv: cached K/V loads."""
+    the decode call writes the newest tokens itself (no reshape_and_cache). cached_kv: cached
+    K/V loads. table_free: decode without block tables (sequence i owns blocks i * MB ..)."""
     c = wl.cfg
     P = c.partition_size if partition_size is None else partition_size
     if copy and len(wl.block_mapping):
@@ -70,8 +70,10 @@ def run_step(dev: Dev, wl, kernel="auto", partition_size=None, tables=None, copy
         pk.reshape_and_cache(dev.key, dev.value, dev.k, dev.v, dev.slots)
     out = torch.full((c.num_seqs, c.num_heads, c.head_dim), float("nan"),
                      dtype=TORCH_DT[c.dtype], device="cuda")
-    pk.paged_attention(out, dev.q, dev.k, dev.v, dev.bt if tables is None else tables, dev.lens,
+    bt = None if table_free else dev.bt if tables is None else tables
+    pk.paged_attention(out, dev.q, dev.k, dev.v, bt, dev.lens,
                        wl.max_context_len, c.scale, P, kernel=kernel,
+                       max_blocks_per_seq=wl.block_tables.shape[1] if table_free else None,
                        work_items=None if order is None else to_dev(np.asarray(order, np.int32)),
                        cached_kv=cached_kv, new_key=dev.key if fused else None,
                        new_value=dev.value if fused else None)

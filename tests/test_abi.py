@@ -96,6 +96,9 @@ def decode(lib, **kw):
     (dict(nk=A16), INVALID),  # new_key without new_value
     (dict(nk=A16, nv=A16 + 8), INVALID),  # misaligned new_value
     (dict(B=0), OK),  # nothing to do, nothing enqueued
+    (dict(bt=None, N=7), INVALID),  # table-free: the pool must hold B * MB blocks
+    (dict(bt=None, kernel=1), UNSUPPORTED),  # table-free runs on the MFMA kernel only
+    (dict(bt=None, kernel=2, B=0), OK),
 ])
 def test_decode_validation(lib, kw, status):
     assert decode(lib, **kw) == status

@@ -239,6 +239,52 @@ def test_fused_edge_lengths(kernel, dtype, S):
     assert np.array_equal(bits(to_host(one, dtype)[0]), bits(np.repeat(wl.value[0], cfg.group, 0)))
 
 
+TABLE_FREE = [("c3", {}, (0, 64)), ("c3", {"head_dim": 64}, (0,)),
+              ("c3", {"block_size": 32}, (0, 64)), ("c3", {"dtype": "f16"}, (0,)),
+              ("c5", {}, (64, 0)), ("c2", {}, (0,))]
+
+
+@pytest.mark.parametrize("name,over,parts", TABLE_FREE,
+                         ids=[f"{c[0]}-{'-'.join(f'{k}{v}' for k, v in c[1].items()) or 'base'}"
+                              for c in TABLE_FREE])
+@pytest.mark.parametrize("fused", [False, True])
+def test_table_free_matches_tables_bit_identical(name, over, parts, fused):
+    """The contiguous reservation decoded through identity tables and without tables gives the
+    same bits, and both match the oracle (which reads through the tables)."""
+    wc = W.contiguous_layout(W.generate(_cfg(name, **over)))
+    dt = wc.cfg.dtype
+    kc, vc = oracle_pools(wc)
+    ref = oracle_out(wc, pools=(kc, vc))
+    for P in parts:
+        paged = run_step(upload(wc), wc, kernel="mfma", partition_size=P, fused=fused)
+        dev = upload(wc)
+        free = run_step(dev, wc, kernel="mfma", partition_size=P, fused=fused, table_free=True)
+        assert torch.equal(free.view(torch.uint8), paged.view(torch.uint8)), f"P={P}"
+        assert oracle.max_abs_err(out_f64(free), ref) <= TOL[dt], f"P={P}"
+        assert np.array_equal(bits(to_host(dev.k, dt)), bits(kc))
+        assert np.array_equal(bits(to_host(dev.v, dt)), bits(vc))
+
+
+@pytest.mark.parametrize("kernel,S", [("auto", 16), ("auto", 32), ("valu", 16)])
+def test_long_contexts_across_block_id_batches(kernel, S):
+    """Contexts long enough that a wave walks more than one batch of block ids (a batch covers
+    64 ids: 32 chunks of 32 positions at block size 16, 64 at block size 32, per wave)."""
+    lens = np.array([4096, 4097, 4160, 5000, 8191, 8192, 8300, 12345, 1, 0, 4095, 16400],
+                    dtype=np.int32)
+    cfg = _cfg("c3", block_size=S, num_seqs=len(lens), num_blocks=int(lens.sum() // S + 64),
+               len_hi=int(lens.max()))
+    wl = W.generate(cfg, lens=lens)
+    kc, vc = oracle_pools(wl)
+    ref = oracle_out(wl, pools=(kc, vc))
+    for P, fused in ((0, False), (0, True), (8192, True), (512, False)):
+        dev = upload(wl)
+        out = run_step(dev, wl, kernel=kernel, partition_size=P, fused=fused,
+                       order=wl.work_items(P))
+        err = oracle.max_abs_err(out_f64(out), ref)
+        assert err <= TOL["bf16"], f"P={P} fused={fused}: {err}"
+        assert not out_f64(out)[9].any()
+
+
 @pytest.mark.parametrize("name,kernel,P", [("c4", "auto", 0), ("c3", "auto", 64),
                                            ("c3", "valu", 0), ("c5", "auto", 64)])
 def test_cached_loads_give_the_same_bits(name, kernel, P):
