@@ -8,14 +8,19 @@ the workload has them), the cache write of each sequence's newest token, paged d
 partition merge when the context is split. By default the cache write is fused into the decode
 launch (--unfused writes with a separate reshape_and_cache launch). Inputs are resident in HBM
 before timing starts.
+
 Prints one JSON line: KV-read GB/s over the step (value), attended tokens/s, the decode
-kernel's roofline figures (timed per launch with HIP events on the launch stream) and the
-oracle's CPU throughput on a bounded sample of the same workload.
+kernel's roofline figures (timed per launch with HIP events on the launch stream), repetition
+statistics of back-to-back launches of each kernel on its own (decode, cache write, block copy,
+merge), and the oracle's CPU throughput on the same workload at one thread and at all cores.
+The oracle is timed first, before anything touches the GPU, so its worker processes are plain
+CPU processes.
 """
 from __future__ import annotations
 
 import argparse
 import json
+import multiprocessing as mp
 import os
 import platform
 import sys
@@ -37,6 +42,10 @@ LAUNCH = {
     "c5": ("auto", 2048, False),
 }
 
+# Sources the decode kernels are built from (a change to any invalidates counter figures).
+KERNEL_SOURCES = {"mfma": ["decode_mfma.hip", "common.hpp", "kernels.hpp"],
+                  "valu": ["decode_valu.hip", "common.hpp", "kernels.hpp"]}
+
 
 def parse():
     ap = argparse.ArgumentParser(description="paged decode benchmark (one GPU)")
@@ -50,35 +59,95 @@ def parse():
                     help="write new tokens with a separate reshape_and_cache launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="CPU time to spend timing the oracle")
+                    help="CPU time to spend timing the oracle on one thread")
+    ap.add_argument("--cpu-all-seconds", type=float, default=3.0,
+                    help="wall time to spend timing the oracle on all cores")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="oracle worker processes (0: the host's cores, at most 16)")
+    ap.add_argument("--reps", type=int, default=5,
+                    help="repetitions of back-to-back launch timing per kernel")
+    ap.add_argument("--launches", type=int, default=100,
+                    help="back-to-back launches per repetition")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     return ap.parse_args()
 
 
-def cpu_baseline(wl, target_s: float):
-    """The oracle's decode (fp64 numpy, one thread) over whole passes of the workload, repeated
-    until about target_s seconds of CPU time have run."""
+# ------------------------------------------------------------------ oracle on the CPU
+
+_WL = None  # the workload, inherited by forked oracle workers
+
+
+def _oracle_part(idx):
+    """One worker's share of an oracle pass: decode of the sequences idx on one thread."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    c = _WL.cfg
+    with threadpool_limits(limits=1):
+        oracle.decode(_WL.q[idx], _WL.k_cache, _WL.v_cache, _WL.block_tables[idx],
+                      _WL.context_lens[idx], c.scale, c.num_kv_heads, c.dtype)
+    return int(_WL.context_lens[idx].sum())
+
+
+def _shares(lens, n):
+    """Sequence index sets for n workers, longest first onto the least loaded."""
+    load = [0] * n
+    parts = [[] for _ in range(n)]
+    for i in np.argsort(-lens, kind="stable"):
+        k = int(np.argmin(load))
+        parts[k].append(int(i))
+        load[k] += int(lens[i])
+    return [np.array(sorted(p), dtype=np.int64) for p in parts if p]
+
+
+def cpu_baseline(wl, one_s: float, all_s: float, workers: int):
+    """The oracle's decode (fp64 numpy) over whole passes of the workload: first on one thread
+    for about one_s seconds, then split over `workers` forked processes (one thread each) for
+    about all_s seconds of wall time."""
+    global _WL
     from threadpoolctl import threadpool_limits
 
     import oracle
     c = wl.cfg
+    elt = 4 if c.dtype == "f32" else 2
+    per_tok = c.num_kv_heads * c.head_dim * elt * 2
     passes, toks, dt = 0, 0, 0.0
     with threadpool_limits(limits=1):
-        while dt < target_s:
+        while dt < one_s:
             t0 = time.perf_counter()
             oracle.decode(wl.q, wl.k_cache, wl.v_cache, wl.block_tables, wl.context_lens,
                           c.scale, c.num_kv_heads, c.dtype)
             dt += time.perf_counter() - t0
             passes += 1
             toks += wl.total_tokens
-    kvb = toks * c.num_kv_heads * c.head_dim * (4 if c.dtype == "f32" else 2) * 2
-    return {"value": round(kvb / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{passes} whole passes over all {c.num_seqs} sequences ({toks} context "
-                      f"tokens), fp64 numpy decode on one thread, {dt:.1f} s",
-            "attended_tokens_per_s": round(toks / dt, 1),
-            "cpu": platform.processor() or platform.machine()}
+    res = {"value": round(toks * per_tok / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+           "kind": "oracle",
+           "sample": f"{passes} whole passes over all {c.num_seqs} sequences ({wl.total_tokens} "
+                     f"context tokens each), fp64 numpy decode on one thread, {dt:.1f} s",
+           "attended_tokens_per_s": round(toks / dt, 1),
+           "cpu": platform.processor() or platform.machine(), "host_cpus": os.cpu_count()}
+    if workers > 1 and all_s > 0:
+        _WL = wl
+        shares = _shares(wl.context_lens, workers)
+        with mp.get_context("fork").Pool(len(shares)) as pool:
+            pool.map(_oracle_part, shares)  # start-up and first touch, untimed
+            passes, toks = 0, 0
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < all_s:
+                toks += sum(pool.map(_oracle_part, shares))
+                passes += 1
+            dt = time.perf_counter() - t0
+        _WL = None
+        res["all_cores"] = {
+            "value": round(toks * per_tok / dt / 1e9, 4), "unit": "GB/s", "cores": len(shares),
+            "sample": f"{passes} whole passes split over {len(shares)} processes (one thread "
+                      f"each, sequences balanced by length), {dt:.1f} s wall",
+            "attended_tokens_per_s": round(toks / dt, 1)}
+    return res
 
+
+# ------------------------------------------------------------------ GPU helpers
 
 def counter_traffic(kernel_sources, workload):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary, if the summary
@@ -101,9 +170,24 @@ def counter_traffic(kernel_sources, workload):
     return int(float(vals["traffic_bytes_per_launch"]))
 
 
-# Sources the decode kernels are built from (a change to any invalidates counter figures).
-KERNEL_SOURCES = {"mfma": ["decode_mfma.hip", "common.hpp", "kernels.hpp"],
-                  "valu": ["decode_valu.hip", "common.hpp", "kernels.hpp"]}
+def launch_stats(torch, fn, launches: int, reps: int, warmup: int = 10):
+    """Microseconds per launch of fn over `reps` repetitions of `launches` back-to-back
+    launches, bracketed by HIP events on the current stream: median, min, max."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(launches):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e3 / launches)
+    per.sort()
+    return {"median_us": round(per[len(per) // 2], 3), "min_us": round(per[0], 3),
+            "max_us": round(per[-1], 3), "launches": launches, "reps": reps}
 
 
 def main():
@@ -112,16 +196,8 @@ def main():
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the "
               "decode path is single-GPU, see DESIGN.md for how it would shard)", file=sys.stderr)
         sys.exit(2)
-    import torch
-
-    sys.path.insert(0, os.path.join(os.path.dirname(os.path.abspath(__file__)), "tests"))
-    import paged_kv_cache_247_amd as pk
     from paged_kv_cache_247_amd import workload as W
 
-    pk.load()  # fails loudly when the library is not built
-    if not torch.cuda.is_available():
-        print("no GPU visible", file=sys.stderr)
-        sys.exit(1)
     name = args.config
     kernel, P, cached = LAUNCH[name]
     kernel = args.kernel or kernel
@@ -130,6 +206,21 @@ def main():
     t0 = time.time()
     wl = W.generate(cfg, poison="zero")
     print(f"[bench] generated {name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        workers = args.cpu_workers or min(16, os.cpu_count() or 1)
+        print(f"[bench] timing the oracle on the CPU (1 thread, then {workers} processes)",
+              file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, args.cpu_seconds, args.cpu_all_seconds, workers)
+
+    import torch
+
+    import paged_kv_cache_247_amd as pk
+    pk.load()  # fails loudly when the library is not built
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
     dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
 
     def dev(a, bf=False):
@@ -150,9 +241,15 @@ def main():
                                 P, q.device) if P else None
     maxlen = wl.max_context_len
     has_copy = len(wl.block_mapping) > 0
+    fused = not args.unfused
     ev = []
 
-    fused = not args.unfused
+    def decode():
+        # With fused=True the decode launch also writes each sequence's newest K/V to its slot.
+        pk.paged_attention_decode(None if P else out, q, kc, vc, bt, lens, maxlen, cfg.scale,
+                                  P, ws, kernel=kernel, work_items=order, cached_kv=cached,
+                                  new_key=key if fused else None,
+                                  new_value=value if fused else None)
 
     def step(record):
         if has_copy:
@@ -162,16 +259,39 @@ def main():
         if record:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-        # With fused=True the decode launch also writes each sequence's newest K/V to its slot.
-        pk.paged_attention_decode(None if P else out, q, kc, vc, bt, lens, maxlen, cfg.scale,
-                                  P, ws, kernel=kernel, work_items=order, cached_kv=cached,
-                                  new_key=key if fused else None,
-                                  new_value=value if fused else None)
+        decode()
         if record:
             e1.record()
             ev.append((e0, e1))
         if P:
             pk.paged_attention_reduce(out, ws, lens, P)
+
+    # Each kernel on its own, back to back (all of them are idempotent on these inputs). This
+    # runs first: its ~0.1 s of sustained launches also brings the GPU out of idle before the
+    # warm-up and timed steps.
+    elt = 4 if cfg.dtype == "f32" else 2
+    tile = cfg.num_kv_heads * cfg.block_size * cfg.head_dim * elt
+    n_new = int((wl.slot_mapping >= 0).sum())
+    kernels = {"paged_attention_decode": dict(
+        launch_stats(torch, decode, args.launches, args.reps),
+        kv_bytes=wl.kv_bytes())}
+    kernels["reshape_and_cache"] = dict(
+        launch_stats(torch, lambda: pk.reshape_and_cache(key, value, kc, vc, slots),
+                     args.launches, args.reps),
+        bytes=n_new * cfg.num_kv_heads * cfg.head_dim * elt * 2 * 2)
+    if has_copy:
+        kernels["copy_blocks"] = dict(
+            launch_stats(torch, lambda: pk.copy_blocks([kc], [vc], mapping), args.launches,
+                         args.reps),
+            bytes=len(wl.block_mapping) * tile * 2 * 2)
+    if P:
+        kernels["paged_attention_reduce"] = dict(
+            launch_stats(torch, lambda: pk.paged_attention_reduce(out, ws, lens, P),
+                         args.launches, args.reps))
+    for k, s in kernels.items():
+        b = s.get("kv_bytes", s.get("bytes"))
+        if b:
+            s["GB_per_s"] = round(b / (s["median_us"] * 1e-6) / 1e9, 2)
 
     for _ in range(args.warmup):
         step(False)
@@ -216,10 +336,12 @@ def main():
                    "unique_kv_bytes": ukvb},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "attended_tokens_per_s": round(wl.total_tokens / (ms_step * 1e-3), 1),
+        "head_token_pairs_per_s": round(cfg.num_heads * wl.total_tokens / (ms_step * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": f"paged_attention_decode ({family})",
                      "ms_per_launch": round(dec_ms, 5), "bytes_per_launch": kvb},
+        "kernels": kernels,
     }
     if args.copy_calibration_gib > 0:
         n = int(args.copy_calibration_gib * (1 << 30)) // 4
@@ -228,10 +350,8 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         line["copy_calibration_bytes"] = n * 4
-    if not args.no_cpu_baseline:
-        del q, kc, vc
-        print("[bench] timing the oracle on the CPU", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 

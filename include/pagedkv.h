@@ -27,7 +27,8 @@
  *   v_cache        [N, Hkv, D, S]   T   -- head_dim rows of S positions; also one contiguous tile
  *   key, value     [T_new, Hkv, D]  T   -- the new tokens of this step
  *   slot_mapping   [T_new]          int64, slot = block_id * S + position_in_block
- *   block_tables   [B, MB]          int32; entries at or past ceil(L_i / S) are never read
+ *   block_tables   [B, MB]          int32; entries at or past ceil(L_i / S) are never used
+ *                                         (decode may read any entry of row i, in bounds)
  *   context_lens   [B]              int32
  *   block_mapping  [M, 2]           int64 (src, dst) pairs
  *   partition workspace (split-context mode, fp32):
