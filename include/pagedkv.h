@@ -188,6 +188,51 @@ pkv_status pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t
 size_t pkv_partition_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                      int32_t max_context_len, int32_t partition_size);
 
+/* ---- Virtually contiguous KV pool (the alternative to paging that vAttention proposes) ----
+ *
+ * The conventional layout gives each sequence one contiguous region sized for its maximum
+ * length; paging replaces it with blocks and a block table (Qualiteg post, items 1-1..1-3).
+ * vAttention's alternative keeps each sequence's KV contiguous in *virtual* memory and backs
+ * it with physical pages only as it grows (vAttention paper, section 3: the issues of the
+ * PagedAttention model, and its table of contents on virtual-memory demand paging). This
+ * pool does that with HIP virtual memory: it reserves, for each of num_seqs sequences and
+ * for K and V separately, address space for max_context_len positions in the contiguous
+ * layout of pkv_paged_attention_decode without a block table (sequence i owns blocks
+ * i * MB .. i * MB + MB - 1, MB = pkv_vmm_pool_blocks_per_seq), and maps physical pages of
+ * page_bytes on demand. Decode then reads it through block_tables = NULL with
+ * max_blocks_per_seq = MB and num_blocks = num_seqs * MB.
+ *
+ * Unlike every other entry point these calls allocate: they are the allocator. The pool
+ * belongs to the device that is current at creation. Any access to a position that is not
+ * mapped faults the GPU: map every position decode or a cache write may touch (the first
+ * L_i positions of sequence i) before launching on the pool. Not thread-safe per pool. */
+typedef struct pkv_vmm_pool pkv_vmm_pool;
+
+/* Reserve the address space (nothing is mapped yet). page_bytes: physical page size, 0 for
+ * the device's recommended granularity, else a multiple of its minimum granularity. MB is
+ * rounded up so that every sequence's region is a whole number of pages. */
+pkv_status pkv_vmm_pool_create(int32_t num_seqs, int32_t max_context_len, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, pkv_dtype dtype,
+                               size_t page_bytes, pkv_vmm_pool** pool);
+/* Back positions [0, num_positions) of sequence seq (K and V) with physical pages; grows
+ * only (a smaller count than already mapped does nothing). */
+pkv_status pkv_vmm_pool_map(pkv_vmm_pool* pool, int32_t seq, int32_t num_positions);
+/* Unmap and free all of sequence seq's pages (the sequence finished). The caller must make
+ * sure no queued GPU work still reads them. */
+pkv_status pkv_vmm_pool_unmap(pkv_vmm_pool* pool, int32_t seq);
+/* Copy the first num_blocks blocks of sequence seq between the pool and caller device memory
+ * (k, v: device, num_blocks * Hkv * S * D elements each, in the decode layouts), on `stream`:
+ * into the pool if to_pool != 0, out of it otherwise. Refuses blocks that are not mapped. */
+pkv_status pkv_vmm_pool_copy(pkv_vmm_pool* pool, int32_t seq, int32_t num_blocks, void* k,
+                             void* v, int32_t to_pool, void* stream);
+/* Unmap everything and release the address space; NULL is ignored. */
+void pkv_vmm_pool_destroy(pkv_vmm_pool* pool);
+void* pkv_vmm_pool_k(const pkv_vmm_pool* pool);        /* device base of the K region */
+void* pkv_vmm_pool_v(const pkv_vmm_pool* pool);        /* device base of the V region */
+int32_t pkv_vmm_pool_blocks_per_seq(const pkv_vmm_pool* pool);
+size_t pkv_vmm_pool_page_bytes(const pkv_vmm_pool* pool);
+size_t pkv_vmm_pool_mapped_bytes(const pkv_vmm_pool* pool); /* K + V physically backed */
+
 const char* pkv_status_string(pkv_status s);
 int pkv_last_hip_error(void);              /* hipError_t behind the last PKV_ERR_HIP */
 const char* pkv_last_error_message(void);  /* thread-local text of the last failure */

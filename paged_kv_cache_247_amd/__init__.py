@@ -3,10 +3,10 @@
 Hand-written HIP kernels behind the C ABI in include/pagedkv.h (libpagedkv.so), with a thin
 ctypes binding. The seeded workload generators live in `workload`.
 """
-from ._lib import (KERNELS, PagedKVError, copy_blocks, load, num_partitions, paged_attention,
-                   paged_attention_decode, paged_attention_reduce, partition_workspace,
-                   reshape_and_cache)
+from ._lib import (KERNELS, DeviceRegion, PagedKVError, VmmPool, copy_blocks, load,
+                   num_partitions, paged_attention, paged_attention_decode,
+                   paged_attention_reduce, partition_workspace, reshape_and_cache)
 
-__all__ = ["KERNELS", "PagedKVError", "copy_blocks", "load", "num_partitions",
-           "paged_attention", "paged_attention_decode", "paged_attention_reduce",
-           "partition_workspace", "reshape_and_cache"]
+__all__ = ["KERNELS", "DeviceRegion", "PagedKVError", "VmmPool", "copy_blocks", "load",
+           "num_partitions", "paged_attention", "paged_attention_decode",
+           "paged_attention_reduce", "partition_workspace", "reshape_and_cache"]

@@ -44,6 +44,16 @@ SIGNATURES = {
     "pkv_last_hip_error": (ctypes.c_int, []),
     "pkv_last_error_message": (ctypes.c_char_p, []),
     "pkv_abi_version": (ctypes.c_int, []),
+    "pkv_vmm_pool_create": (_I, [_I, _I, _I, _I, _I, _I, _Z, ctypes.POINTER(_P)]),
+    "pkv_vmm_pool_map": (_I, [_P, _I, _I]),
+    "pkv_vmm_pool_unmap": (_I, [_P, _I]),
+    "pkv_vmm_pool_copy": (_I, [_P, _I, _I, _P, _P, _I, _P]),
+    "pkv_vmm_pool_destroy": (None, [_P]),
+    "pkv_vmm_pool_k": (_P, [_P]),
+    "pkv_vmm_pool_v": (_P, [_P]),
+    "pkv_vmm_pool_blocks_per_seq": (_I, [_P]),
+    "pkv_vmm_pool_page_bytes": (_Z, [_P]),
+    "pkv_vmm_pool_mapped_bytes": (_Z, [_P]),
 }
 
 
@@ -89,8 +99,30 @@ def _ptr(t: torch.Tensor | None):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+class DeviceRegion:
+    """A raw device buffer that the binding accepts wherever it takes a KV pool: a pointer, a
+    shape, a dtype and a device, with no torch storage behind it. The virtual-memory pool hands
+    these out because no torch operation may touch its unmapped parts."""
+    is_cuda = True
+
+    def __init__(self, ptr: int, shape, dtype: torch.dtype, device: torch.device):
+        self._ptr = int(ptr)
+        self.shape = tuple(int(x) for x in shape)
+        self.dtype = dtype
+        self.device = device
+
+    def data_ptr(self) -> int:
+        return self._ptr
+
+    def dim(self) -> int:
+        return len(self.shape)
+
+    def is_contiguous(self) -> bool:
+        return True
+
+
 def _need(t: torch.Tensor, name: str, dtype=None, ndim=None, device=None):
-    if not isinstance(t, torch.Tensor):
+    if not isinstance(t, (torch.Tensor, DeviceRegion)):
         raise TypeError(f"{name} must be a tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU")
@@ -277,3 +309,73 @@ def paged_attention(out, q, k_cache, v_cache, block_tables, context_lens, max_co
         paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
                                max_context_len, scale, 0, None, **kw)
     return out
+
+
+class VmmPool:
+    """pkv_vmm_pool_*: K and V regions kept virtually contiguous per sequence (the contiguous
+    layout that decode reads without block tables) and backed by physical pages on demand.
+    `k` and `v` are DeviceRegions over the whole reservation; map a sequence's positions before
+    any GPU work touches them. Decode on the pool: paged_attention_decode(..., pool.k, pool.v,
+    None, ..., max_blocks_per_seq=pool.blocks_per_seq)."""
+
+    def __init__(self, num_seqs: int, max_context_len: int, num_kv_heads: int, head_dim: int,
+                 block_size: int, dtype: torch.dtype, page_bytes: int = 0):
+        lib = load()
+        h = ctypes.c_void_p()
+        _check(lib.pkv_vmm_pool_create(num_seqs, max_context_len, num_kv_heads, head_dim,
+                                       block_size, _DTYPES[dtype], page_bytes, ctypes.byref(h)))
+        self._h = h
+        self.num_seqs = num_seqs
+        self.blocks_per_seq = lib.pkv_vmm_pool_blocks_per_seq(h)
+        self.page_bytes = lib.pkv_vmm_pool_page_bytes(h)
+        self.block_shape = (num_kv_heads, block_size, head_dim)
+        dev = torch.device("cuda", torch.cuda.current_device())
+        N = num_seqs * self.blocks_per_seq
+        self.k = DeviceRegion(lib.pkv_vmm_pool_k(h), (N, num_kv_heads, block_size, head_dim),
+                              dtype, dev)
+        self.v = DeviceRegion(lib.pkv_vmm_pool_v(h), (N, num_kv_heads, head_dim, block_size),
+                              dtype, dev)
+
+    @property
+    def mapped_bytes(self) -> int:
+        return load().pkv_vmm_pool_mapped_bytes(self._h)
+
+    def map(self, seq: int, num_positions: int):
+        _check(load().pkv_vmm_pool_map(self._h, seq, num_positions))
+
+    def unmap(self, seq: int):
+        _check(load().pkv_vmm_pool_unmap(self._h, seq))
+
+    def write(self, seq: int, k_blocks: torch.Tensor, v_blocks: torch.Tensor):
+        """Copy blocks [0, n) of sequence seq in from device tensors [n, Hkv, S, D] and
+        [n, Hkv, D, S] (on the current stream)."""
+        self._copy(seq, k_blocks, v_blocks, 1)
+
+    def read(self, seq: int, num_blocks: int):
+        """Blocks [0, num_blocks) of sequence seq, copied out into new tensors."""
+        Hkv, S, D = self.block_shape
+        k = torch.empty((num_blocks, Hkv, S, D), dtype=self.k.dtype, device=self.k.device)
+        v = torch.empty((num_blocks, Hkv, D, S), dtype=self.k.dtype, device=self.k.device)
+        self._copy(seq, k, v, 0)
+        return k, v
+
+    def _copy(self, seq, k, v, to_pool):
+        Hkv, S, D = self.block_shape
+        n = k.shape[0]
+        _need(k, "k", self.k.dtype, 4, self.k.device)
+        _need(v, "v", self.k.dtype, 4, self.k.device)
+        if tuple(k.shape) != (n, Hkv, S, D) or tuple(v.shape) != (n, Hkv, D, S):
+            raise ValueError("blocks must be [n, Hkv, S, D] and [n, Hkv, D, S]")
+        _check(load().pkv_vmm_pool_copy(self._h, seq, n, _ptr(k), _ptr(v), to_pool, _stream(k)))
+
+    def close(self):
+        if self._h:
+            torch.cuda.synchronize()
+            load().pkv_vmm_pool_destroy(self._h)
+            self._h = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()

@@ -21,7 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
-SOURCES = ["api.cpp", "cache_ops.hip", "decode_valu.hip", "decode_mfma.hip", "reduce.hip"]
+SOURCES = ["api.cpp", "vmm.cpp", "cache_ops.hip", "decode_valu.hip", "decode_mfma.hip",
+           "reduce.hip"]
 ARCH = "gfx950"
 # Per-source extra flags. The decode MFMA kernel keeps its accumulators in ordinary VGPRs:
 # with the default heuristic the compiler puts them in AGPRs and copies them back and forth for

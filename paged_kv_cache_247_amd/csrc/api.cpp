@@ -7,13 +7,16 @@
 
 #include <hip/hip_runtime.h>
 
+#include "host_errors.hpp"
 #include "kernels.hpp"
 #include "pagedkv.h"
 
 namespace {
-
 thread_local int t_last_hip = 0;
 thread_local char t_msg[256] = "";
+}  // namespace
+
+namespace pkv {
 
 pkv_status fail(pkv_status s, const char* fmt, ...) {
   va_list ap;
@@ -23,12 +26,22 @@ pkv_status fail(pkv_status s, const char* fmt, ...) {
   return s;
 }
 
+pkv_status hip_failure(hipError_t e, const char* what) {
+  t_last_hip = (int)e;
+  return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace pkv
+
+namespace {
+
+using pkv::fail;
+
 pkv_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return PKV_OK;
   if (e == hipErrorNotSupported)
     return fail(PKV_ERR_UNSUPPORTED, "%s: no kernel instantiation for this shape", what);
-  t_last_hip = (int)e;
-  return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return pkv::hip_failure(e, what);
 }
 
 bool aligned(const void* p, uintptr_t a) { return p && ((uintptr_t)p % a) == 0; }

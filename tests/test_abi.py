@@ -32,7 +32,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
-    assert len(names) == 10, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES), "binding prototypes out of step with the header"
@@ -130,3 +130,21 @@ def test_reduce_and_copy_validation(lib):
     assert c(arr, arr, 2, A16 + 4, 3, 8, 128, 16, 64, 2, None) == INVALID
     assert c(arr, arr, -1, A16, 3, 8, 128, 16, 64, 2, None) == INVALID
     assert c(None, arr, 2, A16, 3, 8, 128, 16, 64, 2, None) == INVALID
+
+
+def test_vmm_pool_validation(lib):
+    """The virtual-memory pool rejects bad arguments before any HIP call; NULL pools are inert."""
+    h = ctypes.c_void_p()
+    assert lib.pkv_vmm_pool_create(4, 64, 8, 128, 16, 2, 0, None) == INVALID
+    assert lib.pkv_vmm_pool_create(0, 64, 8, 128, 16, 2, 0, ctypes.byref(h)) == INVALID
+    assert h.value is None
+    assert lib.pkv_vmm_pool_create(4, 0, 8, 128, 16, 2, 0, ctypes.byref(h)) == INVALID
+    assert lib.pkv_vmm_pool_create(4, 64, 8, 128, 16, 9, 0, ctypes.byref(h)) == INVALID
+    assert lib.pkv_vmm_pool_map(None, 0, 16) == INVALID
+    assert lib.pkv_vmm_pool_unmap(None, 0) == INVALID
+    assert lib.pkv_vmm_pool_copy(None, 0, 1, A16, A16, 1, None) == INVALID
+    assert lib.pkv_last_error_message().decode()
+    lib.pkv_vmm_pool_destroy(None)
+    assert lib.pkv_vmm_pool_k(None) is None and lib.pkv_vmm_pool_v(None) is None
+    assert lib.pkv_vmm_pool_blocks_per_seq(None) == 0
+    assert lib.pkv_vmm_pool_page_bytes(None) == 0 and lib.pkv_vmm_pool_mapped_bytes(None) == 0

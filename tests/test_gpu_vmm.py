@@ -1,0 +1,156 @@
+"""GPU tests of the virtually contiguous KV pool (HIP virtual memory behind the table-free
+decode): parity with the oracle, bit-identity with the same layout in ordinary device memory,
+cache writes into mapped pages, and the pool's own bookkeeping.
+
+Every test maps, for each sequence, the first L_i positions (everything decode and the newest
+token's cache write touch) before any GPU work runs on the pool, and copies only mapped
+blocks."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, TORCH_DT, bits, oracle_pools, out_f64, run_step, to_dev, to_host, upload
+from paged_kv_cache_247_amd import workload as W
+import paged_kv_cache_247_amd as pk
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu(request):
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    print(f"\n[gpu] {request.node.name}", file=sys.stderr, flush=True)
+
+
+def _fill_pool(pool, wc, dev_k, dev_v):
+    """Map each sequence's positions and copy its blocks in from the contiguous layout."""
+    c = wc.cfg
+    MB = wc.block_tables.shape[1]
+    for i in range(c.num_seqs):
+        L = int(wc.context_lens[i])
+        nb = -(-L // c.block_size)
+        pool.map(i, L)
+        if nb:
+            pool.write(i, dev_k[i * MB:i * MB + nb], dev_v[i * MB:i * MB + nb])
+    torch.cuda.synchronize()
+
+
+def _decode(pool, dev, wc, P=0, fused=True, kernel="mfma"):
+    c = wc.cfg
+    out = torch.full((c.num_seqs, c.num_heads, c.head_dim), float("nan"),
+                     dtype=TORCH_DT[c.dtype], device="cuda")
+    pk.paged_attention(out, dev.q, pool.k, pool.v, None, dev.lens, wc.max_context_len, c.scale,
+                       P, kernel=kernel, max_blocks_per_seq=pool.blocks_per_seq,
+                       new_key=dev.key if fused else None,
+                       new_value=dev.value if fused else None)
+    torch.cuda.synchronize()
+    return out
+
+
+CASES = [("c3", {}, (0, 64)), ("c3", {"block_size": 32}, (0,)), ("c5", {}, (64, 0)),
+         ("c3", {"head_dim": 64, "dtype": "f16"}, (0,))]
+
+
+@pytest.mark.parametrize("name,over,parts", CASES,
+                         ids=[f"{c[0]}-{'-'.join(f'{k}{v}' for k, v in c[1].items()) or 'base'}"
+                              for c in CASES])
+def test_vmm_pool_decode_matches_oracle_and_device_memory(name, over, parts):
+    wc = W.contiguous_layout(W.generate(W.SMALL[name].replace(**over)))
+    c = wc.cfg
+    dt = c.dtype
+    kc, vc = oracle_pools(wc)
+    ref = oracle.decode(wc.q, kc, vc, wc.block_tables, wc.context_lens, c.scale,
+                        c.num_kv_heads, dt)
+    MB = wc.block_tables.shape[1]
+    for P in parts:
+        plain = run_step(upload(wc), wc, kernel="mfma", partition_size=P, fused=True,
+                         table_free=True)
+        dev = upload(wc)
+        with pk.VmmPool(c.num_seqs, wc.max_context_len, c.num_kv_heads, c.head_dim,
+                        c.block_size, TORCH_DT[dt]) as pool:
+            assert pool.blocks_per_seq >= -(-wc.max_context_len // c.block_size)
+            print(f"[vmm] page {pool.page_bytes} B, {pool.blocks_per_seq} blocks per sequence",
+                  file=sys.stderr, flush=True)
+            _fill_pool(pool, wc, dev.k, dev.v)
+            out = _decode(pool, dev, wc, P=P)
+            assert oracle.max_abs_err(out_f64(out), ref) <= TOL[dt], f"P={P}"
+            assert torch.equal(out.view(torch.uint8), plain.view(torch.uint8)), f"P={P}"
+            # the fused write landed in the mapped pages, bit for bit
+            for i in range(c.num_seqs):
+                nb = -(-int(wc.context_lens[i]) // c.block_size)
+                if nb:
+                    k, v = pool.read(i, nb)
+                    assert np.array_equal(bits(to_host(k, dt)), bits(kc[i * MB:i * MB + nb]))
+                    assert np.array_equal(bits(to_host(v, dt)), bits(vc[i * MB:i * MB + nb]))
+
+
+def test_vmm_pool_cache_write_through_slots():
+    """reshape_and_cache into the pool, with slots in the pool's own block numbering."""
+    wc = W.contiguous_layout(W.generate(W.SMALL["c3"]))
+    c = wc.cfg
+    dt = c.dtype
+    kc, vc = oracle_pools(wc)
+    MB = wc.block_tables.shape[1]
+    dev = upload(wc)
+    with pk.VmmPool(c.num_seqs, wc.max_context_len, c.num_kv_heads, c.head_dim, c.block_size,
+                    TORCH_DT[dt]) as pool:
+        _fill_pool(pool, wc, dev.k, dev.v)
+        MBv = pool.blocks_per_seq
+        slots = wc.slot_mapping.copy()
+        for i, s_ in enumerate(slots):
+            if s_ >= 0:
+                blk, off = divmod(int(s_), c.block_size)
+                slots[i] = ((blk // MB) * MBv + blk % MB) * c.block_size + off
+        pk.reshape_and_cache(dev.key, dev.value, pool.k, pool.v, to_dev(slots))
+        out = _decode(pool, dev, wc, fused=False)
+        ref = oracle.decode(wc.q, kc, vc, wc.block_tables, wc.context_lens, c.scale,
+                            c.num_kv_heads, dt)
+        assert oracle.max_abs_err(out_f64(out), ref) <= TOL[dt]
+        for i in range(c.num_seqs):
+            nb = -(-int(wc.context_lens[i]) // c.block_size)
+            if nb:
+                k, v = pool.read(i, nb)
+                assert np.array_equal(bits(to_host(k, dt)), bits(kc[i * MB:i * MB + nb]))
+                assert np.array_equal(bits(to_host(v, dt)), bits(vc[i * MB:i * MB + nb]))
+
+
+@pytest.mark.parametrize("page_bytes", [0, 2 << 20])
+def test_vmm_pool_bookkeeping(page_bytes):
+    with pk.VmmPool(3, 4096, 8, 128, 16, torch.bfloat16, page_bytes=page_bytes) as pool:
+        page = pool.page_bytes
+        block = 8 * 16 * 128 * 2
+        if page_bytes:
+            assert page == page_bytes
+        assert page > 0 and (pool.blocks_per_seq * block) % page == 0
+        assert pool.blocks_per_seq >= 256 and pool.mapped_bytes == 0
+
+        def backed(blocks):  # K and V bytes behind the first `blocks` blocks
+            return 2 * -(-blocks * block // page) * page
+
+        pool.map(1, 1)  # one position -> the pages of one block, K and V
+        assert pool.mapped_bytes == backed(1)
+        pool.map(1, 1)  # grows only
+        assert pool.mapped_bytes == backed(1)
+        pool.map(1, 16 * 70 + 1)  # 71 blocks
+        assert pool.mapped_bytes == backed(71)
+        pool.map(2, 4096)
+        assert pool.mapped_bytes == backed(71) + backed(256)
+        with pytest.raises(pk.PagedKVError):
+            pool.map(0, pool.blocks_per_seq * 16 + 1)  # beyond the region
+        k = torch.zeros((3, 8, 16, 128), dtype=torch.bfloat16, device="cuda")
+        v = torch.zeros((3, 8, 128, 16), dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(pk.PagedKVError):
+            pool.write(0, k, v)  # sequence 0 has nothing mapped: refused on the host
+        pool.write(1, k, v)
+        got_k, got_v = pool.read(1, 3)
+        assert torch.equal(got_k, k) and torch.equal(got_v, v)
+        pool.unmap(1)
+        assert pool.mapped_bytes == backed(256)
+        pool.unmap(2)
+        assert pool.mapped_bytes == 0
