@@ -28,6 +28,11 @@ What is computed, and where each step comes from:
 * Requests that share a prefix share its KV blocks (Hacker News discussion of
   PagedAttention, replies on prefix sharing); a private copy of a shared block
   (copy-on-write) copies every element of the block.
+* Prefill: the first forward pass over the prompt computes every prompt token's output and
+  fills the cache, after which generation feeds one token at a time (Qualiteg post,
+  "Deepening Our Understanding ...", the past_key_values loop). A chunk of Q new tokens at the
+  end of a sequence of L positions is the same computation: the token at position p attends
+  to positions 0..p (causal), the whole prompt being the case Q = L.
 * Split-context partitions and their merge are not on the pages; they are an exact
   rewriting of the softmax sum: per partition p, m_p = max logit, l_p = sum exp(s - m_p),
   o_p = sum exp(s - m_p) v / l_p; then M = max m_p, w_p = l_p exp(m_p - M),
@@ -48,7 +53,7 @@ import math
 import numpy as np
 
 __all__ = ["to_f64", "write_cache", "copy_blocks", "gather", "decode", "decode_partials",
-           "reduce_partials", "num_partitions"]
+           "reduce_partials", "num_partitions", "prefill"]
 
 
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
@@ -139,6 +144,35 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads,
             K, V = gather(k_cache, v_cache, block_tables[i], L, g, S, dtype)
             for h in range(g * G, (g + 1) * G):
                 out[i, h] = _attend(qf[i, h], K, V, scale)
+    return out
+
+
+def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+            num_kv_heads, dtype):
+    """Causal attention of each sequence's new tokens over its cache.
+
+    Sequence i has Q_i = query_start[i + 1] - query_start[i] new tokens, rows
+    query_start[i] .. query_start[i + 1] - 1 of q [T, H, D], at positions L_i - Q_i .. L_i - 1
+    (L_i = context_lens[i], the cache holding all L_i positions). The token at position p and
+    head h gets softmax(scale * q K_i[0..p]^T) V_i[0..p] over kv head h // G. Returns float64
+    [T, H, D]."""
+    T, H, D = q.shape
+    G = H // num_kv_heads
+    assert G * num_kv_heads == H
+    S = k_cache.shape[2]
+    qf = to_f64(q, dtype)
+    out = np.zeros((T, H, D))
+    for i in range(len(context_lens)):
+        L = int(context_lens[i])
+        r0, r1 = int(query_start[i]), int(query_start[i + 1])
+        Q = r1 - r0
+        assert 0 <= Q <= L, "more new tokens than positions"
+        for g in range(num_kv_heads):
+            K, V = gather(k_cache, v_cache, block_tables[i], L, g, S, dtype)
+            for t in range(Q):
+                p = L - Q + t
+                for h in range(g * G, (g + 1) * G):
+                    out[r0 + t, h] = _attend(qf[r0 + t, h], K[:p + 1], V[:p + 1], scale)
     return out
 
 

@@ -87,6 +87,9 @@ class Config:
     prefix_len: int = 0  # "prefix": shared prefix tokens (a multiple of block_size)
     cow_seqs: int = 0  # "prefix": sequences whose last shared block gets a private copy
     partition_size: int = 0  # 0 = single pass; >0 = split-context partitions of this size
+    # Query tokens per sequence: 0 = decode (the newest token only); > 0 = chunked prefill of
+    # min(query_len, L_i) new tokens at the end of each context; -1 = whole-prompt prefill.
+    query_len: int = 0
     description: str = ""
 
     @property
@@ -134,6 +137,25 @@ CONFIGS = {
                              "D128, S32, 512-token partitions"),
 }
 
+# Prefill workloads: a chunk of new tokens per sequence over its paged cache (chunked
+# prefill), and whole prompts (the first forward pass of generation).
+PREFILL = {
+    "p1": Config("p1", 16, 32, 8, 128, 16, 8192, "bf16", 2475, "uniform", len_lo=1024,
+                 len_hi=4096, query_len=512,
+                 description="GQA chunked prefill bf16, 16 seqs, 512-token chunks over "
+                             "contexts U[1024, 4096], 32/8 heads, D128, S16"),
+    "p2": Config("p2", 8, 32, 8, 128, 16, 2048, "bf16", 2476, "uniform", len_lo=256,
+                 len_hi=2048, query_len=-1,
+                 description="GQA whole-prompt prefill bf16, 8 prompts U[256, 2048], "
+                             "32/8 heads, D128, S16"),
+}
+PREFILL_SMALL = {
+    "p1": PREFILL["p1"].replace(name="p1s", num_seqs=4, num_heads=8, num_kv_heads=2,
+                                num_blocks=120, len_lo=40, len_hi=300, query_len=70),
+    "p2": PREFILL["p2"].replace(name="p2s", num_seqs=3, num_heads=8, num_kv_heads=2,
+                                num_blocks=60, len_lo=1, len_hi=200),
+}
+
 # Reduced versions with the same structure (ragged tails, several blocks and partitions,
 # GQA groups, a shared prefix), small enough for the oracle to finish in well under a second.
 SMALL = {
@@ -170,6 +192,12 @@ class Workload:
     slot_mapping: np.ndarray  # int64 [B]: slot = block_id * S + offset of that token
     logical_k: list | None = None  # per sequence [L_i, Hkv, D], the whole logical stream
     logical_v: list | None = None
+    # Prefill workloads (query_len != 0): query tokens of sequence i are rows
+    # query_start[i] .. query_start[i + 1] - 1 of q_prefill [T, H, D], at positions
+    # L_i - Q_i .. L_i - 1; the pool then holds every position, the newest included.
+    query_lens: np.ndarray | None = None  # int32 [B]
+    query_start: np.ndarray | None = None  # int32 [B + 1]
+    q_prefill: np.ndarray | None = None
     meta: dict = field(default_factory=dict)
 
     @property
@@ -179,6 +207,31 @@ class Workload:
     @property
     def total_tokens(self) -> int:
         return int(self.context_lens.astype(np.int64).sum())
+
+    def prefill_flops(self) -> int:
+        """Multiply-adds x 2 of a prefill over the query tokens: each token at position p
+        attends to p + 1 positions, for QK^T and for PV, in every q head."""
+        c = self.cfg
+        total = 0
+        for L, Q in zip(self.context_lens.astype(np.int64), self.query_lens.astype(np.int64)):
+            first = L - Q + 1  # positions attended by the first query token
+            total += (first + L) * Q // 2
+        return int(total) * c.num_heads * c.head_dim * 4
+
+    def prefill_work_items(self, tile_tokens: int) -> np.ndarray:
+        """Host-side prefill schedule: units i * T + t (sequence i, query tile t of tile_tokens
+        tokens, T = tiles of the longest query) that have tokens, the most positions first."""
+        Q = self.query_lens.astype(np.int64)
+        L = self.context_lens.astype(np.int64)
+        T = max(int(-(-Q.max() // tile_tokens)), 1) if len(Q) else 1
+        units, cost = [], []
+        for i in range(len(Q)):
+            for t in range(-(-int(Q[i]) // tile_tokens)):
+                last = min((t + 1) * tile_tokens, int(Q[i]))
+                units.append(i * T + t)
+                cost.append(int(L[i] - Q[i]) + last)
+        order = np.argsort(-np.asarray(cost, dtype=np.int64), kind="stable")
+        return np.asarray(units, dtype=np.int32)[order]
 
     def work_items(self, partition_size: int = 0) -> np.ndarray:
         """Host-side decode schedule: the units that have work, largest first.
@@ -338,10 +391,11 @@ def generate(cfg: Config, poison: str = "nan", keep_logical: bool = False,
     pos_of = np.concatenate(pos_of) if B else np.zeros(0, np.int64)
     row_of = np.concatenate(row_of) if B else np.zeros(0, np.int64)
 
-    # The pool before the step holds every position except each sequence's newest one.
-    # Shared prefix positions are placed through sequence 0's (pre-CoW) table only.
+    # The pool before a decode step holds every position except each sequence's newest one
+    # (a prefill reads them all). Shared prefix positions are placed through sequence 0's
+    # (pre-CoW) table only.
     newest = pos_of == (L[seq_of].astype(np.int64) - 1)
-    place = ~newest
+    place = ~newest if cfg.query_len == 0 else np.ones_like(newest)
     if prefix:
         place &= (pos_of >= cfg.prefix_len) | (seq_of == 0)
     blk = tables_before[seq_of[place], pos_of[place] // S].astype(np.int64)
@@ -368,6 +422,12 @@ def generate(cfg: Config, poison: str = "nan", keep_logical: bool = False,
                   k_cache=k_cache, v_cache=v_cache, key=key, value=value,
                   slot_mapping=slot_mapping.astype(np.int64))
     wl.meta["blocks_used"] = cursor
+    if cfg.query_len != 0:
+        Qn = L.astype(np.int64) if cfg.query_len < 0 else np.minimum(L, cfg.query_len)
+        wl.query_lens = Qn.astype(np.int32)
+        wl.query_start = np.concatenate([[0], np.cumsum(Qn)]).astype(np.int32)
+        wl.q_prefill = cast_from_f32(
+            rng.standard_normal((int(Qn.sum()), H, D), dtype=np.float32), cfg.dtype)
     if keep_logical:
         starts = np.concatenate([[0], np.cumsum(L.astype(np.int64))])
         wl.logical_k = [ks[row_of[starts[i]:starts[i + 1]]] for i in range(B)]
