@@ -188,6 +188,37 @@ pkv_status pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t
 size_t pkv_partition_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                      int32_t max_context_len, int32_t partition_size);
 
+/* Paged prefill attention: causal attention of each sequence's new tokens over its paged
+ * cache. Sequence i has Q_i = query_start[i + 1] - query_start[i] new tokens, rows
+ * query_start[i] .. query_start[i + 1] - 1 of q and out, at positions L_i - Q_i .. L_i - 1
+ * (L_i = context_lens[i]; their K/V must already be in the cache, e.g. written with
+ * pkv_reshape_and_cache). The token at position p, head h gets
+ *   out = softmax(scale * q . K_i[0..p]^T) V_i[0..p]   over kv head h / (H / Hkv).
+ * Source: the first forward pass over the prompt that fills the cache before one-token
+ * generation (Qualiteg post, the past_key_values loop in "Deepening Our Understanding ...");
+ * a chunk on top of an existing cache is the same computation; blocks and block table as for
+ * decode (items 1-2, 2-1; vAttention section 3.1).
+ * q, out: device [T, H, D] (T = num_tokens = query_start[B]); k_cache, v_cache, block_tables,
+ * context_lens: as for decode; query_start: device int32 [B + 1], non-decreasing from 0;
+ * max_query_len: a host bound of every Q_i. Work is split into units (sequence i, tile t of
+ * pkv_prefill_tile_tokens query tokens), u = i * NT + t with NT = ceil(max_query_len / tile);
+ * work_items / num_work_items: NULL (all B * NT units in index order; tiles past Q_i do
+ * nothing) or a device int32 list of the units to run in dispatch order (each unit with tokens
+ * exactly once; most positions first shortens the tail). fp16/bf16 only; D in {64, 128};
+ * S in {16, 32}; G in {1, 2, 4, 8, 16}. Caller contract (not checked): Q_i <= L_i <= MB * S.
+ * Rows are written only for real tokens. */
+pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                       const int32_t* query_start, int32_t max_query_len,
+                                       const int32_t* work_items, int32_t num_work_items,
+                                       int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, int32_t num_blocks, float scale,
+                                       pkv_dtype dtype, void* stream);
+/* Query tokens per prefill work unit for this head shape (256 / G; 0 if unsupported). */
+int32_t pkv_prefill_tile_tokens(int32_t num_heads, int32_t num_kv_heads);
+
 /* ---- Virtually contiguous KV pool (the alternative to paging that vAttention proposes) ----
  *
  * The conventional layout gives each sequence one contiguous region sized for its maximum

@@ -5,8 +5,10 @@ ctypes binding. The seeded workload generators live in `workload`.
 """
 from ._lib import (KERNELS, DeviceRegion, PagedKVError, VmmPool, copy_blocks, load,
                    num_partitions, paged_attention, paged_attention_decode,
-                   paged_attention_reduce, partition_workspace, reshape_and_cache)
+                   paged_attention_prefill, paged_attention_reduce, partition_workspace,
+                   prefill_tile_tokens, reshape_and_cache)
 
 __all__ = ["KERNELS", "DeviceRegion", "PagedKVError", "VmmPool", "copy_blocks", "load",
            "num_partitions", "paged_attention", "paged_attention_decode",
-           "paged_attention_reduce", "partition_workspace", "reshape_and_cache"]
+           "paged_attention_prefill", "paged_attention_reduce", "partition_workspace",
+           "prefill_tile_tokens", "reshape_and_cache"]

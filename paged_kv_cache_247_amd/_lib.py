@@ -44,6 +44,9 @@ SIGNATURES = {
     "pkv_last_hip_error": (ctypes.c_int, []),
     "pkv_last_error_message": (ctypes.c_char_p, []),
     "pkv_abi_version": (ctypes.c_int, []),
+    "pkv_paged_attention_prefill": (_I, [_P, _P, _P, _P, _P, _I, _P, _P, _I, _P, _I, _I, _I,
+                                         _I, _I, _I, _I, _I, _F, _I, _P]),
+    "pkv_prefill_tile_tokens": (_I, [_I, _I]),
     "pkv_vmm_pool_create": (_I, [_I, _I, _I, _I, _I, _I, _Z, ctypes.POINTER(_P)]),
     "pkv_vmm_pool_map": (_I, [_P, _I, _I]),
     "pkv_vmm_pool_unmap": (_I, [_P, _I]),
@@ -252,6 +255,45 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         0 if work_items is None else work_items.shape[0], int(max_context_len), B, H,
         Hkv, D, S, N, float(scale), _dt(q), int(partition_size), _ptr(ml), _ptr(es), _ptr(to),
         _stream(q)))
+
+
+def prefill_tile_tokens(num_heads: int, num_kv_heads: int) -> int:
+    """Query tokens per prefill work unit (pkv_prefill_tile_tokens)."""
+    return load().pkv_prefill_tile_tokens(num_heads, num_kv_heads)
+
+
+def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
+                            max_query_len, scale, work_items=None):
+    """pkv_paged_attention_prefill: causal attention of each sequence's new tokens (rows
+    query_start[i] .. query_start[i + 1] - 1 of q [T, H, D], at the last Q_i positions of the
+    sequence, already in the cache) over its paged cache; writes out [T, H, D]. work_items:
+    optional device int32 list of units i * NT + t (tile t of prefill_tile_tokens tokens)."""
+    _need(q, "q", ndim=3)
+    dt = q.dtype
+    T, H, D = q.shape
+    _need(out, "out", dt, 3, q.device)
+    if tuple(out.shape) != (T, H, D):
+        raise ValueError("out must be shaped like q")
+    _need(k_cache, "k_cache", dt, 4, q.device)
+    N, Hkv, S, Dk = k_cache.shape
+    if Dk != D:
+        raise ValueError("head_dim of q and k_cache differ")
+    _need(v_cache, "v_cache", dt, 4, q.device)
+    if tuple(v_cache.shape) != (N, Hkv, D, S):
+        raise ValueError("v_cache must be [N, Hkv, D, S]")
+    _need(block_tables, "block_tables", torch.int32, 2, q.device)
+    B, MB = block_tables.shape
+    _need(context_lens, "context_lens", torch.int32, 1, q.device)
+    _need(query_start, "query_start", torch.int32, 1, q.device)
+    if context_lens.shape[0] != B or query_start.shape[0] != B + 1:
+        raise ValueError("context_lens [B] and query_start [B + 1] must match the tables")
+    if work_items is not None:
+        _need(work_items, "work_items", torch.int32, 1, q.device)
+    _check(load().pkv_paged_attention_prefill(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), MB,
+        _ptr(context_lens), _ptr(query_start), int(max_query_len), _ptr(work_items),
+        0 if work_items is None else work_items.shape[0], B, T, H, Hkv, D, S, N, float(scale),
+        _dt(q), _stream(q)))
 
 
 def paged_attention_reduce(out, workspace, context_lens, partition_size):

@@ -22,13 +22,14 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 SOURCES = ["api.cpp", "vmm.cpp", "cache_ops.hip", "decode_valu.hip", "decode_mfma.hip",
-           "reduce.hip"]
+           "reduce.hip", "prefill.hip"]
 ARCH = "gfx950"
 # Per-source extra flags. The decode MFMA kernel keeps its accumulators in ordinary VGPRs:
 # with the default heuristic the compiler puts them in AGPRs and copies them back and forth for
 # the per-chunk rescale, which costs instructions and pushes the 128-wide head past the
 # register budget of two waves per SIMD.
-EXTRA_FLAGS = {"decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA_FLAGS = {"decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

@@ -10,6 +10,7 @@
 #include "host_errors.hpp"
 #include "kernels.hpp"
 #include "pagedkv.h"
+#include "prefill.hpp"
 
 namespace {
 thread_local int t_last_hip = 0;
@@ -263,6 +264,71 @@ pkv_status pkv_paged_attention_reduce(void* out, const float* max_logits,
   p.partition_size = partition_size;
   p.max_num_partitions = max_num_partitions;
   return hip_status(pkv::launch_reduce(to_dt(dtype), head_dim, p, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+int32_t pkv_prefill_tile_tokens(int32_t num_heads, int32_t num_kv_heads) {
+  if (num_kv_heads <= 0 || num_heads <= 0 || num_heads % num_kv_heads) return 0;
+  const int G = num_heads / num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return 0;
+  return pkv::kPrefillRows / G;
+}
+
+pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                       const int32_t* query_start, int32_t max_query_len,
+                                       const int32_t* work_items, int32_t num_work_items,
+                                       int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, int32_t num_blocks, float scale,
+                                       pkv_dtype dtype, void* stream) {
+  const char* fn = "pkv_paged_attention_prefill";
+  pkv_status st = check_tile(fn, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PKV_OK) return st;
+  if (dtype == PKV_F32)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: fp32 inputs (the matrix-core kernel takes fp16/bf16)", fn);
+  if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0 || num_work_items < 0)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: num_seqs %d num_tokens %d max_query_len %d", fn,
+                num_seqs, num_tokens, max_query_len);
+  if (num_heads <= 0 || num_heads % num_kv_heads)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: num_heads %d not a positive multiple of num_kv_heads %d",
+                fn, num_heads, num_kv_heads);
+  const int32_t tile = pkv_prefill_tile_tokens(num_heads, num_kv_heads);
+  if (tile == 0)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: query group %d (supported: 1, 2, 4, 8, 16)", fn,
+                num_heads / num_kv_heads);
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: num_blocks %d max_blocks_per_seq %d", fn,
+                num_blocks, max_blocks_per_seq);
+  if (!isfinite(scale)) return fail(PKV_ERR_INVALID_ARGUMENT, "%s: scale is not finite", fn);
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4) ||
+      (work_items && !aligned(work_items, 4)))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: a tensor pointer is null or misaligned", fn);
+  const int64_t tiles = ((int64_t)max_query_len + tile - 1) / tile;
+  const int64_t units = work_items ? num_work_items : (int64_t)num_seqs * tiles;
+  if ((int64_t)num_seqs * tiles > INT32_MAX || units * num_kv_heads > INT32_MAX)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: too many work units", fn);
+  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0 || units == 0) return PKV_OK;
+  pkv::PrefillParams p;
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.query_start = query_start;
+  p.work_items = work_items;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.num_tiles = (int32_t)tiles;
+  p.num_units = (int32_t)units;
+  p.scale_log2e = scale * pkv::kLog2e;
+  return hip_status(pkv::launch_prefill(to_dt(dtype), head_dim, block_size, p,
+                                        reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
 pkv_status pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,

@@ -88,13 +88,13 @@ pkv_status add_pages(pkv_vmm_pool* p, int kv, int32_t seq, size_t want) {
     char* at = region(p, kv, seq) + v.size() * p->page_bytes;
     e = hipMemMap(at, p->page_bytes, 0, h, 0);
     if (e != hipSuccess) {
-      hipMemRelease(h);
+      (void)hipMemRelease(h);
       return pkv::hip_failure(e, "pkv_vmm_pool_map: hipMemMap");
     }
     e = hipMemSetAccess(at, p->page_bytes, &access, 1);
     if (e != hipSuccess) {
-      hipMemUnmap(at, p->page_bytes);
-      hipMemRelease(h);
+      (void)hipMemUnmap(at, p->page_bytes);
+      (void)hipMemRelease(h);
       return pkv::hip_failure(e, "pkv_vmm_pool_map: hipMemSetAccess");
     }
     v.push_back(h);
@@ -191,7 +191,7 @@ void pkv_vmm_pool_destroy(pkv_vmm_pool* p) {
   if (!p) return;
   for (int kv = 0; kv < 2; ++kv) {
     for (int32_t s = 0; s < (int32_t)p->pages[kv].size(); ++s) drop_pages(p, kv, s, 0);
-    if (p->base[kv]) hipMemAddressFree(p->base[kv], p->seq_bytes * (size_t)p->num_seqs);
+    if (p->base[kv]) (void)hipMemAddressFree(p->base[kv], p->seq_bytes * (size_t)p->num_seqs);
   }
   delete p;
 }

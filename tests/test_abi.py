@@ -32,7 +32,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
-    assert len(names) == 20, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES), "binding prototypes out of step with the header"
@@ -148,3 +148,43 @@ def test_vmm_pool_validation(lib):
     assert lib.pkv_vmm_pool_k(None) is None and lib.pkv_vmm_pool_v(None) is None
     assert lib.pkv_vmm_pool_blocks_per_seq(None) == 0
     assert lib.pkv_vmm_pool_page_bytes(None) == 0 and lib.pkv_vmm_pool_mapped_bytes(None) == 0
+
+
+def prefill(lib, **kw):
+    a = dict(out=A16, q=A16, k=A16, v=A16, bt=A16, MB=4, lens=A16, qs=A16, maxq=64, order=None,
+             nitems=0, B=2, T=100, H=8, Hkv=2, D=128, S=16, N=32, scale=0.125, dtype=2)
+    a.update(kw)
+    return lib.pkv_paged_attention_prefill(
+        a["out"], a["q"], a["k"], a["v"], a["bt"], a["MB"], a["lens"], a["qs"], a["maxq"],
+        a["order"], a["nitems"], a["B"], a["T"], a["H"], a["Hkv"], a["D"], a["S"], a["N"],
+        a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=0), UNSUPPORTED),  # fp32
+    (dict(D=96), UNSUPPORTED),
+    (dict(S=8), UNSUPPORTED),
+    (dict(H=6, Hkv=4), INVALID),
+    (dict(H=64, Hkv=2), UNSUPPORTED),  # group 32
+    (dict(q=None), INVALID),
+    (dict(qs=A16 + 2), INVALID),
+    (dict(order=A16 + 2), INVALID),
+    (dict(B=-1), INVALID),
+    (dict(maxq=-1), INVALID),
+    (dict(N=0), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(B=0), OK),
+    (dict(T=0), OK),
+    (dict(order=A16, nitems=0), OK),  # an empty work list: nothing enqueued
+])
+def test_prefill_validation(lib, kw, status):
+    assert prefill(lib, **kw) == status
+
+
+def test_prefill_tile_tokens(lib):
+    assert lib.pkv_prefill_tile_tokens(32, 8) == 64
+    assert lib.pkv_prefill_tile_tokens(32, 32) == 256
+    assert lib.pkv_prefill_tile_tokens(64, 4) == 16
+    assert lib.pkv_prefill_tile_tokens(6, 4) == 0
+    assert lib.pkv_prefill_tile_tokens(96, 1) == 0
+    assert lib.pkv_prefill_tile_tokens(64, 2) == 0  # group 32
