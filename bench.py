@@ -29,6 +29,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix-core peak, AMD published
 
 # Launch configuration the benchmark uses for each workload: (kernel family, partition size,
 # cached K/V loads). With longest-first dispatch, single-pass decode is fastest up to 4k-token
@@ -52,7 +53,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c3", choices=sorted(LAUNCH))
+    ap.add_argument("--config", default="c3", choices=sorted(LAUNCH) + ["p1", "p2"],
+                    help="c1..c5: decode workloads; p1, p2: prefill workloads")
     ap.add_argument("--kernel", default=None, choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--unfused", action="store_true",
@@ -201,12 +203,118 @@ def launch_stats(torch, fn, launches: int, reps: int, warmup: int = 10):
             "max_us": round(per[-1], 3), "launches": launches, "reps": reps}
 
 
+def prefill_cpu_baseline(wl, one_s: float):
+    """The prefill oracle (fp64 numpy, one thread) over whole sequences of the workload,
+    longest contexts first, until about one_s seconds have run."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    c = wl.cfg
+    done, flops, dt = 0, 0, 0.0
+    with threadpool_limits(limits=1):
+        for i in np.argsort(-wl.context_lens, kind="stable"):
+            if dt >= one_s:
+                break
+            L, Q = int(wl.context_lens[i]), int(wl.query_lens[i])
+            r0 = int(wl.query_start[i])
+            t0 = time.perf_counter()
+            oracle.prefill(wl.q_prefill[r0:r0 + Q], wl.k_cache, wl.v_cache,
+                           wl.block_tables[i:i + 1], wl.context_lens[i:i + 1],
+                           np.array([0, Q], dtype=np.int32), c.scale, c.num_kv_heads, c.dtype)
+            dt += time.perf_counter() - t0
+            done += 1
+            flops += (2 * (L - Q) + Q + 1) * Q // 2 * c.num_heads * c.head_dim * 4
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {c.num_seqs} sequences (longest contexts first), fp64 numpy "
+                      f"prefill on one thread, {dt:.1f} s",
+            "cpu": cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def prefill_main(args):
+    """Prefill workloads: one step is the prefill attention launch over every sequence's new
+    tokens (their K/V already in the cache), work units largest first."""
+    import torch
+
+    import paged_kv_cache_247_amd as pk
+    from paged_kv_cache_247_amd import workload as W
+
+    cfg = W.PREFILL[args.config]
+    wl = W.generate(cfg, poison="zero")
+    cpu = None if args.no_cpu_baseline else prefill_cpu_baseline(wl, args.cpu_seconds)
+    pk.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    q, kc, vc = dev(wl.q_prefill), dev(wl.k_cache), dev(wl.v_cache)
+    bt, lens, qs = dev(wl.block_tables), dev(wl.context_lens), dev(wl.query_start)
+    out = torch.empty_like(q)
+    tile = pk.prefill_tile_tokens(cfg.num_heads, cfg.num_kv_heads)
+    order = dev(wl.prefill_work_items(tile))
+    maxq = int(wl.query_lens.max())
+
+    def prefill():
+        pk.paged_attention_prefill(out, q, kc, vc, bt, lens, qs, maxq, cfg.scale,
+                                   work_items=order)
+
+    kernels = {"paged_attention_prefill": launch_stats(torch, prefill, args.launches, args.reps)}
+    ev = []
+    for _ in range(args.warmup):
+        prefill()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        prefill()
+        e1.record()
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    launch_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    fl = wl.prefill_flops()
+    kernels["paged_attention_prefill"]["TFLOP_per_s"] = round(
+        fl / (kernels["paged_attention_prefill"]["median_us"] * 1e-6) / 1e12, 2)
+    line = {
+        "metric": "paged prefill TFLOP/s (% of MI355X bf16 matrix-core peak) + query tokens/s",
+        "value": round(fl / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.description}", "num_seqs": cfg.num_seqs,
+                   "num_heads": cfg.num_heads, "num_kv_heads": cfg.num_kv_heads,
+                   "head_dim": cfg.head_dim, "block_size": cfg.block_size, "seed": cfg.seed,
+                   "query_tokens": int(wl.query_start[-1]), "context_tokens": wl.total_tokens,
+                   "flops": fl, "tile_tokens": tile, "work_units": int(len(order))},
+        "query_tokens_per_s": round(int(wl.query_start[-1]) / (ms_step * 1e-3), 1),
+        "roofline": {"bound": "mfma", "achieved": round(fl / (launch_ms * 1e-3) / 1e12, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(fl / (launch_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "paged_attention_prefill",
+                     "ms_per_launch": round(launch_ms, 5), "flops_per_launch": fl},
+        "kernels": kernels,
+    }
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the "
               "decode path is single-GPU, see DESIGN.md for how it would shard)", file=sys.stderr)
         sys.exit(2)
+    if args.config in ("p1", "p2"):
+        prefill_main(args)
+        return
     from paged_kv_cache_247_amd import workload as W
 
     name = args.config
