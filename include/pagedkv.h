@@ -76,7 +76,8 @@ typedef enum {
   PKV_OK = 0,
   PKV_ERR_INVALID_ARGUMENT = 1, /* a size, pointer or alignment is wrong */
   PKV_ERR_UNSUPPORTED = 2,      /* a valid shape this build has no kernel for */
-  PKV_ERR_HIP = 3               /* the HIP runtime refused a launch */
+  PKV_ERR_HIP = 3,              /* the HIP runtime refused a launch */
+  PKV_ERR_NO_BLOCKS = 4         /* the block manager has too few free blocks */
 } pkv_status;
 
 typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
@@ -218,6 +219,68 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
                                        pkv_dtype dtype, void* stream);
 /* Query tokens per prefill work unit for this head shape (256 / G; 0 if unsupported). */
 int32_t pkv_prefill_tile_tokens(int32_t num_heads, int32_t num_kv_heads);
+
+/* ---- Host block manager ----
+ *
+ * The bookkeeping paging needs on the host (Qualiteg post: blocks taken "as needed" and
+ * released, item 1-3; logical blocks mapped to physical ones by the block table; per-iteration
+ * scheduling that swaps requests in and out, item 2-2; Hacker News discussion: prefix sharing
+ * with copy-on-write). Physical blocks [0, num_blocks) of the device pool carry reference
+ * counts; a sequence is an ordered list of blocks and a token count. Sharing (fork) adds
+ * references; appending a token into a block that other sequences still hold first moves the
+ * sequence to a private copy (the caller copies the block with pkv_copy_blocks); freeing drops
+ * references and returns blocks that reach zero. Swapping moves a sequence's blocks to a host
+ * pool of num_host_blocks (the caller copies them with pkv_swap_blocks) and back. Host-only, no
+ * GPU work; not thread-safe per manager. Sequence ids are caller-chosen non-negative int64. */
+typedef struct pkv_block_manager pkv_block_manager;
+
+pkv_status pkv_bm_create(int32_t num_blocks, int32_t num_host_blocks, int32_t block_size,
+                         pkv_block_manager** bm);
+void pkv_bm_destroy(pkv_block_manager* bm);
+int32_t pkv_bm_free_blocks(const pkv_block_manager* bm);       /* device blocks not in use */
+int32_t pkv_bm_free_host_blocks(const pkv_block_manager* bm);
+/* A new sequence holding num_tokens positions (its prompt): ceil(num_tokens / S) fresh
+ * blocks. PKV_ERR_NO_BLOCKS (nothing changed) if they are not all free. */
+pkv_status pkv_bm_add(pkv_block_manager* bm, int64_t seq, int32_t num_tokens);
+/* child becomes a copy of parent that shares all of its blocks (one more reference each). */
+pkv_status pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child);
+/* Room for one more token of seq: returns its slot (block * S + offset). If the token opens a
+ * new block, a fresh block is appended. If it falls into a block that is shared, the sequence
+ * gets a fresh private block in its place and *copy_src / *copy_dst name the block to copy
+ * (else both are -1); the copy must happen before the token is written. PKV_ERR_NO_BLOCKS
+ * (nothing changed) if a needed block is not free. */
+pkv_status pkv_bm_append(pkv_block_manager* bm, int64_t seq, int64_t* slot, int32_t* copy_src,
+                         int32_t* copy_dst);
+/* Drop seq: every block loses one reference; blocks reaching zero are free again. */
+pkv_status pkv_bm_free(pkv_block_manager* bm, int64_t seq);
+int32_t pkv_bm_num_tokens(const pkv_block_manager* bm, int64_t seq);  /* -1 if unknown */
+int32_t pkv_bm_ref_count(const pkv_block_manager* bm, int32_t block);  /* -1 if out of range */
+/* Block tables of n sequences (host int32 [n, max_blocks], -1 past each sequence's blocks)
+ * and their token counts (host int32 [n]). PKV_ERR_INVALID_ARGUMENT if a sequence is unknown,
+ * swapped out, or holds more than max_blocks blocks. */
+pkv_status pkv_bm_tables(const pkv_block_manager* bm, const int64_t* seqs, int32_t n,
+                         int32_t max_blocks, int32_t* tables, int32_t* context_lens);
+/* Swap seq out to host blocks: fills pairs (host int32 [2 * nb], nb = its block count) with
+ * (device block, host block) and releases its device references (a shared block stays on the
+ * device for its other holders, and this sequence gets a host copy of it).
+ * *num_pairs = nb. PKV_ERR_NO_BLOCKS (nothing changed) without enough free host blocks. */
+pkv_status pkv_bm_swap_out(pkv_block_manager* bm, int64_t seq, int32_t* pairs,
+                           int32_t max_pairs, int32_t* num_pairs);
+/* Swap seq back in: fresh device blocks; pairs = (host block, device block). */
+pkv_status pkv_bm_swap_in(pkv_block_manager* bm, int64_t seq, int32_t* pairs, int32_t max_pairs,
+                          int32_t* num_pairs);
+
+/* Copy whole blocks between a device pool and a host pool (both K and V, one layer):
+ * for each pair (src, dst) of host int32 pairs [2 * num_pairs], block dst of (dst_k, dst_v)
+ * becomes a copy of block src of (src_k, src_v); every block is block_bytes long, and the
+ * pools hold num_src_blocks / num_dst_blocks blocks (pairs outside them are refused before
+ * anything is enqueued). to_device != 0: sources are host memory, destinations device
+ * memory; else the reverse. Host pools should be pinned (hipHostMalloc) for the copies to be
+ * asynchronous on `stream`. */
+pkv_status pkv_swap_blocks(const void* src_k, const void* src_v, int32_t num_src_blocks,
+                           void* dst_k, void* dst_v, int32_t num_dst_blocks,
+                           const int32_t* pairs, int32_t num_pairs, size_t block_bytes,
+                           int32_t to_device, void* stream);
 
 /* ---- Virtually contiguous KV pool (the alternative to paging that vAttention proposes) ----
  *

@@ -47,6 +47,21 @@ SIGNATURES = {
     "pkv_paged_attention_prefill": (_I, [_P, _P, _P, _P, _P, _I, _P, _P, _I, _P, _I, _I, _I,
                                          _I, _I, _I, _I, _I, _F, _I, _P]),
     "pkv_prefill_tile_tokens": (_I, [_I, _I]),
+    "pkv_bm_create": (_I, [_I, _I, _I, ctypes.POINTER(_P)]),
+    "pkv_bm_destroy": (None, [_P]),
+    "pkv_bm_free_blocks": (_I, [_P]),
+    "pkv_bm_free_host_blocks": (_I, [_P]),
+    "pkv_bm_add": (_I, [_P, ctypes.c_int64, _I]),
+    "pkv_bm_fork": (_I, [_P, ctypes.c_int64, ctypes.c_int64]),
+    "pkv_bm_append": (_I, [_P, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64),
+                           ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "pkv_bm_free": (_I, [_P, ctypes.c_int64]),
+    "pkv_bm_num_tokens": (_I, [_P, ctypes.c_int64]),
+    "pkv_bm_ref_count": (_I, [_P, _I]),
+    "pkv_bm_tables": (_I, [_P, _P, _I, _I, _P, _P]),
+    "pkv_bm_swap_out": (_I, [_P, ctypes.c_int64, _P, _I, ctypes.POINTER(_I)]),
+    "pkv_bm_swap_in": (_I, [_P, ctypes.c_int64, _P, _I, ctypes.POINTER(_I)]),
+    "pkv_swap_blocks": (_I, [_P, _P, _I, _P, _P, _I, _P, _I, _Z, _I, _P]),
     "pkv_vmm_pool_create": (_I, [_I, _I, _I, _I, _I, _I, _Z, ctypes.POINTER(_P)]),
     "pkv_vmm_pool_map": (_I, [_P, _I, _I]),
     "pkv_vmm_pool_unmap": (_I, [_P, _I]),
@@ -88,10 +103,18 @@ def load(path: str | None = None) -> ctypes.CDLL:
     return lib
 
 
+class OutOfBlocks(PagedKVError):
+    """PKV_ERR_NO_BLOCKS: the block manager has too few free blocks (nothing was changed)."""
+
+
+PKV_ERR_NO_BLOCKS = 4
+
+
 def _check(status: int):
     if status != 0:
         lib = load()
-        raise PagedKVError(status, lib.pkv_last_error_message().decode())
+        cls = OutOfBlocks if status == PKV_ERR_NO_BLOCKS else PagedKVError
+        raise cls(status, lib.pkv_last_error_message().decode())
 
 
 def _stream(t: torch.Tensor):
@@ -421,3 +444,93 @@ class VmmPool:
 
     def __exit__(self, *exc):
         self.close()
+
+
+class BlockManager:
+    """pkv_bm_*: reference-counted physical blocks of a device pool and a host pool, per-sequence
+    block lists, fork (sharing), copy-on-write on append, swap out/in. Host bookkeeping only:
+    the copies it asks for are the caller's (copy_blocks, swap_blocks)."""
+
+    def __init__(self, num_blocks: int, num_host_blocks: int, block_size: int):
+        h = ctypes.c_void_p()
+        _check(load().pkv_bm_create(num_blocks, num_host_blocks, block_size, ctypes.byref(h)))
+        self._h = h
+        self.num_blocks, self.num_host_blocks, self.block_size = num_blocks, num_host_blocks, block_size
+
+    def __del__(self):
+        if getattr(self, "_h", None):
+            load().pkv_bm_destroy(self._h)
+            self._h = None
+
+    @property
+    def free_blocks(self) -> int:
+        return load().pkv_bm_free_blocks(self._h)
+
+    @property
+    def free_host_blocks(self) -> int:
+        return load().pkv_bm_free_host_blocks(self._h)
+
+    def add(self, seq: int, num_tokens: int):
+        _check(load().pkv_bm_add(self._h, seq, num_tokens))
+
+    def fork(self, parent: int, child: int):
+        _check(load().pkv_bm_fork(self._h, parent, child))
+
+    def append(self, seq: int):
+        """Slot of seq's next token, and the (src, dst) block copy it needs first (or None)."""
+        slot, src, dst = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+        _check(load().pkv_bm_append(self._h, seq, ctypes.byref(slot), ctypes.byref(src),
+                                    ctypes.byref(dst)))
+        return slot.value, (None if src.value < 0 else (src.value, dst.value))
+
+    def free(self, seq: int):
+        _check(load().pkv_bm_free(self._h, seq))
+
+    def num_tokens(self, seq: int) -> int:
+        return load().pkv_bm_num_tokens(self._h, seq)
+
+    def ref_count(self, block: int) -> int:
+        return load().pkv_bm_ref_count(self._h, block)
+
+    def tables(self, seqs, max_blocks: int):
+        """(int32 [n, max_blocks] block tables, int32 [n] token counts) of the sequences."""
+        import numpy as np
+        ids = np.ascontiguousarray(seqs, dtype=np.int64)
+        t = np.empty((len(ids), max_blocks), dtype=np.int32)
+        lens = np.empty(len(ids), dtype=np.int32)
+        _check(load().pkv_bm_tables(self._h, ids.ctypes.data, len(ids), max_blocks,
+                                    t.ctypes.data, lens.ctypes.data))
+        return t, lens
+
+    def _swap(self, fn, seq, max_pairs):
+        import numpy as np
+        pairs = np.empty((max(max_pairs, 1), 2), dtype=np.int32)
+        n = ctypes.c_int32()
+        _check(fn(self._h, seq, pairs.ctypes.data, max_pairs, ctypes.byref(n)))
+        return pairs[:n.value].copy()
+
+    def swap_out(self, seq: int, max_pairs: int = 1 << 16):
+        """(device block, host block) pairs to copy out; seq now lives in host blocks."""
+        return self._swap(load().pkv_bm_swap_out, seq, max_pairs)
+
+    def swap_in(self, seq: int, max_pairs: int = 1 << 16):
+        """(host block, device block) pairs to copy in; seq lives on the device again."""
+        return self._swap(load().pkv_bm_swap_in, seq, max_pairs)
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, pairs, to_device: bool):
+    """pkv_swap_blocks: copy whole blocks (pairs int32 [M, 2] of (src, dst)) between a device
+    pool and a host pool, on the current stream. The host pools are pinned CPU tensors shaped
+    like the device pools."""
+    import numpy as np
+    dev = dst_k if to_device else src_k
+    for t, nm in ((src_k, "src_k"), (src_v, "src_v"), (dst_k, "dst_k"), (dst_v, "dst_v")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if src_k.shape[1:] != dst_k.shape[1:] or src_v.shape[1:] != dst_v.shape[1:]:
+        raise ValueError("pools of different block shapes")
+    pairs = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    block_bytes = src_k[0].numel() * src_k.element_size()
+    _check(load().pkv_swap_blocks(_ptr(src_k), _ptr(src_v), src_k.shape[0], _ptr(dst_k),
+                                  _ptr(dst_v), dst_k.shape[0], pairs.ctypes.data, len(pairs),
+                                  block_bytes, 1 if to_device else 0, _stream(dev)))

@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
-SOURCES = ["api.cpp", "vmm.cpp", "cache_ops.hip", "decode_valu.hip", "decode_mfma.hip",
+SOURCES = ["api.cpp", "vmm.cpp", "block_manager.cpp", "cache_ops.hip", "decode_valu.hip", "decode_mfma.hip",
            "reduce.hip", "prefill.hip"]
 ARCH = "gfx950"
 # Per-source extra flags. The decode MFMA kernel keeps its accumulators in ordinary VGPRs:

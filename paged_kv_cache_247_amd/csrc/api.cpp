@@ -380,6 +380,7 @@ const char* pkv_status_string(pkv_status s) {
     case PKV_ERR_INVALID_ARGUMENT: return "invalid argument";
     case PKV_ERR_UNSUPPORTED: return "unsupported shape";
     case PKV_ERR_HIP: return "HIP runtime error";
+    case PKV_ERR_NO_BLOCKS: return "out of blocks";
   }
   return "unknown status";
 }
