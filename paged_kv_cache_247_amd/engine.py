@@ -1,0 +1,195 @@
+"""A live decode loop over the paged kernels: an iteration-level scheduler on top of the block
+manager, on synthetic tokens.
+
+Continuous batching as the Qualiteg post describes it ("In a Nutshell ..." item 2-2): the
+batch is re-formed at every iteration instead of per request, so requests join as soon as
+their blocks fit, leave the moment they finish, and are swapped out to host memory and back
+when the pool runs short (item 1-3: blocks are taken and returned as needed). Requests that
+share a prefix share its blocks and get private copies of a shared block when they write into
+it (Hacker News discussion of PagedAttention).
+
+There is no model: the query, key and value vectors of position p of request r are seeded
+draws (N(0,1) rounded to the cache type), so that every step's attention can be checked
+against a plain reference over each sequence's history. Each step is: swap-ins, admissions
+(the prompt's K/V written with reshape_and_cache), one slot per running sequence (copy-on-write
+block copies first; preemption by swap-out when blocks run out), then one decode launch that
+also writes every sequence's newest K/V. Everything runs on the current stream in that order.
+"""
+from __future__ import annotations
+
+import dataclasses
+from collections import deque
+
+import numpy as np
+import torch
+
+from . import _lib as L
+from .workload import cast_from_f32
+
+_TORCH = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
+@dataclasses.dataclass
+class Request:
+    rid: int
+    prompt_len: int
+    new_tokens: int       # tokens to generate
+    generated: int = 0
+    origin: int = -1      # request whose stream this one continues (forks), -1 = its own
+    fork_pos: int = 0     # positions inherited from origin
+
+
+class DecodeEngine:
+    def __init__(self, num_blocks: int, num_host_blocks: int, num_heads: int, num_kv_heads: int,
+                 head_dim: int, block_size: int, max_blocks_per_seq: int, dtype: str = "bf16",
+                 seed: int = 0):
+        self.H, self.Hkv, self.D, self.S = num_heads, num_kv_heads, head_dim, block_size
+        self.MB, self.dtype, self.seed = max_blocks_per_seq, dtype, seed
+        self.bm = L.BlockManager(num_blocks, num_host_blocks, block_size)
+        tdt = _TORCH[dtype]
+        self.k = torch.zeros((num_blocks, num_kv_heads, block_size, head_dim), dtype=tdt,
+                             device="cuda")
+        self.v = torch.zeros((num_blocks, num_kv_heads, head_dim, block_size), dtype=tdt,
+                             device="cuda")
+        self.hk = torch.zeros((max(num_host_blocks, 1), num_kv_heads, block_size, head_dim),
+                              dtype=tdt, pin_memory=True)
+        self.hv = torch.zeros((max(num_host_blocks, 1), num_kv_heads, head_dim, block_size),
+                              dtype=tdt, pin_memory=True)
+        self.requests: dict[int, Request] = {}
+        self.waiting: deque[int] = deque()
+        self.running: list[int] = []
+        self.swapped: deque[int] = deque()
+        self.finished: list[int] = []
+        self.stats = {"steps": 0, "swap_outs": 0, "swap_ins": 0, "cow_copies": 0,
+                      "admitted": 0}
+
+    # ------------------------------------------------------------ synthetic tokens
+    def _stream_owner(self, rid: int, pos: int) -> int:
+        """Request whose stream holds position pos of rid (forks inherit their origin's)."""
+        r = self.requests[rid]
+        while r.origin >= 0 and pos < r.fork_pos:
+            r = self.requests[r.origin]
+        return r.rid
+
+    def token(self, rid: int, pos: int):
+        """(q [H, D], k [Hkv, D], v [Hkv, D]) of position pos of request rid, storage type."""
+        owner = self._stream_owner(rid, pos)
+        rng = np.random.default_rng([self.seed, owner, pos])
+        x = rng.standard_normal((self.H + 2 * self.Hkv, self.D), dtype=np.float32)
+        x = cast_from_f32(x, self.dtype)
+        return x[:self.H], x[self.H:self.H + self.Hkv], x[self.H + self.Hkv:]
+
+    def _dev(self, a: np.ndarray) -> torch.Tensor:
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    # ------------------------------------------------------------ requests
+    def submit(self, rid: int, prompt_len: int, new_tokens: int):
+        self.requests[rid] = Request(rid, prompt_len, new_tokens)
+        self.waiting.append(rid)
+
+    def fork(self, parent: int, child: int, new_tokens: int):
+        """child continues parent's sequence as it stands, sharing its blocks; its own tokens
+        start at the parent's current length."""
+        if parent not in self.running:
+            raise ValueError("only a running request can be forked")
+        n = self.bm.num_tokens(parent)
+        self.bm.fork(parent, child)
+        self.requests[child] = Request(child, n, new_tokens, origin=parent, fork_pos=n)
+        self.running.append(child)
+
+    # ------------------------------------------------------------ one iteration
+    def _write_prompt(self, rid: int):
+        n = self.requests[rid].prompt_len
+        if n == 0:
+            return
+        t, _ = self.bm.tables([rid], self.MB)
+        pos = np.arange(n)
+        slots = t[0, pos // self.S].astype(np.int64) * self.S + pos % self.S
+        toks = [self.token(rid, int(p)) for p in pos]
+        ks = np.stack([k for _, k, _ in toks])
+        vs = np.stack([v for _, _, v in toks])
+        L.reshape_and_cache(self._dev(ks), self._dev(vs), self.k, self.v, self._dev(slots))
+
+    def _swap_out(self, rid: int):
+        pairs = self.bm.swap_out(rid)
+        L.swap_blocks(self.k, self.v, self.hk, self.hv, pairs, to_device=False)
+        self.running.remove(rid)
+        self.swapped.appendleft(rid)
+        self.stats["swap_outs"] += 1
+
+    def _swap_in(self, rid: int):
+        pairs = self.bm.swap_in(rid)
+        L.swap_blocks(self.hk, self.hv, self.k, self.v, pairs, to_device=True)
+        self.running.append(rid)
+        self.stats["swap_ins"] += 1
+
+    def step(self):
+        """One iteration. Returns ({rid: (row of out, position decoded)}, out [B, H, D]) for
+        the sequences decoded this step (out is None when none ran)."""
+        # 1. swapped-out requests first (oldest preempted first), then new ones, while they fit
+        while self.swapped:
+            rid = self.swapped[0]
+            need = -(-self.bm.num_tokens(rid) // self.S) + 1
+            if self.bm.free_blocks < need:
+                break
+            self.swapped.popleft()
+            self._swap_in(rid)
+        while self.waiting and not self.swapped:
+            rid = self.waiting[0]
+            need = -(-self.requests[rid].prompt_len // self.S) + 1
+            if self.bm.free_blocks < need:
+                break
+            self.waiting.popleft()
+            self.bm.add(rid, self.requests[rid].prompt_len)
+            self._write_prompt(rid)
+            self.running.append(rid)
+            self.stats["admitted"] += 1
+        # 2. one slot per running sequence, in admission order. When blocks run out, the
+        # youngest sequence that has not taken its slot yet is swapped out (possibly the one
+        # asking), and the append is tried again.
+        copies, order, i = [], list(self.running), 0
+        while i < len(order):
+            rid = order[i]
+            try:
+                _, cow = self.bm.append(rid)
+            except L.OutOfBlocks:
+                if len(order) == 1:
+                    raise
+                self._swap_out(order.pop())
+                continue
+            if cow is not None:
+                copies.append(cow)
+            i += 1
+        if copies:
+            L.copy_blocks([self.k], [self.v], self._dev(np.asarray(copies, dtype=np.int64)))
+            self.stats["cow_copies"] += len(copies)
+        # 3. decode every running sequence, writing its newest K/V
+        seqs = order
+        if not seqs:
+            self.stats["steps"] += 1
+            return {}, None
+        t, lens = self.bm.tables(seqs, self.MB)
+        q = np.stack([self.token(r, int(n) - 1)[0] for r, n in zip(seqs, lens)])
+        kn = np.stack([self.token(r, int(n) - 1)[1] for r, n in zip(seqs, lens)])
+        vn = np.stack([self.token(r, int(n) - 1)[2] for r, n in zip(seqs, lens)])
+        out = torch.empty((len(seqs), self.H, self.D), dtype=_TORCH[self.dtype], device="cuda")
+        L.paged_attention(out, self._dev(q), self.k, self.v, self._dev(t), self._dev(lens),
+                          int(lens.max()), 1.0 / float(np.sqrt(self.D)), 0,
+                          new_key=self._dev(kn), new_value=self._dev(vn))
+        # 4. finish
+        result = {r: (k, int(n) - 1) for k, (r, n) in enumerate(zip(seqs, lens))}
+        for r in seqs:
+            req = self.requests[r]
+            req.generated += 1
+            if req.generated >= req.new_tokens:
+                self.bm.free(r)
+                self.running.remove(r)
+                self.finished.append(r)
+        self.stats["steps"] += 1
+        return result, out
+
+    def done(self) -> bool:
+        return not (self.waiting or self.running or self.swapped)
