@@ -217,7 +217,7 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
                                        int32_t num_kv_heads, int32_t head_dim,
                                        int32_t block_size, int32_t num_blocks, float scale,
                                        pkv_dtype dtype, void* stream);
-/* Query tokens per prefill work unit for this head shape (256 / G; 0 if unsupported). */
+/* Query tokens per prefill work unit for this head shape (128 / G; 0 if unsupported). */
 int32_t pkv_prefill_tile_tokens(int32_t num_heads, int32_t num_kv_heads);
 
 /* ---- Host block manager ----

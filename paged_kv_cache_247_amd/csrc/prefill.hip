@@ -9,16 +9,19 @@
 // (same post, "There are logical blocks and physical blocks ..."), as the attention operator
 // over non-contiguous KV-cache blocks requires (vAttention, section 3.1).
 //
-// Work: a workgroup of 8 waves owns (sequence i, kv head g, a tile of 256 / G query tokens):
-// 256 rows (token x head of the group, token-major), 32 per wave as two 16-column tiles of
+// Work: a workgroup of 4 waves owns (sequence i, kv head g, a tile of 128 / G query tokens):
+// 128 rows (token x head of the group, token-major), 32 per wave as two 16-column tiles of
 // v_mfma_f32_16x16x32_{bf16,f16}. Unlike decode, the query side is large, so every 32-position
 // KV chunk is staged in LDS once per workgroup (buffer loads straight into LDS, spread over the
-// waves, two stages) and read by all eight waves: for each column tile the logits
-// S^T = K Q^T (rows positions, columns query rows; K rows permuted as in decode so that a
-// lane's accumulator holds eight consecutive positions of its own row), the causal mask and
-// online softmax of the lane's own row, then O^T += V^T P^T with V^T read from LDS as the A
-// operand. Consecutive workgroups take consecutive kv heads, so with 8 kv heads every tile of
-// one head runs on the same XCD and the tiles of a sequence share that XCD's L2.
+// waves, a ring of four stages with one barrier per chunk) and read by all four waves: for
+// each column tile the logits S^T = K Q^T (rows positions, columns query rows; K rows permuted
+// as in decode so that a lane's accumulator holds eight consecutive positions of its own row),
+// the causal mask (only on chunks that reach a row's limit) and online softmax of the lane's
+// own row, then O^T += V^T P^T with V^T read from LDS as the A operand, and the row sums as a
+// tile of ones times P^T. Two workgroups share a CU, so that one's softmax (vector ALU) runs
+// beside the other's matrix products instead of in lockstep behind the same barriers.
+// Consecutive workgroups take consecutive kv heads, so with 8 kv heads every tile of one head
+// runs on the same XCD and the tiles of a sequence share that XCD's L2.
 #include <type_traits>
 
 #include "prefill.hpp"
@@ -33,6 +36,7 @@ template <> struct PMfma<Dt::BF16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ __bf16 narrow(float x) { return (__bf16)x; }
+  static constexpr uint32_t kOnePair = 0x3f803f80u;  // two bf16 1.0
 };
 template <> struct PMfma<Dt::F16> {
   using V8 = f16x8;
@@ -40,6 +44,22 @@ template <> struct PMfma<Dt::F16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ _Float16 narrow(float x) { return (_Float16)x; }
+  static constexpr uint32_t kOnePair = 0x3c003c00u;  // two f16 1.0
+};
+
+// Maxima of logits that are finite or -inf. fmaxf also quiets signalling NaNs, which costs
+// an extra instruction per operand; these are the bare instructions.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float d;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+struct OpMaxRaw {
+  __device__ __forceinline__ float operator()(float a, float b) const {
+    float d;
+    asm("v_max_f32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+    return d;
+  }
 };
 
 // At most N vector memory operations of this wave outstanding (they complete in order).
@@ -61,6 +81,7 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 constexpr int kBufferFlags = 0x00020000;  // raw buffer descriptor dword 3 (gfx9 family)
+constexpr int kStages = 4;                 // LDS stages of KV chunks in flight
 
 template <Dt DT, int D, int S>
 __global__ void __launch_bounds__(kPrefillWaves * 64)
@@ -87,7 +108,7 @@ prefill_kernel(const PrefillParams a) {
   using M = PMfma<DT>;
   using V8 = typename M::V8;
   using T = typename Elt<DT>::T;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[kStages * STAGE];
 
   const int Hkv = a.num_kv_heads;
   const int H = a.num_heads;
@@ -121,6 +142,10 @@ prefill_kernel(const PrefillParams a) {
 
   // Lane (r, c) owns row rr = 32 wave + 16 j + c of each column tile j: token rr / G, head
   // g G + rr % G. Rows past the chunk's tokens compute on zero queries and are not stored.
+  // A negative scale is carried by the queries: flipping their sign bits is exact, and then
+  // the logits' scale factor cl is positive, so the scaled maximum is cl times the raw one.
+  const bool flip = a.scale_log2e < 0.0f;
+  const float cl = flip ? -a.scale_log2e : a.scale_log2e;
   int plim[2];
   bool valid[2];
   size_t orow[2];
@@ -138,6 +163,7 @@ prefill_kernel(const PrefillParams a) {
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (valid[j]) v = *reinterpret_cast<const u32x4*>(qbase + (orow[j] + 32 * kk + 8 * r) * EB);
+      if (flip) v ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
       qb[j][kk] = __builtin_bit_cast(V8, v);
     }
   }
@@ -171,32 +197,35 @@ prefill_kernel(const PrefillParams a) {
   };
   auto rot = [](int t) { return t + 4 * (t >> 4); };
 
-  // This wave's share of chunk n's loads into stage st: K pieces (rows of the chunk, pieces
-  // rotated as in decode) or V^T pieces (contiguous 1 KiB of a block's [D][S] tile).
+  // This wave's share of chunk n's loads into stage st: LPW consecutive 1 KiB pieces, all of
+  // K or all of V^T and all of one block (so one block id and one descriptor per chunk).
+  // K pieces are rows of the chunk with their 16-byte parts rotated as in decode; V^T pieces
+  // are contiguous 1 KiB of a block's [D][S] tile.
+  static_assert(TILE % (LPW * 1024) == 0, "a wave's loads of a chunk stay within one block");
+  const int x0 = wave * LPW;  // first piece: K pieces 0 .. NLK - 1, then V^T pieces
+  const bool wave_k = x0 < NLK;
+  const int xb = wave_k ? x0 : x0 - NLK;
+  const int wave_blk = xb * 1024 / TILE;  // block of the chunk these pieces come from
   auto issue = [&](int n, int st) {
     if (n * BPC >= 64 * (id_kb + 1)) {
       id_kb = (n * BPC) / 64;
       id_batch = load_id_batch(id_kb);
     }
-    char* dst = smem + st * STAGE;
+    char* dst = smem + st * STAGE + (wave_k ? 0 : KB);
+    // (A named descriptor: passed as a temporary, the host pass drops the kernel stub.)
+    const __amdgpu_buffer_rsrc_t rs = rsrc(wave_k ? kpool : vpool, block_id(n * BPC + wave_blk));
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
-      const int x = wave * LPW + j;
-      if (x < NLK) {
+      const int x = xb + j;
+      int voff;
+      if (wave_k) {
         const int t = x * (1024 / RB) + lane / NPC;
-        const int jt = (lane % NPC - rot(t)) & (NPC - 1);
-        // (A named descriptor: passed as a temporary, the host pass drops the kernel stub.)
-        const __amdgpu_buffer_rsrc_t rs = rsrc(kpool, block_id(n * BPC + t / S));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (__attribute__((address_space(3))) void*)(dst + x * 1024), 16,
-            (t % S) * RB + jt * 16, 0, 0, 0);
+        voff = (t % S) * RB + ((lane % NPC - rot(t)) & (NPC - 1)) * 16;
       } else {
-        const int xv = x - NLK;
-        const __amdgpu_buffer_rsrc_t rs = rsrc(vpool, block_id(n * BPC + xv / PPT));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (__attribute__((address_space(3))) void*)(dst + KB + xv * 1024), 16,
-            (xv % PPT) * 1024 + lane * 16, 0, 0, 0);
+        voff = (x % PPT) * 1024 + lane * 16;
       }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(dst + x * 1024), 16, voff, 0, 0, 0);
     }
   };
 
@@ -215,14 +244,14 @@ prefill_kernel(const PrefillParams a) {
         asm volatile("ds_read_b128 %0, %1" : "=v"(kr[gi][kk]) : "v"(addr) : "memory");
       }
     }
+    // V^T rows d = 16 nt + c: the nt step is a constant, carried in the instruction's offset.
+    const char* vp = (S == 16) ? vs + (r >> 1) * TILE + c * (S * EB) + (r & 1) * 16
+                               : vs + c * (S * EB) + r * 16;
+    const uint32_t vaddr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)vp;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int d = 16 * nt + c;
-      const char* p = (S == 16) ? vs + (r >> 1) * TILE + d * (S * EB) + (r & 1) * 16
-                                : vs + d * (S * EB) + r * 16;
-      const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-      asm volatile("ds_read_b128 %0, %1" : "=v"(vr[nt]) : "v"(addr) : "memory");
-    }
+    for (int nt = 0; nt < NT; ++nt)
+      asm volatile("ds_read_b128 %0, %1 offset:%2"
+                   : "=v"(vr[nt]) : "v"(vaddr), "i"(16 * nt * S * EB) : "memory");
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi)
@@ -232,24 +261,38 @@ prefill_kernel(const PrefillParams a) {
     for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+v"(vr[nt]));
   };
 
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
-  f32x4 acc[2][NT];
+  // Online softmax with a lazily moved reference: m[j] is the row's reference maximum (log2
+  // units), lsum[j] the row's sum of 2^(s - m) (every element of it: the sum comes from the
+  // matrix cores, a tile of ones times P^T, so it adds exactly the 16-bit weights that multiply
+  // V). A chunk whose maximum stays within kSlack of the reference uses it as it is: its
+  // weights are at most 2^kSlack, which the 16-bit P operand and the fp32 sums hold as well as
+  // weights below 1. Only when a row's maximum passes the reference by more than that (in
+  // practice the first chunk, and rarely later) does the wave move it and rescale the
+  // accumulators. The result, acc / lsum, does not depend on the reference.
+  constexpr float kSlack = 8.0f;
+  float m[2] = {-INFINITY, -INFINITY};
+  f32x4 acc[2][NT], lsum[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < 2; ++j) {
+    lsum[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[j][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  const V8 ones = __builtin_bit_cast(V8, u32x4{M::kOnePair, M::kOnePair, M::kOnePair, M::kOnePair});
 
   const int wave_first_limit = base + wt0;  // smallest limit among this wave's rows
   const int wave_last_limit = base + wt1;   // largest
 
-  auto compute = [&](int n, int st) {
+  // masked: the chunk reaches past some row's limit of this wave (the causal edge, or
+  // positions >= L).
+  auto compute = [&](int n, int st, bool masked) {
     u32x4 kr[2][KK];
     u32x4 vr[NT];
     read_stage(st, kr, vr);
     const int pos0 = n * CT + 8 * r;  // this lane's first position of the chunk
     // Positions at or past L may hold anything (even NaN): zero their V, 0 * NaN is NaN.
     const int nv = L - pos0;
-    if (n * CT + CT > L && nv < 8) {
+    if (masked && n * CT + CT > L && nv < 8) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint32_t keep = (2 * q + 1 < nv) ? 0xffffffffu : (2 * q < nv) ? 0x0000ffffu : 0u;
@@ -257,7 +300,6 @@ prefill_kernel(const PrefillParams a) {
         for (int nt = 0; nt < NT; ++nt) vr[nt][q] &= keep;
       }
     }
-    const bool need_mask = n * CT + CT - 1 > wave_first_limit;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -267,61 +309,62 @@ prefill_kernel(const PrefillParams a) {
         s1 = M::mac(__builtin_bit_cast(V8, kr[1][kk]), qb[j][kk], s1);
       }
       float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-      float mx = -INFINITY;
+      if (masked) {  // uniform: a branch, not a select on every chunk
+        const int lim = plim[j] - pos0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sv[e] = (!need_mask || pos0 + e <= plim[j]) ? sv[e] * a.scale_log2e : -INFINITY;
-        mx = fmaxf(mx, sv[e]);
+        for (int e = 0; e < 8; ++e) sv[e] = e <= lim ? sv[e] : -INFINITY;
       }
-      mx = across16(mx, OpMax());
-      mx = across32(mx, OpMax());
-      const float mnew = fmaxf(m[j], mx);  // finite: position 0 is in every row's range
-      const float alpha = __builtin_amdgcn_exp2f(m[j] - mnew);
-      m[j] = mnew;
+      float x = max3_raw(sv[0], sv[1], sv[2]);
+      x = max3_raw(x, sv[3], sv[4]);
+      x = max3_raw(x, sv[5], sv[6]);
+      x = OpMaxRaw()(x, sv[7]);
+      x = across16(x, OpMaxRaw());
+      x = across32(x, OpMaxRaw());
+      const float mx = x * cl;  // -inf when the chunk lies wholly past the row's limit
+      if (__builtin_amdgcn_ballot_w64(mx > m[j] + kSlack)) {
+        const float mnew = fmaxf(m[j], mx);  // finite: every row sees position 0 first
+        const float alpha = __builtin_amdgcn_exp2f(m[j] - mnew);
+        m[j] = mnew;
+        lsum[j] *= alpha;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[j][nt] *= alpha;
+      }
       V8 pb;
-      float psum = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pb[e] = M::narrow(__builtin_amdgcn_exp2f(sv[e] - mnew));
-        psum += (float)pb[e];
-      }
-      l[j] = fmaf(l[j], alpha, psum);
+      for (int e = 0; e < 8; ++e) pb[e] = M::narrow(__builtin_amdgcn_exp2f(fmaf(sv[e], cl, -m[j])));
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        acc[j][nt] *= alpha;
+      for (int nt = 0; nt < NT; ++nt)
         acc[j][nt] = M::mac(__builtin_bit_cast(V8, vr[nt]), pb, acc[j][nt]);
-      }
+      lsum[j] = M::mac(ones, pb, lsum[j]);
     }
   };
 
-  issue(0, 0);
+  // A ring of kStages stages, chunk n in stage n % kStages, loads running kStages - 1 chunks
+  // ahead, one barrier per chunk. At the top of iteration n this wave's loads of chunks up to
+  // n + kStages - 2 are issued; waiting until only those after chunk n remain, then the
+  // barrier, makes chunk n whole for every wave and tells that every wave is done with chunk
+  // n - 1, whose stage then takes chunk n + kStages - 1.
+  for (int k = 0; k < kStages - 1 && k < nch; ++k) issue(k, k);
   for (int n = 0; n < nch; ++n) {
-    const int st = n & 1;
-    stage_barrier();  // every wave is done with chunk n - 1: its stage may be refilled
-    if (n + 1 < nch) {
-      issue(n + 1, st ^ 1);
-      wait_vm_le<LPW>();  // this wave's loads of chunk n are in (it issued LPW since)
-    } else {
-      wait_vm_le<0>();
+    const int st = n % kStages;
+    switch (min(kStages - 2, nch - 1 - n)) {  // chunks issued after chunk n
+      case 0: wait_vm_le<0>(); break;
+      case 1: wait_vm_le<LPW>(); break;
+      default: wait_vm_le<2 * LPW>(); break;
     }
-    stage_barrier();  // every wave's loads of chunk n are in
-    if (wave_live && n * CT <= wave_last_limit) compute(n, st);
+    stage_barrier();
+    if (n + kStages - 1 < nch) issue(n + kStages - 1, (n + kStages - 1) % kStages);
+    if (wave_live && n * CT <= wave_last_limit) compute(n, st, n * CT + CT - 1 > wave_first_limit);
   }
 
-  // Lane (r, c) holds O^T[16 nt + 4 r + e][row c] of each column tile, and the part of the
-  // row's softmax sum over its own positions (the rescale factors were common to the four
-  // lanes of a column, so the parts add up).
+  // Lane (r, c) holds O^T[16 nt + 4 r + e][row c] of each column tile, and the row's whole
+  // softmax sum.
   if (!wave_live) return;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    l[j] = across16(l[j], OpAdd());
-    l[j] = across32(l[j], OpAdd());
-  }
   T* out = reinterpret_cast<T*>(a.out);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     if (!valid[j]) continue;
-    const float inv = 1.0f / l[j];
+    const float inv = 1.0f / lsum[j][0];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       T v4[4];

@@ -9,9 +9,9 @@
 
 namespace pkv {
 
-// Rows (query token x head of a kv-head group) of one workgroup: 8 waves of 32 rows. A work
-// unit is (sequence i, kv head g, tile t of 256 / G query tokens).
-constexpr int kPrefillWaves = 8;
+// Rows (query token x head of a kv-head group) of one workgroup: 4 waves of 32 rows. A work
+// unit is (sequence i, kv head g, tile t of 128 / G query tokens).
+constexpr int kPrefillWaves = 4;
 constexpr int kPrefillRows = kPrefillWaves * 32;
 
 struct PrefillParams {

@@ -182,9 +182,9 @@ def test_prefill_validation(lib, kw, status):
 
 
 def test_prefill_tile_tokens(lib):
-    assert lib.pkv_prefill_tile_tokens(32, 8) == 64
-    assert lib.pkv_prefill_tile_tokens(32, 32) == 256
-    assert lib.pkv_prefill_tile_tokens(64, 4) == 16
+    assert lib.pkv_prefill_tile_tokens(32, 8) == 32
+    assert lib.pkv_prefill_tile_tokens(32, 32) == 128
+    assert lib.pkv_prefill_tile_tokens(64, 4) == 8
     assert lib.pkv_prefill_tile_tokens(6, 4) == 0
     assert lib.pkv_prefill_tile_tokens(96, 1) == 0
     assert lib.pkv_prefill_tile_tokens(64, 2) == 0  # group 32
