@@ -27,9 +27,10 @@ ARCH = "gfx950"
 # Per-source extra flags. The decode MFMA kernel keeps its accumulators in ordinary VGPRs:
 # with the default heuristic the compiler puts them in AGPRs and copies them back and forth for
 # the per-chunk rescale, which costs instructions and pushes the 128-wide head past the
-# register budget of two waves per SIMD.
+# register budget of two waves per SIMD. The prefill kernel does the same, and is built without
+# NaN semantics (no arithmetic in it meets a NaN), so its maxima need no quieting instructions.
 EXTRA_FLAGS = {"decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-               "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+               "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
 
 
 def hipcc() -> str:

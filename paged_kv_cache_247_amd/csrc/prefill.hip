@@ -22,6 +22,10 @@
 // beside the other's matrix products instead of in lockstep behind the same barriers.
 // Consecutive workgroups take consecutive kv heads, so with 8 kv heads every tile of one head
 // runs on the same XCD and the tiles of a sequence share that XCD's L2.
+//
+// Built with -fno-honor-nans: no arithmetic here meets a NaN (cache slots past a sequence's end
+// may hold anything; their logits are replaced by -inf with integer selects and their values
+// cleared with bit masks before any arithmetic), so maxima compile to bare v_max3_f32.
 #include <type_traits>
 
 #include "prefill.hpp"
@@ -45,21 +49,6 @@ template <> struct PMfma<Dt::F16> {
   }
   static __device__ __forceinline__ _Float16 narrow(float x) { return (_Float16)x; }
   static constexpr uint32_t kOnePair = 0x3c003c00u;  // two f16 1.0
-};
-
-// Maxima of logits that are finite or -inf. fmaxf also quiets signalling NaNs, which costs
-// an extra instruction per operand; these are the bare instructions.
-__device__ __forceinline__ float max3_raw(float a, float b, float c) {
-  float d;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
-  return d;
-}
-struct OpMaxRaw {
-  __device__ __forceinline__ float operator()(float a, float b) const {
-    float d;
-    asm("v_max_f32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
-    return d;
-  }
 };
 
 // At most N vector memory operations of this wave outstanding (they complete in order).
@@ -269,8 +258,11 @@ prefill_kernel(const PrefillParams a) {
   // weights below 1. Only when a row's maximum passes the reference by more than that (in
   // practice the first chunk, and rarely later) does the wave move it and rescale the
   // accumulators. The result, acc / lsum, does not depend on the reference.
+  // A lane tests only its own eight logits of the row against the row's threshold thr[j] (a
+  // raw logit whose weight would be 2^kSlack); the row maximum, which needs the four lanes of
+  // the row, is formed only when some lane of the wave passes it.
   constexpr float kSlack = 8.0f;
-  float m[2] = {-INFINITY, -INFINITY};
+  float m[2] = {-INFINITY, -INFINITY}, thr[2] = {-INFINITY, -INFINITY};
   f32x4 acc[2][NT], lsum[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -314,17 +306,16 @@ prefill_kernel(const PrefillParams a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) sv[e] = e <= lim ? sv[e] : -INFINITY;
       }
-      float x = max3_raw(sv[0], sv[1], sv[2]);
-      x = max3_raw(x, sv[3], sv[4]);
-      x = max3_raw(x, sv[5], sv[6]);
-      x = OpMaxRaw()(x, sv[7]);
-      x = across16(x, OpMaxRaw());
-      x = across32(x, OpMaxRaw());
-      const float mx = x * cl;  // -inf when the chunk lies wholly past the row's limit
-      if (__builtin_amdgcn_ballot_w64(mx > m[j] + kSlack)) {
-        const float mnew = fmaxf(m[j], mx);  // finite: every row sees position 0 first
+      // -inf when the lane's positions lie past the row's limit
+      float x = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      if (__builtin_amdgcn_ballot_w64(x > thr[j])) {
+        x = across16(x, OpMax());
+        x = across32(x, OpMax());
+        const float mnew = fmaxf(m[j], x * cl);  // finite: every row sees position 0 first
         const float alpha = __builtin_amdgcn_exp2f(m[j] - mnew);
         m[j] = mnew;
+        thr[j] = (mnew + kSlack) / cl;  // +inf when cl = 0: every weight is then 2^-m
         lsum[j] *= alpha;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[j][nt] *= alpha;
