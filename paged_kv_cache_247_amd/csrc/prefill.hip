@@ -292,6 +292,9 @@ prefill_kernel(const PrefillParams a) {
         for (int nt = 0; nt < NT; ++nt) vr[nt][q] &= keep;
       }
     }
+    // Logits of both column tiles first, then one test for both: the part after it is one
+    // straight run (exp, P, the PV products) that the compiler can interleave across the tiles.
+    float sv[2][8];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -300,19 +303,31 @@ prefill_kernel(const PrefillParams a) {
         s0 = M::mac(__builtin_bit_cast(V8, kr[0][kk]), qb[j][kk], s0);
         s1 = M::mac(__builtin_bit_cast(V8, kr[1][kk]), qb[j][kk], s1);
       }
-      float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-      if (masked) {  // uniform: a branch, not a select on every chunk
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sv[j][e] = s0[e];
+        sv[j][4 + e] = s1[e];
+      }
+    }
+    if (masked) {  // uniform: a branch, not a select on every chunk
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
         const int lim = plim[j] - pos0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sv[e] = e <= lim ? sv[e] : -INFINITY;
+        for (int e = 0; e < 8; ++e) sv[j][e] = e <= lim ? sv[j][e] : -INFINITY;
       }
-      // -inf when the lane's positions lie past the row's limit
-      float x = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-      if (__builtin_amdgcn_ballot_w64(x > thr[j])) {
-        x = across16(x, OpMax());
-        x = across32(x, OpMax());
-        const float mnew = fmaxf(m[j], x * cl);  // finite: every row sees position 0 first
+    }
+    float x[2];  // -inf where the lane's positions lie past the row's limit
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      x[j] = fmaxf(fmaxf(fmaxf(sv[j][0], sv[j][1]), fmaxf(sv[j][2], sv[j][3])),
+                   fmaxf(fmaxf(sv[j][4], sv[j][5]), fmaxf(sv[j][6], sv[j][7])));
+    if (__builtin_amdgcn_ballot_w64(x[0] > thr[0] || x[1] > thr[1])) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float y = across16(x[j], OpMax());
+        y = across32(y, OpMax());
+        const float mnew = fmaxf(m[j], y * cl);  // finite: every row sees position 0 first
         const float alpha = __builtin_amdgcn_exp2f(m[j] - mnew);
         m[j] = mnew;
         thr[j] = (mnew + kSlack) / cl;  // +inf when cl = 0: every weight is then 2^-m
@@ -320,9 +335,13 @@ prefill_kernel(const PrefillParams a) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[j][nt] *= alpha;
       }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
       V8 pb;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = M::narrow(__builtin_amdgcn_exp2f(fmaf(sv[e], cl, -m[j])));
+      for (int e = 0; e < 8; ++e)
+        pb[e] = M::narrow(__builtin_amdgcn_exp2f(fmaf(sv[j][e], cl, -m[j])));
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         acc[j][nt] = M::mac(__builtin_bit_cast(V8, vr[nt]), pb, acc[j][nt]);
