@@ -13,7 +13,7 @@
 // 128 rows (token x head of the group, token-major), 32 per wave as two 16-column tiles of
 // v_mfma_f32_16x16x32_{bf16,f16}. Unlike decode, the query side is large, so every 32-position
 // KV chunk is staged in LDS once per workgroup (buffer loads straight into LDS, spread over the
-// waves, a ring of four stages with one barrier per chunk) and read by all four waves: for
+// waves, a ring of four stages, one barrier per two chunks) and read by all four waves: for
 // each column tile the logits S^T = K Q^T (rows positions, columns query rows; K rows permuted
 // as in decode so that a lane's accumulator holds eight consecutive positions of its own row),
 // the causal mask (only on chunks that reach a row's limit) and online softmax of the lane's
@@ -349,22 +349,20 @@ prefill_kernel(const PrefillParams a) {
     }
   };
 
-  // A ring of kStages stages, chunk n in stage n % kStages, loads running kStages - 1 chunks
-  // ahead, one barrier per chunk. At the top of iteration n this wave's loads of chunks up to
-  // n + kStages - 2 are issued; waiting until only those after chunk n remain, then the
-  // barrier, makes chunk n whole for every wave and tells that every wave is done with chunk
-  // n - 1, whose stage then takes chunk n + kStages - 1.
-  for (int k = 0; k < kStages - 1 && k < nch; ++k) issue(k, k);
-  for (int n = 0; n < nch; ++n) {
-    const int st = n % kStages;
-    switch (min(kStages - 2, nch - 1 - n)) {  // chunks issued after chunk n
-      case 0: wait_vm_le<0>(); break;
-      case 1: wait_vm_le<LPW>(); break;
-      default: wait_vm_le<2 * LPW>(); break;
-    }
+  // A ring of four stages, chunk n in stage n % 4, consumed two chunks per barrier. Before
+  // the barrier of step n (chunks n and n + 1) this wave waits for its own loads of them;
+  // after it, every wave's loads of them are in and every wave is done with chunks n - 2 and
+  // n - 1, whose stages then take chunks n + 2 and n + 3 (used one step later).
+  static_assert(kStages == 4, "two chunks per step, two steps of stages");
+  for (int k = 0; k < 2 && k < nch; ++k) issue(k, k);
+  for (int n = 0; n < nch; n += 2) {
+    wait_vm_le<0>();
     stage_barrier();
-    if (n + kStages - 1 < nch) issue(n + kStages - 1, (n + kStages - 1) % kStages);
-    if (wave_live && n * CT <= wave_last_limit) compute(n, st, n * CT + CT - 1 > wave_first_limit);
+    for (int k = n + 2; k < n + 4 && k < nch; ++k) issue(k, k % kStages);
+#pragma unroll 1
+    for (int k = n; k < n + 2 && k < nch; ++k)
+      if (wave_live && k * CT <= wave_last_limit)
+        compute(k, k % kStages, k * CT + CT - 1 > wave_first_limit);
   }
 
   // Lane (r, c) holds O^T[16 nt + 4 r + e][row c] of each column tile, and the row's whole
