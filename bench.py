@@ -70,6 +70,9 @@ def parse():
                     help="repetitions of back-to-back launch timing per kernel")
     ap.add_argument("--launches", type=int, default=100,
                     help="back-to-back launches per repetition")
+    ap.add_argument("--shard", default=None, metavar="KIND:N",
+                    help="run one GPU's share of an N-GPU job at its real shape: kv:N keeps "
+                         "1/N of the kv heads (and their q heads), seq:N 1/N of the sequences")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     return ap.parse_args()
@@ -322,6 +325,22 @@ def main():
     kernel = args.kernel or kernel
     P = P if args.partition_size is None else args.partition_size
     cfg = W.CONFIGS[name]
+    shard = None
+    if args.shard:
+        kind, _, n = args.shard.partition(":")
+        n = int(n)
+        if kind == "kv" and n >= 1 and cfg.num_kv_heads % n == 0:
+            cfg = cfg.replace(num_heads=cfg.num_heads // n, num_kv_heads=cfg.num_kv_heads // n)
+        elif kind == "seq" and n >= 1 and cfg.num_seqs % n == 0:
+            cfg = cfg.replace(num_seqs=cfg.num_seqs // n)
+        else:
+            print(f"--shard {args.shard}: expected kv:N (N dividing {cfg.num_kv_heads}) or "
+                  f"seq:N (N dividing {cfg.num_seqs})", file=sys.stderr)
+            sys.exit(2)
+        shard = {"kind": kind, "of_gpus": n}
+        cfg = cfg.replace(description=f"{cfg.description}; one GPU's share of {args.shard} "
+                                      f"({cfg.num_seqs} seqs, {cfg.num_heads}/"
+                                      f"{cfg.num_kv_heads} heads)")
     t0 = time.time()
     wl = W.generate(cfg, poison="zero")
     print(f"[bench] generated {name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -428,7 +447,7 @@ def main():
     kvb = wl.kv_bytes()
     family = "mfma" if (kernel == "mfma" or (kernel == "auto" and cfg.dtype != "f32"
                                              and cfg.group >= 4)) else "valu"
-    traffic = counter_traffic(KERNEL_SOURCES[family], name)
+    traffic = None if shard else counter_traffic(KERNEL_SOURCES[family], name)
     value = kvb / (ms_step * 1e-3) / 1e9
     ukvb = wl.unique_kv_bytes() if has_copy else kvb
     # With shared prefix blocks the logical bytes count the prefix once per sequence, but it is
@@ -454,7 +473,7 @@ def main():
                    "context_tokens": wl.total_tokens, "max_context_len": maxlen,
                    "kernel": kernel, "partition_size": P, "cached_kv": cached,
                    "fused_cache_write": fused, "kv_bytes": kvb,
-                   "unique_kv_bytes": ukvb},
+                   "unique_kv_bytes": ukvb, "shard": shard},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "attended_tokens_per_s": round(wl.total_tokens / (ms_step * 1e-3), 1),
         "head_token_pairs_per_s": round(cfg.num_heads * wl.total_tokens / (ms_step * 1e-3), 1),
