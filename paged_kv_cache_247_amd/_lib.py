@@ -524,9 +524,16 @@ def swap_blocks(src_k, src_v, dst_k, dst_v, pairs, to_device: bool):
     like the device pools."""
     import numpy as np
     dev = dst_k if to_device else src_k
+    if len({t.dtype for t in (src_k, src_v, dst_k, dst_v)}) != 1:
+        raise TypeError("the pools must share one dtype")
     for t, nm in ((src_k, "src_k"), (src_v, "src_v"), (dst_k, "dst_k"), (dst_v, "dst_v")):
         if not t.is_contiguous():
             raise ValueError(f"{nm} must be contiguous")
+        on_device = nm.startswith("dst") == bool(to_device)
+        if on_device and not t.is_cuda:
+            raise ValueError(f"{nm} is the device pool: it must be on the GPU")
+        if not on_device and (t.is_cuda or not t.is_pinned()):
+            raise ValueError(f"{nm} is the host pool: it must be pinned CPU memory")
     if src_k.shape[1:] != dst_k.shape[1:] or src_v.shape[1:] != dst_v.shape[1:]:
         raise ValueError("pools of different block shapes")
     pairs = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)

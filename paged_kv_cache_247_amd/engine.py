@@ -8,6 +8,11 @@ when the pool runs short (item 1-3: blocks are taken and returned as needed). Re
 share a prefix share its blocks and get private copies of a shared block when they write into
 it (Hacker News discussion of PagedAttention).
 
+With prefill_chunk > 0 prompts are not written whole at admission: each step a prompting
+sequence takes its next chunk of up to prefill_chunk prompt tokens (their K/V written, then one
+paged prefill launch gives every chunk token's attention output over the sequence so far) while
+the other sequences decode, so long prompts do not stall the batch.
+
 There is no model: the query, key and value vectors of position p of request r are seeded
 draws (N(0,1) rounded to the cache type), so that every step's attention can be checked
 against a plain reference over each sequence's history. Each step is: swap-ins, admissions
@@ -37,31 +42,40 @@ class Request:
     generated: int = 0
     origin: int = -1      # request whose stream this one continues (forks), -1 = its own
     fork_pos: int = 0     # positions inherited from origin
+    prefilled: int = 0    # prompt positions in the cache (chunked prefill)
 
 
 class DecodeEngine:
     def __init__(self, num_blocks: int, num_host_blocks: int, num_heads: int, num_kv_heads: int,
                  head_dim: int, block_size: int, max_blocks_per_seq: int, dtype: str = "bf16",
-                 seed: int = 0):
+                 seed: int = 0, prefill_chunk: int = 0, device="cuda", ops=None):
+        """ops: the kernel entry points (reshape_and_cache, copy_blocks, swap_blocks,
+        paged_attention, paged_attention_prefill); the HIP library by default. The block
+        manager is always the library's."""
         self.H, self.Hkv, self.D, self.S = num_heads, num_kv_heads, head_dim, block_size
         self.MB, self.dtype, self.seed = max_blocks_per_seq, dtype, seed
+        self.chunk = prefill_chunk
+        self.scale = 1.0 / float(np.sqrt(head_dim))
+        self.ops = ops if ops is not None else L
+        self.device = torch.device(device)
         self.bm = L.BlockManager(num_blocks, num_host_blocks, block_size)
         tdt = _TORCH[dtype]
         self.k = torch.zeros((num_blocks, num_kv_heads, block_size, head_dim), dtype=tdt,
-                             device="cuda")
+                             device=self.device)
         self.v = torch.zeros((num_blocks, num_kv_heads, head_dim, block_size), dtype=tdt,
-                             device="cuda")
+                             device=self.device)
+        pin = self.device.type == "cuda"
         self.hk = torch.zeros((max(num_host_blocks, 1), num_kv_heads, block_size, head_dim),
-                              dtype=tdt, pin_memory=True)
+                              dtype=tdt, pin_memory=pin)
         self.hv = torch.zeros((max(num_host_blocks, 1), num_kv_heads, head_dim, block_size),
-                              dtype=tdt, pin_memory=True)
+                              dtype=tdt, pin_memory=pin)
         self.requests: dict[int, Request] = {}
         self.waiting: deque[int] = deque()
         self.running: list[int] = []
         self.swapped: deque[int] = deque()
         self.finished: list[int] = []
         self.stats = {"steps": 0, "swap_outs": 0, "swap_ins": 0, "cow_copies": 0,
-                      "admitted": 0}
+                      "admitted": 0, "prefill_chunks": 0, "short_chunks": 0}
 
     # ------------------------------------------------------------ synthetic tokens
     def _stream_owner(self, rid: int, pos: int) -> int:
@@ -82,8 +96,8 @@ class DecodeEngine:
     def _dev(self, a: np.ndarray) -> torch.Tensor:
         a = np.ascontiguousarray(a)
         if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(a).cuda()
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(self.device)
+        return torch.from_numpy(a).to(self.device)
 
     # ------------------------------------------------------------ requests
     def submit(self, rid: int, prompt_len: int, new_tokens: int):
@@ -97,7 +111,10 @@ class DecodeEngine:
             raise ValueError("only a running request can be forked")
         n = self.bm.num_tokens(parent)
         self.bm.fork(parent, child)
-        self.requests[child] = Request(child, n, new_tokens, origin=parent, fork_pos=n)
+        if self.requests[parent].prefilled < self.requests[parent].prompt_len:
+            raise ValueError("a request still reading its prompt cannot be forked")
+        self.requests[child] = Request(child, n, new_tokens, origin=parent, fork_pos=n,
+                                       prefilled=n)
         self.running.append(child)
 
     # ------------------------------------------------------------ one iteration
@@ -111,24 +128,29 @@ class DecodeEngine:
         toks = [self.token(rid, int(p)) for p in pos]
         ks = np.stack([k for _, k, _ in toks])
         vs = np.stack([v for _, _, v in toks])
-        L.reshape_and_cache(self._dev(ks), self._dev(vs), self.k, self.v, self._dev(slots))
+        self.ops.reshape_and_cache(self._dev(ks), self._dev(vs), self.k, self.v, self._dev(slots))
 
     def _swap_out(self, rid: int):
         pairs = self.bm.swap_out(rid)
-        L.swap_blocks(self.k, self.v, self.hk, self.hv, pairs, to_device=False)
+        self.ops.swap_blocks(self.k, self.v, self.hk, self.hv, pairs, to_device=False)
         self.running.remove(rid)
         self.swapped.appendleft(rid)
         self.stats["swap_outs"] += 1
 
     def _swap_in(self, rid: int):
         pairs = self.bm.swap_in(rid)
-        L.swap_blocks(self.hk, self.hv, self.k, self.v, pairs, to_device=True)
+        self.ops.swap_blocks(self.hk, self.hv, self.k, self.v, pairs, to_device=True)
         self.running.append(rid)
         self.stats["swap_ins"] += 1
 
+    def _prompting(self, rid: int) -> bool:
+        r = self.requests[rid]
+        return self.chunk > 0 and r.prefilled < r.prompt_len
+
     def step(self):
-        """One iteration. Returns ({rid: (row of out, position decoded)}, out [B, H, D]) for
-        the sequences decoded this step (out is None when none ran)."""
+        """One iteration. Returns a dict: "decode" {rid: (row of decode_out, position)} with
+        "decode_out" [B, H, D], and "prefill" {rid: (first row of prefill_out, first position,
+        tokens)} with "prefill_out" [T, H, D] (outputs are None when nothing of that kind ran)."""
         # 1. swapped-out requests first (oldest preempted first), then new ones, while they fit
         while self.swapped:
             rid = self.swapped[0]
@@ -139,57 +161,97 @@ class DecodeEngine:
             self._swap_in(rid)
         while self.waiting and not self.swapped:
             rid = self.waiting[0]
-            need = -(-self.requests[rid].prompt_len // self.S) + 1
-            if self.bm.free_blocks < need:
+            P = self.requests[rid].prompt_len
+            first = min(self.chunk, P) if self.chunk else P
+            if self.bm.free_blocks < -(-first // self.S) + 1:
                 break
             self.waiting.popleft()
-            self.bm.add(rid, self.requests[rid].prompt_len)
-            self._write_prompt(rid)
+            if self.chunk:
+                self.bm.add(rid, 0)
+            else:
+                self.bm.add(rid, P)
+                self._write_prompt(rid)
+                self.requests[rid].prefilled = P
             self.running.append(rid)
             self.stats["admitted"] += 1
-        # 2. one slot per running sequence, in admission order. When blocks run out, the
-        # youngest sequence that has not taken its slot yet is swapped out (possibly the one
-        # asking), and the append is tried again.
-        copies, order, i = [], list(self.running), 0
+        # 2. slots, in admission order: the next prompt chunk of a prompting sequence, one
+        # token of a decoding one. When blocks run out, the youngest sequence that has not
+        # taken its slots yet is swapped out (possibly the one asking) and the append is tried
+        # again; a prompt chunk that got some of its slots is cut short instead.
+        copies, order, i, take = [], list(self.running), 0, {}
         while i < len(order):
             rid = order[i]
+            want = (min(self.chunk, self.requests[rid].prompt_len - self.requests[rid].prefilled)
+                    if self._prompting(rid) else 1)
+            got = 0
             try:
-                _, cow = self.bm.append(rid)
+                while got < want:
+                    _, cow = self.bm.append(rid)
+                    got += 1
+                    if cow is not None:
+                        copies.append(cow)
             except L.OutOfBlocks:
-                if len(order) == 1:
-                    raise
-                self._swap_out(order.pop())
-                continue
-            if cow is not None:
-                copies.append(cow)
+                if got == 0:
+                    if len(order) == 1:
+                        raise
+                    self._swap_out(order.pop())
+                    continue
+                self.stats["short_chunks"] += 1
+            take[rid] = got
             i += 1
         if copies:
-            L.copy_blocks([self.k], [self.v], self._dev(np.asarray(copies, dtype=np.int64)))
+            self.ops.copy_blocks([self.k], [self.v], self._dev(np.asarray(copies, dtype=np.int64)))
             self.stats["cow_copies"] += len(copies)
-        # 3. decode every running sequence, writing its newest K/V
-        seqs = order
-        if not seqs:
-            self.stats["steps"] += 1
-            return {}, None
-        t, lens = self.bm.tables(seqs, self.MB)
-        q = np.stack([self.token(r, int(n) - 1)[0] for r, n in zip(seqs, lens)])
-        kn = np.stack([self.token(r, int(n) - 1)[1] for r, n in zip(seqs, lens)])
-        vn = np.stack([self.token(r, int(n) - 1)[2] for r, n in zip(seqs, lens)])
-        out = torch.empty((len(seqs), self.H, self.D), dtype=_TORCH[self.dtype], device="cuda")
-        L.paged_attention(out, self._dev(q), self.k, self.v, self._dev(t), self._dev(lens),
-                          int(lens.max()), 1.0 / float(np.sqrt(self.D)), 0,
-                          new_key=self._dev(kn), new_value=self._dev(vn))
-        # 4. finish
-        result = {r: (k, int(n) - 1) for k, (r, n) in enumerate(zip(seqs, lens))}
-        for r in seqs:
-            req = self.requests[r]
-            req.generated += 1
-            if req.generated >= req.new_tokens:
-                self.bm.free(r)
-                self.running.remove(r)
-                self.finished.append(r)
+        res = {"decode": {}, "decode_out": None, "prefill": {}, "prefill_out": None}
+        pre = [r for r in order if self._prompting(r)]
+        dec = [r for r in order if not self._prompting(r)]
+        # 3. prompt chunks: their K/V into the cache, then causal attention of each chunk token
+        # over its sequence so far
+        if pre:
+            t, lens = self.bm.tables(pre, self.MB)
+            rows, slots, qs = [], [], [0]
+            for r, tab, n in zip(pre, t, lens):
+                p0 = self.requests[r].prefilled
+                for p in range(p0, int(n)):
+                    rows.append(self.token(r, p))
+                    slots.append(int(tab[p // self.S]) * self.S + p % self.S)
+                res["prefill"][r] = (qs[-1], p0, int(n) - p0)
+                qs.append(qs[-1] + int(n) - p0)
+            q = np.stack([x[0] for x in rows])
+            self.ops.reshape_and_cache(self._dev(np.stack([x[1] for x in rows])),
+                                self._dev(np.stack([x[2] for x in rows])), self.k, self.v,
+                                self._dev(np.asarray(slots, dtype=np.int64)))
+            out = torch.empty((len(rows), self.H, self.D), dtype=_TORCH[self.dtype],
+                              device=self.device)
+            self.ops.paged_attention_prefill(out, self._dev(q), self.k, self.v, self._dev(t),
+                                      self._dev(lens), self._dev(np.asarray(qs, np.int32)),
+                                      int(np.diff(qs).max()), self.scale)
+            res["prefill_out"] = out
+            for r, n in zip(pre, lens):
+                self.requests[r].prefilled = int(n)
+            self.stats["prefill_chunks"] += len(pre)
+        # 4. decode every other running sequence, writing its newest K/V
+        if dec:
+            t, lens = self.bm.tables(dec, self.MB)
+            toks = [self.token(r, int(n) - 1) for r, n in zip(dec, lens)]
+            out = torch.empty((len(dec), self.H, self.D), dtype=_TORCH[self.dtype],
+                              device=self.device)
+            self.ops.paged_attention(out, self._dev(np.stack([x[0] for x in toks])), self.k, self.v,
+                              self._dev(t), self._dev(lens), int(lens.max()), self.scale, 0,
+                              new_key=self._dev(np.stack([x[1] for x in toks])),
+                              new_value=self._dev(np.stack([x[2] for x in toks])))
+            res["decode"] = {r: (k, int(n) - 1) for k, (r, n) in enumerate(zip(dec, lens))}
+            res["decode_out"] = out
+            # 5. finish
+            for r in dec:
+                req = self.requests[r]
+                req.generated += 1
+                if req.generated >= req.new_tokens:
+                    self.bm.free(r)
+                    self.running.remove(r)
+                    self.finished.append(r)
         self.stats["steps"] += 1
-        return result, out
+        return res
 
     def done(self) -> bool:
         return not (self.waiting or self.running or self.swapped)

@@ -182,3 +182,16 @@ def test_random_operations_keep_the_books_straight():
         assert bm.free_blocks == int((holders == 0).sum())
         host_used = sum(-(-bm.num_tokens(s) // S) for s in swapped)
         assert bm.free_host_blocks == NH - host_used
+
+
+def test_swap_blocks_checks_where_the_pools_live():
+    """Host pools are pinned CPU memory and device pools GPU memory; anything else is refused
+    before a copy is queued (this container has no GPU, so every call here is refused)."""
+    import torch
+    k = torch.zeros((4, 2, S, 8), dtype=torch.bfloat16)
+    v = torch.zeros((4, 2, 8, S), dtype=torch.bfloat16)
+    for to_device in (True, False):
+        with pytest.raises(ValueError, match="pool"):
+            pk.swap_blocks(k, v, k.clone(), v.clone(), [[0, 1]], to_device=to_device)
+    with pytest.raises(TypeError, match="dtype"):
+        pk.swap_blocks(k, v.float(), k.clone(), v.clone(), [[0, 1]], to_device=True)
