@@ -137,8 +137,9 @@ pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, 
   const int64_t units = work_items ? (int64_t)num_work_items : (int64_t)num_seqs * ranges;
   if ((int64_t)num_seqs * ranges > INT32_MAX)
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: %lld units", fn, (long long)num_seqs * ranges);
-  const int64_t grid = units * num_kv_heads;
-  if (grid > INT32_MAX) return fail(PKV_ERR_INVALID_ARGUMENT, "%s: grid of %lld workgroups", fn, (long long)grid);
+  const int64_t grid = units * num_kv_heads;  // the MFMA kernel pads units to a multiple of 8
+  if ((units + 7) / 8 * 8 * num_kv_heads > INT32_MAX)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: grid of %lld workgroups", fn, (long long)grid);
   if (grid == 0) return PKV_OK;
 
   pkv::DecodeParams p;

@@ -63,6 +63,7 @@ __device__ __forceinline__ void wait_vm_le() {
 
 // Dword 3 of a raw buffer descriptor on gfx9-family chips: 32-bit data format, no swizzle,
 // no index stride.
+constexpr int kXcds = 8;  // XCDs of the MI355X, which take workgroups round robin
 constexpr int kBufferFlags = 0x00020000;
 
 template <Dt DT, int D, int S, int NW, bool PARTIAL, bool NTL, bool TBL>
@@ -101,9 +102,21 @@ decode_mfma_kernel(const DecodeParams a) {
   const int H = a.num_heads;
   const int G = H / Hkv;
   const int MB = a.max_blocks_per_seq;
+  // Workgroups go to the XCDs round robin (w % 8). Unshared KV: every kv head of a unit on one
+  // XCD (groups of 8 Hkv workgroups hold 8 units, head g of the group's unit j at 8 g + j), so
+  // an XCD streams whole blocks of its sequences. Shared prefix blocks (cached loads): head g of
+  // every unit on XCD g % 8, so a shared block's head tile stays in one XCD's L2.
   const int w = blockIdx.x;
-  const int g = w % Hkv;  // consecutive workgroups take different kv heads (XCD round robin)
-  const int slot = w / Hkv;
+  int g, slot;
+  if constexpr (NTL) {
+    constexpr int XC = kXcds;
+    g = (w % (XC * Hkv)) / XC;
+    slot = (w / (XC * Hkv)) * XC + w % XC;
+    if (slot >= a.num_units) return;  // the grid is padded to whole groups of 8 units
+  } else {
+    g = w % Hkv;
+    slot = w / Hkv;
+  }
   int unit = a.work_items ? a.work_items[slot] : slot;
   unit = min(max(unit, 0), a.num_seqs * a.num_ranges - 1);
   const int part = unit % a.num_ranges;
@@ -481,7 +494,8 @@ constexpr int kMfmaWaves = 4;
 
 template <Dt DT, int D, int S, bool PARTIAL, bool NTL>
 hipError_t launch_p(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)p.num_units * p.num_kv_heads);
+  const unsigned units = NTL ? (p.num_units + kXcds - 1) / kXcds * kXcds : p.num_units;
+  const dim3 grid(units * (unsigned)p.num_kv_heads);
   const dim3 block(kMfmaWaves * 64);
   if (p.block_tables)
     decode_mfma_kernel<DT, D, S, kMfmaWaves, PARTIAL, NTL, true><<<grid, block, 0, stream>>>(p);
