@@ -100,6 +100,9 @@ CASES = [
     ("c5", {"dtype": "f16", "head_dim": 64}, "auto", (64, 0)),
     ("c5", {"dtype": "f32"}, "auto", (64, 0)),
     ("c5", {"num_heads": 4}, "auto", (0, 64)),  # group 2, block 32
+    ("c3", {"num_heads": 4, "num_kv_heads": 1}, "auto", (0, 64)),  # one kv head (a kv:8 share)
+    ("c5", {"num_heads": 8, "num_kv_heads": 1}, "auto", (64, 0)),  # one kv head, group 8
+    ("c3", {"num_seqs": 9}, "auto", (0,)),  # units spill into a second group of 8
 ]
 
 
