@@ -50,6 +50,13 @@ void release_device(pkv_block_manager* bm, int32_t b) {
   if (--bm->ref[(size_t)b] == 0) bm->free_dev.push_back(b);
 }
 
+// Host allocations (the sequence map, block lists) happen before any change to the books, so
+// running out of host memory leaves them as they were; no exception leaves the C ABI. The free
+// lists never grow past their size at creation, so returning blocks allocates nothing.
+pkv_status out_of_memory(const char* fn) {
+  return fail(PKV_ERR_INVALID_ARGUMENT, "%s: out of host memory", fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -62,11 +69,16 @@ pkv_status pkv_bm_create(int32_t num_blocks, int32_t num_host_blocks, int32_t bl
     return fail(PKV_ERR_INVALID_ARGUMENT, "pkv_bm_create: num_blocks %d num_host_blocks %d block_size %d",
                 num_blocks, num_host_blocks, block_size);
   pkv_block_manager* bm = new (std::nothrow) pkv_block_manager;
-  if (!bm) return fail(PKV_ERR_INVALID_ARGUMENT, "pkv_bm_create: out of host memory");
-  bm->block_size = block_size;
-  bm->ref.assign((size_t)num_blocks, 0);
-  bm->free_dev = id_stack(num_blocks);
-  bm->free_host = id_stack(num_host_blocks);
+  if (!bm) return out_of_memory("pkv_bm_create");
+  try {
+    bm->block_size = block_size;
+    bm->ref.assign((size_t)num_blocks, 0);
+    bm->free_dev = id_stack(num_blocks);
+    bm->free_host = id_stack(num_host_blocks);
+  } catch (const std::bad_alloc&) {
+    delete bm;
+    return out_of_memory("pkv_bm_create");
+  }
   *out = bm;
   return PKV_OK;
 }
@@ -88,15 +100,21 @@ pkv_status pkv_bm_add(pkv_block_manager* bm, int64_t seq, int32_t num_tokens) {
   const size_t nb = ((size_t)num_tokens + bm->block_size - 1) / bm->block_size;
   if (nb > bm->free_dev.size())
     return fail(PKV_ERR_NO_BLOCKS, "pkv_bm_add: %zu blocks needed, %zu free", nb, bm->free_dev.size());
-  Seq s;
-  s.tokens = num_tokens;
+  Seq* s;
+  try {
+    s = &bm->seqs.emplace(seq, Seq{}).first->second;
+    s->blocks.reserve(nb);
+  } catch (const std::bad_alloc&) {
+    bm->seqs.erase(seq);
+    return out_of_memory("pkv_bm_add");
+  }
+  s->tokens = num_tokens;
   for (size_t k = 0; k < nb; ++k) {
     const int32_t b = bm->free_dev.back();
     bm->free_dev.pop_back();
     bm->ref[(size_t)b] = 1;
-    s.blocks.push_back(b);
+    s->blocks.push_back(b);
   }
-  bm->seqs.emplace(seq, std::move(s));
   return PKV_OK;
 }
 
@@ -106,9 +124,14 @@ pkv_status pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child) {
   if (!p || p->on_host)
     return fail(PKV_ERR_INVALID_ARGUMENT, "pkv_bm_fork: parent %lld unknown or swapped out", (long long)parent);
   if (find(bm, child)) return fail(PKV_ERR_INVALID_ARGUMENT, "pkv_bm_fork: child %lld exists", (long long)child);
-  Seq c = *p;
-  for (int32_t b : c.blocks) ++bm->ref[(size_t)b];
-  bm->seqs.emplace(child, std::move(c));
+  try {
+    Seq c = *p;
+    p = nullptr;  // the map may rehash below
+    const Seq& k = bm->seqs.emplace(child, std::move(c)).first->second;
+    for (int32_t b : k.blocks) ++bm->ref[(size_t)b];
+  } catch (const std::bad_alloc&) {
+    return out_of_memory("pkv_bm_fork");
+  }
   return PKV_OK;
 }
 
@@ -122,6 +145,11 @@ pkv_status pkv_bm_append(pkv_block_manager* bm, int64_t seq, int64_t* slot, int3
   *copy_src = *copy_dst = -1;
   const int32_t S = bm->block_size;
   const int32_t pos = s->tokens;
+  try {
+    s->blocks.reserve(s->blocks.size() + 1);
+  } catch (const std::bad_alloc&) {
+    return out_of_memory("pkv_bm_append");
+  }
   if (pos % S == 0) {  // the token opens a new block
     if (bm->free_dev.empty()) return fail(PKV_ERR_NO_BLOCKS, "pkv_bm_append: no free block");
     const int32_t b = bm->free_dev.back();

@@ -81,6 +81,11 @@ pkv_status add_pages(pkv_vmm_pool* p, int kv, int32_t seq, size_t want) {
   access.location.type = hipMemLocationTypeDevice;
   access.location.id = p->device;
   access.flags = hipMemAccessFlagsProtReadWrite;
+  try {
+    v.reserve(want);  // the only host allocation here, before any page exists
+  } catch (const std::bad_alloc&) {
+    return fail(PKV_ERR_INVALID_ARGUMENT, "pkv_vmm_pool_map: out of host memory");
+  }
   while (v.size() < want) {
     hipMemGenericAllocationHandle_t h;
     hipError_t e = hipMemCreate(&h, p->page_bytes, &prop, 0);
@@ -147,7 +152,12 @@ pkv_status pkv_vmm_pool_create(int32_t num_seqs, int32_t max_context_len, int32_
   p->block_bytes = block_bytes;
   p->page_bytes = page;
   p->seq_bytes = mb * block_bytes;
-  for (int kv = 0; kv < 2; ++kv) p->pages[kv].assign(num_seqs, {});
+  try {
+    for (int kv = 0; kv < 2; ++kv) p->pages[kv].assign(num_seqs, {});
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: out of host memory", fn);
+  }
   const size_t total = p->seq_bytes * (size_t)num_seqs;
   for (int kv = 0; kv < 2; ++kv) {
     e = hipMemAddressReserve(&p->base[kv], total, page, nullptr, 0);

@@ -101,6 +101,10 @@ class DecodeEngine:
 
     # ------------------------------------------------------------ requests
     def submit(self, rid: int, prompt_len: int, new_tokens: int):
+        if rid in self.requests:
+            raise ValueError(f"request id {rid} is taken")
+        if prompt_len < 0 or new_tokens < 1:
+            raise ValueError("prompt_len >= 0 and new_tokens >= 1")
         self.requests[rid] = Request(rid, prompt_len, new_tokens)
         self.waiting.append(rid)
 
@@ -109,10 +113,14 @@ class DecodeEngine:
         start at the parent's current length."""
         if parent not in self.running:
             raise ValueError("only a running request can be forked")
-        n = self.bm.num_tokens(parent)
-        self.bm.fork(parent, child)
         if self.requests[parent].prefilled < self.requests[parent].prompt_len:
             raise ValueError("a request still reading its prompt cannot be forked")
+        if child in self.requests:
+            raise ValueError(f"request id {child} is taken")
+        if new_tokens < 1:
+            raise ValueError("new_tokens >= 1")
+        n = self.bm.num_tokens(parent)
+        self.bm.fork(parent, child)
         self.requests[child] = Request(child, n, new_tokens, origin=parent, fork_pos=n,
                                        prefilled=n)
         self.running.append(child)

@@ -130,3 +130,23 @@ def test_loop_keeps_every_sequence_consistent(block_size, num_blocks, chunk):
 def test_prompt_chunks_cut_short_when_blocks_run_out():
     st = run_loop(16, 12, 64, [70, 66, 60, 50, 2, 3], 3)
     assert st["short_chunks"] > 0 and st["swap_outs"] > 0
+
+
+def test_bad_requests_are_refused_without_side_effects():
+    eng = DecodeEngine(num_blocks=8, num_host_blocks=4, num_heads=4, num_kv_heads=2,
+                       head_dim=32, block_size=16, max_blocks_per_seq=4, prefill_chunk=8,
+                       device="cpu", ops=OracleOps)
+    eng.submit(1, 20, 3)
+    for bad in (lambda: eng.submit(1, 5, 2), lambda: eng.submit(2, -1, 2),
+                lambda: eng.submit(3, 4, 0)):
+        with pytest.raises(ValueError):
+            bad()
+    eng.step()  # request 1 is admitted and reads the first 8 of its 20 prompt positions
+    with pytest.raises(ValueError, match="prompt"):
+        eng.fork(1, 9, 4)
+    with pytest.raises(ValueError, match="running"):
+        eng.fork(7, 9, 4)
+    assert eng.bm.num_tokens(9) == -1 and eng.bm.ref_count(0) <= 1
+    while not eng.done():
+        eng.step()
+    assert eng.bm.free_blocks == 8
