@@ -312,7 +312,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the "
-              "decode path is single-GPU, see DESIGN.md for how it would shard)", file=sys.stderr)
+              "path runs on one GPU; --shard runs one GPU's share of a larger job)", file=sys.stderr)
         sys.exit(2)
     if args.config in ("p1", "p2"):
         prefill_main(args)
