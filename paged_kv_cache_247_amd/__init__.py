@@ -4,13 +4,13 @@ Hand-written HIP kernels behind the C ABI in include/pagedkv.h (libpagedkv.so), 
 ctypes binding. The seeded workload generators live in `workload`.
 """
 from ._lib import (KERNELS, BlockManager, DeviceRegion, OutOfBlocks, PagedKVError, VmmPool,
-                   copy_blocks, load, swap_blocks,
+                   auto_partition_size, copy_blocks, load, swap_blocks,
                    num_partitions, paged_attention, paged_attention_decode,
                    paged_attention_prefill, paged_attention_reduce, partition_workspace,
                    prefill_tile_tokens, reshape_and_cache)
 
 __all__ = ["KERNELS", "BlockManager", "DeviceRegion", "OutOfBlocks", "PagedKVError", "VmmPool",
-           "copy_blocks", "load", "swap_blocks",
+           "auto_partition_size", "copy_blocks", "load", "swap_blocks",
            "num_partitions", "paged_attention", "paged_attention_decode",
            "paged_attention_prefill", "paged_attention_reduce", "partition_workspace",
            "prefill_tile_tokens", "reshape_and_cache"]

@@ -357,10 +357,33 @@ def copy_blocks(k_caches, v_caches, block_mapping):
                                   Hkv, D, S, N, _dt(k0), _stream(k0)))
 
 
+AUTO_PARTITION_TOKENS = 2048
+
+
+def auto_partition_size(num_seqs: int, num_kv_heads: int, block_size: int,
+                        device=None, num_cus: int | None = None) -> int:
+    """Host policy for split-context decode: single pass (0) when the (sequence, kv head) units
+    fill two rounds of the GPU's workgroup slots (two per CU), else 2048-token partitions, so
+    that a few long sequences do not leave most CUs idle behind them. Measured on the GQA shape
+    at equal total tokens: 128 sequences single pass 188 us; 64 sequences 195.5 -> 190.3 us and
+    32 sequences 218.7 -> 187.3 us with 2048-token partitions (merge included)."""
+    if num_cus is None:
+        num_cus = torch.cuda.get_device_properties(device if device is not None else
+                                                   torch.cuda.current_device()).multi_processor_count
+    if num_seqs * num_kv_heads >= 4 * num_cus:
+        return 0
+    return max(block_size, AUTO_PARTITION_TOKENS // block_size * block_size)
+
+
 def paged_attention(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
                     scale, partition_size=0, workspace=None, kernel="auto", work_items=None,
                     cached_kv=False, new_key=None, new_value=None, max_blocks_per_seq=None):
-    """The whole decode: single pass, or partitions then their merge, on the current stream."""
+    """The whole decode: single pass, or partitions then their merge, on the current stream.
+    partition_size="auto" applies auto_partition_size (a work list, if given, must have been
+    built for the size it picks)."""
+    if partition_size == "auto":
+        partition_size = auto_partition_size(q.shape[0], k_cache.shape[1], k_cache.shape[2],
+                                             q.device)
     kw = dict(kernel=kernel, work_items=work_items, cached_kv=cached_kv, new_key=new_key,
               new_value=new_value, max_blocks_per_seq=max_blocks_per_seq)
     if partition_size:

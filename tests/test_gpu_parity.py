@@ -352,3 +352,23 @@ def test_full_size_sampled_against_oracle(name):
     ref = oracle_out(wl, seqs)
     err = oracle.max_abs_err(out[seqs], ref)
     assert err <= TOL[cfg.dtype], f"{name}: {err}"
+
+
+def test_auto_partition_size_matches_oracle():
+    """partition_size="auto" on a batch of few long sequences picks split-context partitions
+    and still matches the oracle; on many sequences it stays single pass."""
+    cfg = W.SMALL["c5"]
+    wl = W.generate(cfg)
+    dt = cfg.dtype
+    P = pk.auto_partition_size(cfg.num_seqs, cfg.num_kv_heads, cfg.block_size)
+    assert P > 0 and P % cfg.block_size == 0
+    d = upload(wl)
+    if len(wl.block_mapping):
+        pk.copy_blocks([d.k], [d.v], d.mapping)
+    pk.reshape_and_cache(d.key, d.value, d.k, d.v, d.slots)
+    out = torch.full((cfg.num_seqs, cfg.num_heads, cfg.head_dim), float("nan"),
+                     dtype=TORCH_DT[dt], device="cuda")
+    pk.paged_attention(out, d.q, d.k, d.v, d.bt, d.lens, wl.max_context_len, cfg.scale, "auto")
+    torch.cuda.synchronize()
+    assert oracle.max_abs_err(out_f64(out), oracle_out(wl)) <= TOL[dt]
+    assert pk.auto_partition_size(4096, 8, 16) == 0
