@@ -3,8 +3,9 @@
     python -m paged_kv_cache_247_amd.build [--jobs N] [--verbose]
 
 Every source is compiled to an object under paged_kv_cache_247_amd/_build/ and the objects are
-linked into paged_kv_cache_247_amd/libpagedkv.so. Packed-fp32 instruction selection is switched
-off for all device code (-packed-fp32-ops).
+linked into paged_kv_cache_247_amd/libpagedkv.so; the two decode sources are compiled once per
+block size (-DPKV_BLOCK_SIZE=S), so the objects build in parallel. Packed-fp32 instruction
+selection is switched off for all device code (-packed-fp32-ops).
 """
 from __future__ import annotations
 
@@ -21,8 +22,14 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
-SOURCES = ["api.cpp", "vmm.cpp", "block_manager.cpp", "cache_ops.hip", "decode_valu.hip", "decode_mfma.hip",
+BLOCK_SIZES = (16, 32, 64, 128, 256)
+PER_BLOCK_SIZE = ("decode_valu.hip", "decode_mfma.hip")
+SOURCES = ["api.cpp", "vmm.cpp", "block_manager.cpp", "cache_ops.hip", *PER_BLOCK_SIZE,
            "reduce.hip", "prefill.hip"]
+# (source, object stem, defines): one unit of parallel compilation each
+UNITS = [(src, f"{os.path.splitext(src)[0]}_s{S}", [f"-DPKV_BLOCK_SIZE={S}"])
+         for src in PER_BLOCK_SIZE for S in BLOCK_SIZES] + \
+        [(src, os.path.splitext(src)[0], []) for src in SOURCES if src not in PER_BLOCK_SIZE]
 ARCH = "gfx950"
 # Per-source extra flags. The decode MFMA kernel keeps its accumulators in ordinary VGPRs:
 # with the default heuristic the compiler puts them in AGPRs and copies them back and forth for
@@ -46,9 +53,10 @@ def common_flags():
             "-Wall", "-Wno-unused-command-line-argument"]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), "-x", "hip", *common_flags(), *EXTRA_FLAGS.get(src, []), "-c",
+def _compile(unit, verbose: bool) -> str:
+    src, stem, defines = unit
+    obj = os.path.join(BUILD, stem + ".o")
+    cmd = [hipcc(), "-x", "hip", *common_flags(), *EXTRA_FLAGS.get(src, []), *defines, "-c",
            os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -64,9 +72,9 @@ def _compile(src: str, verbose: bool) -> str:
 
 def build(jobs: int | None = None, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 16)
+    jobs = jobs or min(len(UNITS), os.cpu_count() or 4, 16)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        objs = list(ex.map(lambda u: _compile(u, verbose), UNITS))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

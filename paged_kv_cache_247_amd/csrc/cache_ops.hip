@@ -63,6 +63,9 @@ hipError_t write_d(int block_size, const CacheWriteParams& p, hipStream_t stream
   switch (block_size) {
     case 16: reshape_and_cache_kernel<DT, D, 16><<<grid, 256, 0, stream>>>(p); break;
     case 32: reshape_and_cache_kernel<DT, D, 32><<<grid, 256, 0, stream>>>(p); break;
+    case 64: reshape_and_cache_kernel<DT, D, 64><<<grid, 256, 0, stream>>>(p); break;
+    case 128: reshape_and_cache_kernel<DT, D, 128><<<grid, 256, 0, stream>>>(p); break;
+    case 256: reshape_and_cache_kernel<DT, D, 256><<<grid, 256, 0, stream>>>(p); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();

@@ -27,6 +27,10 @@
 
 #include "kernels.hpp"
 
+#ifndef PKV_BLOCK_SIZE
+#error "build once per block size with -DPKV_BLOCK_SIZE=16|32|64|128|256"
+#endif
+
 namespace pkv {
 namespace {
 
@@ -72,10 +76,11 @@ decode_mfma_kernel(const DecodeParams a) {
   static_assert(DT == Dt::BF16 || DT == Dt::F16, "16-bit inputs only");
   constexpr int EB = 2;
   constexpr int CT = 32;        // positions per chunk
-  constexpr int BPC = CT / S;   // blocks per chunk
+  constexpr int BPC = S < CT ? CT / S : 1;  // blocks per chunk
+  constexpr int CPK = S > CT ? S / CT : 1;  // chunks per block
   constexpr int KK = D / 32;    // k-steps of the logits product
   constexpr int NT = D / 16;    // 16-row tiles of the output product
-  static_assert(BPC == 1 || BPC == 2, "block_size 16 or 32");
+  static_assert(BPC * S == CT || CPK * CT == S, "block_size 16, 32, 64, 128 or 256");
   using M = Mfma<DT>;
   using V8 = typename M::V8;
   using T = typename Elt<DT>::T;
@@ -131,17 +136,19 @@ decode_mfma_kernel(const DecodeParams a) {
   const int contig0 = i * MB;
   const int start = part * a.range_tokens;
 
-  // Waves take chunks wave, wave + NW, ... of the range: local chunk m of this wave covers
-  // logical blocks start / S + (wave + NW m) BPC + e, e < BPC. The wave keeps the ids of CPB
-  // consecutive local chunks in one register, lane BPC (m % CPB) + e holding block e of local
-  // chunk m, and picks them out with readlane. One coalesced vector load fills it every CPB
-  // chunks. (The block table cannot be read through the scalar cache inside the loop: the
+  // Waves take chunks wave, wave + NW, ... of the range: local chunk m of this wave is chunk
+  // n = wave + NW m, which covers logical blocks start / S + n BPC + e, e < BPC (blocks of 16
+  // or 32 positions), or rows (n % CPK) CT .. + CT of logical block start / S + n / CPK (larger
+  // blocks). The wave keeps the ids of CPB consecutive local chunks in one register, lane
+  // BPC (m % CPB) + e holding block e of local chunk m, and picks them out with readlane. One
+  // coalesced vector load fills it every CPB chunks. (The block table cannot be read through the scalar cache inside the loop: the
   // direct-to-LDS loads count as writes to unknown memory, which rules scalar loads out.)
   // The first batch is loaded now, in parallel with the context length; any entry of the row
   // may be read and ids are clamped into the pool before use.
   constexpr int CPB = 64 / BPC;
   auto load_id_batch = [&](int kb) {
-    const int blk = start / S + (wave + NW * (kb * CPB + lane / BPC)) * BPC + lane % BPC;
+    const int n = wave + NW * (kb * CPB + lane / BPC);
+    const int blk = start / S + (BPC == 2 ? n * BPC + lane % BPC : n / CPK);
     return blk < MB ? bt[blk] : 0;
   };
   int id_batch = 0;
@@ -183,23 +190,31 @@ decode_mfma_kernel(const DecodeParams a) {
   // K: this lane's operand rows are chunk positions t = 8(c/4) + (c%4) (+4 for the second
   // product), pieces 4 kk + r.
   const int k_tau = 8 * (c >> 2) + (c & 3);
-  // V^T: row d = 16 nt + c, positions 8r .. 8r+7 of block 8r / S.
+  // V^T: row d = 16 nt + c, positions 8r .. 8r+7 of the chunk (in block 8r / S when a chunk
+  // spans two blocks).
   const int v_blk = (8 * r) / S;
   const int v_off = c * S * EB + ((8 * r) % S) * EB;  // + nt * 16 rows
 
   struct Ids {
     int b0, b1;
+    int ro;  // first row of the chunk within block b0 (nonzero only for blocks over 32)
     // This lane's V^T pieces of the chunk, formed with the ids a step early; pieces 4 KiB and
     // more past vt are addressed from vt4 (= vt + 4 KiB, the reach of an immediate offset).
     const char* vt;
     const char* vt4;
+    // Blocks over 32 positions: the V^T rows are S elements apart, so the pieces span more
+    // than twice the immediate reach; they are loaded through a descriptor of the chunk's
+    // column range instead, the lane's offset in a VGPR and each row tile's in a scalar.
+    __amdgpu_buffer_rsrc_t vr;
   };
   auto clamp_id = [&](int id) { return min(max(id, 0), a.num_blocks - 1); };
   // Physical ids of local chunk m's blocks; a second block past the range reuses the first (its
   // positions are masked). Called for m = 0, 1, 2, ... in order.
   auto fetch_ids = [&](int m) {
-    const int b0 = start / S + (wave + NW * m) * BPC;
+    const int n = wave + NW * m;
+    const int b0 = start / S + (BPC == 2 ? n * BPC : n / CPK);
     Ids ids;
+    ids.ro = (n % CPK) * CT;
     if constexpr (TBL) {
       if (m > 0 && m % CPB == 0) {
         id_batch = load_id_batch(m / CPB);
@@ -216,8 +231,14 @@ decode_mfma_kernel(const DecodeParams a) {
       ids.b0 = clamp_id(contig0 + b0);
       ids.b1 = (BPC == 2 && b0 + 1 < blk_end) ? clamp_id(contig0 + b0 + 1) : ids.b0;
     }
-    ids.vt = vpool + (size_t)(v_blk ? ids.b1 : ids.b0) * id_stride + v_off;
-    ids.vt4 = ids.vt + 4096;
+    if constexpr (CPK > 1) {
+      ids.vr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(vpool + (size_t)ids.b0 * id_stride + (size_t)ids.ro * EB), 0,
+          (int)tile_bytes - ids.ro * EB, kBufferFlags);
+    } else {
+      ids.vt = vpool + (size_t)(v_blk ? ids.b1 : ids.b0) * id_stride + v_off;
+      ids.vt4 = ids.vt + 4096;
+    }
     return ids;
   };
 
@@ -234,14 +255,15 @@ decode_mfma_kernel(const DecodeParams a) {
   // as an in-order vector memory operation, while a global load into LDS makes it flush the
   // whole counter at every later wait.
   static_assert(S % (1024 / RB) == 0, "a 1 KiB load stays within one block");
-  auto tile_rsrc = [&](int id) {
+  auto tile_rsrc = [&](int id, int ro) {
     return __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(kpool + (size_t)id * id_stride), 0, (int)tile_bytes, kBufferFlags);
+        const_cast<char*>(kpool + (size_t)id * id_stride + (size_t)ro * RB), 0,
+        (int)tile_bytes - ro * RB, kBufferFlags);
   };
   auto load = [&](const Ids& ids, Regs& R, int slot) {
     char* dst = smem + (wave * 2 + slot) * SLOT;
-    const __amdgpu_buffer_rsrc_t r0 = tile_rsrc(ids.b0);
-    const __amdgpu_buffer_rsrc_t r1 = BPC == 2 ? tile_rsrc(ids.b1) : r0;
+    const __amdgpu_buffer_rsrc_t r0 = tile_rsrc(ids.b0, ids.ro);
+    const __amdgpu_buffer_rsrc_t r1 = BPC == 2 ? tile_rsrc(ids.b1, 0) : r0;
 #pragma unroll
     for (int x = 0; x < KLD; ++x) {
       const int t = x * (1024 / RB) + lane / NPC;
@@ -255,7 +277,11 @@ decode_mfma_kernel(const DecodeParams a) {
     for (int nt = 0; nt < NT; ++nt) {
       constexpr int kStep = 16 * S * EB;
       const int off = nt * kStep;
-      R.v[nt] = load_kv<NTL, u32x4>(off < 4096 ? ids.vt + off : ids.vt4 + (off - 4096));
+      if constexpr (CPK > 1)
+        R.v[nt] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(ids.vr, v_off, off, NTL ? 2 : 0));
+      else
+        R.v[nt] = load_kv<NTL, u32x4>(off < 4096 ? ids.vt + off : ids.vt4 + (off - 4096));
     }
   };
   // Operand pieces of chunk K from the wave's slot. The reads are issued as inline LDS
@@ -510,35 +536,29 @@ hipError_t launch_s(bool partial, bool nt, const DecodeParams& p, hipStream_t st
   return nt ? launch_p<DT, D, S, false, true>(p, stream) : launch_p<DT, D, S, false, false>(p, stream);
 }
 
-template <Dt DT, int D>
-hipError_t launch_d(int block_size, bool partial, bool nt, const DecodeParams& p,
-                    hipStream_t stream) {
-  switch (block_size) {
-    case 16: return launch_s<DT, D, 16>(partial, nt, p, stream);
-    case 32: return launch_s<DT, D, 32>(partial, nt, p, stream);
-    default: return hipErrorNotSupported;
-  }
-}
-
-template <Dt DT>
-hipError_t launch_t(int head_dim, int block_size, bool partial, bool nt, const DecodeParams& p,
+template <Dt DT, int S>
+hipError_t launch_d(int head_dim, bool partial, bool nt, const DecodeParams& p,
                     hipStream_t stream) {
   switch (head_dim) {
-    case 64: return launch_d<DT, 64>(block_size, partial, nt, p, stream);
-    case 128: return launch_d<DT, 128>(block_size, partial, nt, p, stream);
+    case 64: return launch_s<DT, 64, S>(partial, nt, p, stream);
+    case 128: return launch_s<DT, 128, S>(partial, nt, p, stream);
     default: return hipErrorNotSupported;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_mfma(Dt dt, int head_dim, int block_size, bool partial, bool nt,
-                              const DecodeParams& p, hipStream_t stream) {
+template <int S>
+hipError_t launch_decode_mfma_bs(Dt dt, int head_dim, bool partial, bool nt,
+                                 const DecodeParams& p, hipStream_t stream) {
   switch (dt) {
-    case Dt::F16: return launch_t<Dt::F16>(head_dim, block_size, partial, nt, p, stream);
-    case Dt::BF16: return launch_t<Dt::BF16>(head_dim, block_size, partial, nt, p, stream);
+    case Dt::F16: return launch_d<Dt::F16, S>(head_dim, partial, nt, p, stream);
+    case Dt::BF16: return launch_d<Dt::BF16, S>(head_dim, partial, nt, p, stream);
     default: return hipErrorNotSupported;
   }
 }
+
+template hipError_t launch_decode_mfma_bs<PKV_BLOCK_SIZE>(Dt, int, bool, bool,
+                                                          const DecodeParams&, hipStream_t);
 
 }  // namespace pkv

@@ -9,13 +9,19 @@
 // and physical blocks, and the two are linked by a block table"), and each sequence uses
 // only its own length, with no padding (same post, item 2-1).
 //
-// Lane geometry for a K tile [S][D] of a (block, kv head): a token row is LPR lanes x 16
-// bytes, so one wave load covers ROWS = 64 / LPR rows; lane (r, c) with r = lane / LPR and
-// c = lane % LPR owns positions r*TPL .. r*TPL+TPL-1 of every block and the 16-byte column
-// piece c of the K row. For the V^T tile [D][S] the same lane reads, for each of its VEC
-// head-dim rows d = c + LPR*y, the TPL contiguous positions it owns; so the softmax weights a
-// lane needs for P.V are the ones it computed itself, with no exchange.
+// A wave steps through the range CS = min(S, 32) positions at a time: a whole block up to
+// 32 positions, else a 32-position slice of one (so registers do not grow with S).
+// Lane geometry for the CS rows of a K tile [S][D] of a (block, kv head): a token row is LPR
+// lanes x 16 bytes, so one wave load covers ROWS = 64 / LPR rows; lane (r, c) with
+// r = lane / LPR and c = lane % LPR owns positions r*TPL .. r*TPL+TPL-1 of every step and the
+// 16-byte column piece c of the K row. For the V^T tile [D][S] the same lane reads, for each of
+// its VEC head-dim rows d = c + LPR*y, the TPL contiguous positions it owns; so the softmax
+// weights a lane needs for P.V are the ones it computed itself, with no exchange.
 #include "kernels.hpp"
+
+#ifndef PKV_BLOCK_SIZE
+#error "build once per block size with -DPKV_BLOCK_SIZE=16|32|64|128|256"
+#endif
 
 namespace pkv {
 namespace {
@@ -27,7 +33,9 @@ decode_valu_kernel(const DecodeParams a) {
   constexpr int VEC = 16 / EB;   // elements per 16-byte piece
   constexpr int LPR = D / VEC;   // lanes per K row
   constexpr int ROWS = 64 / LPR; // K rows per wave load
-  constexpr int TPL = S / ROWS;  // positions per lane per block
+  constexpr int CS = S < 32 ? S : 32;  // positions per step
+  constexpr int SPB = S / CS;    // steps per block
+  constexpr int TPL = CS / ROWS; // positions per lane per step
   constexpr int VB = TPL * EB;   // bytes per lane per V^T row
   constexpr int VW = VB / 4;     // 32-bit words per lane per V^T row
   static_assert(LPR >= 8 && LPR <= 32 && TPL >= 1, "unsupported head_dim/block_size/dtype");
@@ -57,10 +65,11 @@ decode_valu_kernel(const DecodeParams a) {
   auto table = [&](int j) { return bt[j]; };
   const int start = part * a.range_tokens;
 
-  // Waves take blocks start/S + wave, + NW, ...; the first one's id is fetched before the
-  // context length arrives (any entry of the row may be read; ids are clamped before use).
-  const int b_first = start / S + wave;
-  const int first_id = b_first < MB ? table(b_first) : 0;
+  // Waves take steps start/CS + wave, + NW, ... (step b covers positions b*CS .. b*CS+CS-1 of
+  // logical block b / SPB); the first one's id is fetched before the context length arrives
+  // (any entry of the row may be read; ids are clamped before use).
+  const int b_first = start / CS + wave;
+  const int first_id = b_first / SPB < MB ? table(b_first / SPB) : 0;
 
   int L = a.context_lens[i];
   L = min(max(L, 0), MB * S);
@@ -75,7 +84,7 @@ decode_valu_kernel(const DecodeParams a) {
   // last range) and the cache is read only up to L-2.
   const bool fused = a.new_key != nullptr && start + a.range_tokens >= L;
   const int end = min(start + a.range_tokens, L) - (fused ? 1 : 0);
-  const int blk_hi = (end + S - 1) / S;
+  const int blk_hi = (end + CS - 1) / CS;  // first step past the cached range
 
   // This lane's 16-byte piece of q for every head of the group, widened to fp32.
   float qf[G][VEC];
@@ -112,9 +121,10 @@ decode_valu_kernel(const DecodeParams a) {
   };
 
   auto clamp_id = [&](int id) { return min(max(id, 0), a.num_blocks - 1); };
-  auto load = [&](int id, Regs& R) {
-    const char* kt = kpool + (size_t)id * id_stride + k_off;
-    const char* vt = vpool + (size_t)id * id_stride + v_off;
+  auto load = [&](int id, int b, Regs& R) {
+    const int ob = (b % SPB) * CS;  // first position of step b within its block
+    const char* kt = kpool + (size_t)id * id_stride + (size_t)ob * D * EB + k_off;
+    const char* vt = vpool + (size_t)id * id_stride + ob * EB + v_off;
 #pragma unroll
     for (int x = 0; x < TPL; ++x) load_words<16, NTL>(kt + x * D * EB, R.k[x]);
 #pragma unroll
@@ -140,7 +150,7 @@ decode_valu_kernel(const DecodeParams a) {
 #pragma unroll
       for (int h = 0; h < G; ++h) s[x][h] = group_reduce<LPR>(s[x][h], OpAdd());
 
-    const int pos0 = b * S + r * TPL;
+    const int pos0 = b * CS + r * TPL;
     float mx[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -163,7 +173,7 @@ decode_valu_kernel(const DecodeParams a) {
         l[h] += s[x][h];
       }
     }
-    const bool tail = (b + 1) * S > end;
+    const bool tail = (b + 1) * CS > end;
 #pragma unroll
     for (int y = 0; y < VEC; ++y) {
       float vf[TPL];
@@ -228,22 +238,22 @@ decode_valu_kernel(const DecodeParams a) {
   int b = b_first;
   if (b < blk_hi) {
     Regs A, B;
-    load(clamp_id(first_id), A);
-    int id = b + NW < blk_hi ? clamp_id(table(b + NW)) : 0;
+    load(clamp_id(first_id), b, A);
+    int id = b + NW < blk_hi ? clamp_id(table((b + NW) / SPB)) : 0;
     if (fused) use_new_rows();
-    // Two register sets: block b + NW loads while block b computes; its id was fetched one
+    // Two register sets: step b + NW loads while step b computes; its id was fetched one
     // step earlier still.
     while (true) {
       if (b + NW < blk_hi) {
-        load(id, B);
-        if (b + 2 * NW < blk_hi) id = clamp_id(table(b + 2 * NW));
+        load(id, b + NW, B);
+        if (b + 2 * NW < blk_hi) id = clamp_id(table((b + 2 * NW) / SPB));
       }
       compute(b, A);
       b += NW;
       if (b >= blk_hi) break;
       if (b + NW < blk_hi) {
-        load(id, A);
-        if (b + 2 * NW < blk_hi) id = clamp_id(table(b + 2 * NW));
+        load(id, b + NW, A);
+        if (b + 2 * NW < blk_hi) id = clamp_id(table((b + 2 * NW) / SPB));
       }
       compute(b, B);
       b += NW;
@@ -350,36 +360,30 @@ hipError_t launch_s(int group, bool partial, bool nt, const DecodeParams& p,
   }
 }
 
-template <Dt DT, int D>
-hipError_t launch_d(int block_size, int group, bool partial, bool nt, const DecodeParams& p,
+template <Dt DT, int S>
+hipError_t launch_d(int head_dim, int group, bool partial, bool nt, const DecodeParams& p,
                     hipStream_t stream) {
-  switch (block_size) {
-    case 16: return launch_s<DT, D, 16>(group, partial, nt, p, stream);
-    case 32: return launch_s<DT, D, 32>(group, partial, nt, p, stream);
-    default: return hipErrorNotSupported;
-  }
-}
-
-template <Dt DT>
-hipError_t launch_t(int head_dim, int block_size, int group, bool partial, bool nt,
-                    const DecodeParams& p, hipStream_t stream) {
   switch (head_dim) {
-    case 64: return launch_d<DT, 64>(block_size, group, partial, nt, p, stream);
-    case 128: return launch_d<DT, 128>(block_size, group, partial, nt, p, stream);
+    case 64: return launch_s<DT, 64, S>(group, partial, nt, p, stream);
+    case 128: return launch_s<DT, 128, S>(group, partial, nt, p, stream);
     default: return hipErrorNotSupported;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_valu(Dt dt, int head_dim, int block_size, int group, bool partial,
-                              bool nt, const DecodeParams& p, hipStream_t stream) {
+template <int S>
+hipError_t launch_decode_valu_bs(Dt dt, int head_dim, int group, bool partial, bool nt,
+                                 const DecodeParams& p, hipStream_t stream) {
   switch (dt) {
-    case Dt::F32: return launch_t<Dt::F32>(head_dim, block_size, group, partial, nt, p, stream);
-    case Dt::F16: return launch_t<Dt::F16>(head_dim, block_size, group, partial, nt, p, stream);
-    case Dt::BF16: return launch_t<Dt::BF16>(head_dim, block_size, group, partial, nt, p, stream);
+    case Dt::F32: return launch_d<Dt::F32, S>(head_dim, group, partial, nt, p, stream);
+    case Dt::F16: return launch_d<Dt::F16, S>(head_dim, group, partial, nt, p, stream);
+    case Dt::BF16: return launch_d<Dt::BF16, S>(head_dim, group, partial, nt, p, stream);
   }
   return hipErrorNotSupported;
 }
+
+template hipError_t launch_decode_valu_bs<PKV_BLOCK_SIZE>(Dt, int, int, bool, bool,
+                                                          const DecodeParams&, hipStream_t);
 
 }  // namespace pkv

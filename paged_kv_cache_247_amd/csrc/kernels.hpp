@@ -72,10 +72,53 @@ struct CacheWriteParams {
 // Each returns hipSuccess or the launch error; hipErrorNotSupported if no instantiation
 // matches (the C ABI validates shapes before calling, so that is a library bug).
 // nt: non-temporal K/V loads (else cached loads, for shared prefixes).
-hipError_t launch_decode_valu(Dt dt, int head_dim, int block_size, int group, bool partial,
-                              bool nt, const DecodeParams& p, hipStream_t stream);
-hipError_t launch_decode_mfma(Dt dt, int head_dim, int block_size, bool partial, bool nt,
-                              const DecodeParams& p, hipStream_t stream);
+//
+// The decode kernels are built once per block size (decode_valu.hip and decode_mfma.hip are
+// compiled with -DPKV_BLOCK_SIZE=S, one object each), so each S is its own explicit
+// instantiation and no other translation unit instantiates them.
+template <int S>
+hipError_t launch_decode_valu_bs(Dt dt, int head_dim, int group, bool partial, bool nt,
+                                 const DecodeParams& p, hipStream_t stream);
+template <int S>
+hipError_t launch_decode_mfma_bs(Dt dt, int head_dim, bool partial, bool nt,
+                                 const DecodeParams& p, hipStream_t stream);
+#define PKV_DECODE_BLOCK_SIZE(S)                                                              \
+  extern template hipError_t launch_decode_valu_bs<S>(Dt, int, int, bool, bool,              \
+                                                      const DecodeParams&, hipStream_t);     \
+  extern template hipError_t launch_decode_mfma_bs<S>(Dt, int, bool, bool,                   \
+                                                      const DecodeParams&, hipStream_t);
+PKV_DECODE_BLOCK_SIZE(16)
+PKV_DECODE_BLOCK_SIZE(32)
+PKV_DECODE_BLOCK_SIZE(64)
+PKV_DECODE_BLOCK_SIZE(128)
+PKV_DECODE_BLOCK_SIZE(256)
+#undef PKV_DECODE_BLOCK_SIZE
+
+inline hipError_t launch_decode_valu(Dt dt, int head_dim, int block_size, int group,
+                                     bool partial, bool nt, const DecodeParams& p,
+                                     hipStream_t stream) {
+  switch (block_size) {
+    case 16: return launch_decode_valu_bs<16>(dt, head_dim, group, partial, nt, p, stream);
+    case 32: return launch_decode_valu_bs<32>(dt, head_dim, group, partial, nt, p, stream);
+    case 64: return launch_decode_valu_bs<64>(dt, head_dim, group, partial, nt, p, stream);
+    case 128: return launch_decode_valu_bs<128>(dt, head_dim, group, partial, nt, p, stream);
+    case 256: return launch_decode_valu_bs<256>(dt, head_dim, group, partial, nt, p, stream);
+    default: return hipErrorNotSupported;
+  }
+}
+
+inline hipError_t launch_decode_mfma(Dt dt, int head_dim, int block_size, bool partial,
+                                     bool nt, const DecodeParams& p, hipStream_t stream) {
+  switch (block_size) {
+    case 16: return launch_decode_mfma_bs<16>(dt, head_dim, partial, nt, p, stream);
+    case 32: return launch_decode_mfma_bs<32>(dt, head_dim, partial, nt, p, stream);
+    case 64: return launch_decode_mfma_bs<64>(dt, head_dim, partial, nt, p, stream);
+    case 128: return launch_decode_mfma_bs<128>(dt, head_dim, partial, nt, p, stream);
+    case 256: return launch_decode_mfma_bs<256>(dt, head_dim, partial, nt, p, stream);
+    default: return hipErrorNotSupported;
+  }
+}
+
 hipError_t launch_reduce(Dt dt, int head_dim, const ReduceParams& p, hipStream_t stream);
 hipError_t launch_reshape_and_cache(Dt dt, int head_dim, int block_size,
                                     const CacheWriteParams& p, hipStream_t stream);
