@@ -38,10 +38,13 @@ What is computed, and where each step comes from:
   o_p = sum exp(s - m_p) v / l_p; then M = max m_p, w_p = l_p exp(m_p - M),
   out = sum w_p o_p / sum w_p.
 
-Layout (the same statement the C header makes):
+Layout (the same statement the C header makes; the pages fix none of it):
   q, out       [B, H, D]
   k_cache      [N, Hkv, S, D]   element (b, g, t, d)
-  v_cache      [N, Hkv, D, S]   element (b, g, d, t)
+  v_cache      [N, Hkv, (S / VS) D, VS] with VS = min(S, 32): position t of the block is
+               column t % VS of column group t // VS, and head dim d is row d of that group,
+               so element (b, g, d, t) sits at [b, g, (t // VS) D + d, t % VS]. For S <= 32
+               there is one group and this is [N, Hkv, D, S].
   block_tables [B, MB] int32; entries past ceil(L_i / S) are never read
   context_lens [B] int32; L_i = 0 gives a zero output and no partials
 bf16 arrays are uint16 bit patterns; "f64" storage is accepted for invariance tests.
@@ -52,8 +55,16 @@ import math
 
 import numpy as np
 
-__all__ = ["to_f64", "write_cache", "copy_blocks", "gather", "decode", "decode_partials",
+__all__ = ["V_GROUP", "v_group", "to_f64", "write_cache", "copy_blocks", "gather", "decode", "decode_partials",
            "reduce_partials", "num_partitions", "prefill"]
+
+
+V_GROUP = 32  # most block positions in one column group of the V layout
+
+
+def v_group(block_size: int) -> int:
+    """Positions per column group of a V block (VS in the layout statement)."""
+    return min(int(block_size), V_GROUP)
 
 
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
@@ -72,6 +83,8 @@ def write_cache(k_cache, v_cache, key, value, slot_mapping, block_size):
     Token t with slot s >= 0 lands at block s // S, position s % S; a negative slot is
     skipped. Slots must be distinct (one correct result only then)."""
     S = block_size
+    VS = v_group(S)
+    D = k_cache.shape[3]
     slots = [int(s) for s in slot_mapping]
     live = [s for s in slots if s >= 0]
     assert len(set(live)) == len(live), "duplicate slots"
@@ -82,9 +95,10 @@ def write_cache(k_cache, v_cache, key, value, slot_mapping, block_size):
             continue
         b, off = s // S, s % S
         assert 0 <= b < k.shape[0], "slot outside the pool"
+        grp, col = off // VS, off % VS
         for g in range(k.shape[1]):
             k[b, g, off, :] = key[t, g, :]
-            v[b, g, :, off] = value[t, g, :]
+            v[b, g, grp * D:(grp + 1) * D, col] = value[t, g, :]
     return k, v
 
 
@@ -106,6 +120,8 @@ def copy_blocks(k_caches, v_caches, block_mapping):
 def gather(k_cache, v_cache, table_row, L, g, block_size, dtype):
     """Contiguous K_i, V_i [L, D] (float64) of one sequence and kv head g."""
     S = block_size
+    VS = v_group(S)
+    D = k_cache.shape[3]
     nb = -(-int(L) // S)
     Ks, Vs = [], []
     for j in range(nb):
@@ -113,8 +129,10 @@ def gather(k_cache, v_cache, table_row, L, g, block_size, dtype):
         assert 0 <= b < k_cache.shape[0], "block id outside the pool"
         rows = min(S, int(L) - j * S)
         Ks.append(to_f64(k_cache[b, g, :rows, :], dtype))
-        Vs.append(to_f64(v_cache[b, g, :, :rows], dtype).T)
-    D = k_cache.shape[3]
+        # V positions 0..rows-1 of the block, column group by column group
+        for grp in range(-(-rows // VS)):
+            cols = min(VS, rows - grp * VS)
+            Vs.append(to_f64(v_cache[b, g, grp * D:(grp + 1) * D, :cols], dtype).T)
     if not Ks:
         return np.zeros((0, D)), np.zeros((0, D))
     return np.concatenate(Ks, axis=0), np.concatenate(Vs, axis=0)

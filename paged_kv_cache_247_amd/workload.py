@@ -18,7 +18,9 @@ Sources for what is generated:
 
 Pool layout (one layer):
   k_cache[N, Hkv, S, D]  -- token rows, head_dim contiguous
-  v_cache[N, Hkv, D, S]  -- head_dim rows, block positions contiguous
+  v_cache[N, Hkv, (S/VS) D, VS], VS = min(S, 32) -- column groups of VS block positions,
+      head_dim rows within each (position t, dim d at row (t // VS) D + d, column t % VS);
+      for S <= 32 simply [N, Hkv, D, S]
 bf16 values are carried as uint16 bit patterns (numpy has no bf16 type).
 
 Reading of the length of a step: context_lens[i] counts the token written this step. The
@@ -55,6 +57,16 @@ def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     lsb = (u >> np.uint32(16)) & np.uint32(1)
     return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def v_group(block_size: int) -> int:
+    """Positions per column group of the V pool layout."""
+    return min(int(block_size), 32)
+
+
+def v_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int):
+    VS = v_group(block_size)
+    return (num_blocks, num_kv_heads, block_size // VS * head_dim, VS)
 
 
 def cast_from_f32(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -115,6 +127,18 @@ class Config:
 
     def replace(self, **kw) -> "Config":
         return dataclasses.replace(self, **kw)
+
+    def with_block_size(self, S: int) -> "Config":
+        """The same workload in blocks of S positions: the pool keeps at least its capacity in
+        positions and holds the worst-case draw (every sequence at the longest length, the
+        shared prefix and the copy-on-write targets)."""
+        if self.prefix_len % S or (self.partition_size and self.partition_size % S):
+            raise ValueError(f"block size {S} does not divide the prefix or the partitions")
+        own = self.max_len - self.prefix_len
+        need = self.num_seqs * -(-own // S) + self.prefix_len // S + self.cow_seqs
+        scaled = -(-self.num_blocks * self.block_size // S)
+        return self.replace(block_size=S, num_blocks=max(need, scaled),
+                            description=f"{self.description}; block size {S}")
 
 
 # The five serving-shaped workloads. Sizes: tiny fp32; 7B-like MHA; grouped-query;
@@ -186,7 +210,7 @@ class Workload:
     block_mapping: np.ndarray  # int64 [M, 2]: (src, dst) copy-on-write pairs
     q: np.ndarray  # [B, H, D]
     k_cache: np.ndarray  # [N, Hkv, S, D]: pool before this step's copies and writes
-    v_cache: np.ndarray  # [N, Hkv, D, S]
+    v_cache: np.ndarray  # [N, Hkv, (S / VS) D, VS], VS = min(S, 32)
     key: np.ndarray  # [B, Hkv, D]: newest token of each sequence
     value: np.ndarray  # [B, Hkv, D]
     slot_mapping: np.ndarray  # int64 [B]: slot = block_id * S + offset of that token
@@ -400,10 +424,12 @@ def generate(cfg: Config, poison: str = "nan", keep_logical: bool = False,
         place &= (pos_of >= cfg.prefix_len) | (seq_of == 0)
     blk = tables_before[seq_of[place], pos_of[place] // S].astype(np.int64)
     slot_off = pos_of[place] % S
+    VS = v_group(S)
     k_cache = _fill((N, Hkv, S, D), cfg.dtype, poison, rng)
-    v_cache = _fill((N, Hkv, D, S), cfg.dtype, poison, rng)
+    v_cache = _fill((N, Hkv, (S // VS) * D, VS), cfg.dtype, poison, rng)
     k_cache[blk, :, slot_off, :] = ks[row_of[place]]
-    v_cache[blk, :, :, slot_off] = vs[row_of[place]]
+    v_cache.reshape(N, Hkv, S // VS, D, VS)[blk, :, slot_off // VS, :, slot_off % VS] = \
+        vs[row_of[place]]
 
     # Newest token of each sequence: written by reshape_and_cache during the step. A sequence
     # with an empty context has none: its slot is -1 (skipped) and its rows are zero.

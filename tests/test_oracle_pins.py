@@ -101,6 +101,16 @@ def test_paged_equals_padded_dense_sdpa(name):
     assert check_dense(wl) < 1e-12
 
 
+@pytest.mark.parametrize("S", [64, 256])
+@pytest.mark.parametrize("name", ["c3", "c4"])
+def test_paged_equals_padded_dense_sdpa_large_blocks(name, S):
+    cfg = W.SMALL[name]
+    if cfg.prefix_len:
+        cfg = cfg.replace(prefix_len=S, len_hi=S + 40, num_blocks=64)
+    wl = W.generate(cfg.with_block_size(S), keep_logical=True)
+    assert check_dense(wl) < 1e-12
+
+
 @pytest.mark.parametrize("name", ["c1", "c3", "c5"])
 def test_decode_is_last_row_of_causal_recompute(name):
     wl = W.generate(W.SMALL[name], keep_logical=True)
@@ -262,9 +272,12 @@ def test_linearity_in_v():
 
 def brute_decode(q, kc, vc, tables, lens, scale, Hkv):
     """Pure-Python loops with math.exp / math.fsum, reading the pools as flat lists through
-    the layout's element offsets ((b*Hkv + g)*S + t)*D + d and ((b*Hkv + g)*D + d)*S + t."""
+    the layout's element offsets: K at ((b*Hkv + g)*S + t)*D + d; V at
+    ((b*Hkv + g)*S + VS*(t // VS))*D + VS*d + t % VS with VS = min(S, 32) (for S <= 32 that
+    is ((b*Hkv + g)*D + d)*S + t)."""
     B, H, D = q.shape
     N, _, S, _ = kc.shape
+    VS = min(S, 32)
     kf = kc.astype(np.float64).ravel().tolist()
     vf = vc.astype(np.float64).ravel().tolist()
     G = H // Hkv
@@ -277,7 +290,8 @@ def brute_decode(q, kc, vc, tables, lens, scale, Hkv):
             for pos in range(L):
                 b, t = int(tables[i][pos // S]), pos % S
                 krow = [kf[((b * Hkv + g) * S + t) * D + d] for d in range(D)]
-                vrow = [vf[((b * Hkv + g) * D + d) * S + t] for d in range(D)]
+                vrow = [vf[((b * Hkv + g) * S + VS * (t // VS)) * D + VS * d + t % VS]
+                        for d in range(D)]
                 logits.append(scale * math.fsum(float(q[i, h, d]) * krow[d] for d in range(D)))
                 rows.append(vrow)
             if not L:
@@ -297,6 +311,22 @@ def test_brute_force_tiny():
     out = _decode(wl, kc, vc)
     ref = brute_decode(wl.q, kc, vc, wl.block_tables, wl.context_lens, cfg.scale, 2)
     assert oracle.max_abs_err(out, ref) < 1e-12
+
+
+@pytest.mark.parametrize("S,len_hi", [(64, 150), (128, 300)])
+def test_brute_force_large_blocks(S, len_hi):
+    """Blocks of several V column groups: contexts end inside the first, second and later
+    groups of a block."""
+    assert check_brute_large(S, len_hi) < 1e-12
+
+
+def check_brute_large(S, len_hi):
+    cfg = W.Config("tinyS", 3, 4, 2, 4, S, 12, "f32", 97, "uniform", len_lo=1, len_hi=len_hi)
+    wl = W.generate(cfg, lens=np.array([len_hi, S + 5, 33], dtype=np.int32))
+    kc, vc = _step_pool(wl)
+    out = _decode(wl, kc, vc)
+    ref = brute_decode(wl.q, kc, vc, wl.block_tables, wl.context_lens, cfg.scale, 2)
+    return oracle.max_abs_err(out, ref)
 
 
 def test_gather_follows_layout_statement():
@@ -344,6 +374,7 @@ def _all_pins_pass():
     for name in ("c1", "c3", "c5"):
         wl = W.generate(W.SMALL[name], keep_logical=True)
         ok = ok and check_dense(wl) < 1e-12 and check_split(wl, 2 * wl.cfg.block_size) < 1e-12
+    ok = ok and check_brute_large(64, 150) < 1e-12
     return bool(ok)
 
 
@@ -407,6 +438,14 @@ def _bad_decode_gqa(q, k_cache, v_cache, block_tables, context_lens, scale, num_
     return out
 
 
+def _bad_gather_v_groups(k_cache, v_cache, table_row, L, g, S, dtype):
+    """Reads the V column groups of a block in the wrong order (rows as d * groups + group)."""
+    N, Hkv, R, VS = v_cache.shape
+    G = R // k_cache.shape[3]
+    vv = v_cache.reshape(N, Hkv, k_cache.shape[3], G, VS).transpose(0, 1, 3, 2, 4)
+    return _orig_gather(k_cache, vv.reshape(N, Hkv, R, VS), table_row, L, g, S, dtype)
+
+
 _orig_gather = pa.gather
 
 
@@ -416,6 +455,7 @@ _orig_gather = pa.gather
     ("gather", _bad_gather_full_last_block),
     ("gather", _bad_gather_shifted_table),
     ("gather", _bad_gather_wrong_head),
+    ("gather", _bad_gather_v_groups),
     ("reduce_partials", _bad_reduce_sign),
     ("write_cache", _bad_write_swapped),
 ])
