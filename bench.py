@@ -70,6 +70,9 @@ def parse():
                     help="repetitions of back-to-back launch timing per kernel")
     ap.add_argument("--launches", type=int, default=100,
                     help="back-to-back launches per repetition")
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="run the workload in blocks of this many positions (16..256); the "
+                         "pool keeps at least its capacity")
     ap.add_argument("--shard", default=None, metavar="KIND:N",
                     help="run one GPU's share of an N-GPU job at its real shape: kv:N keeps "
                          "1/N of the kv heads (and their q heads), seq:N 1/N of the sequences")
@@ -324,6 +327,8 @@ def main():
     kernel = args.kernel or kernel
     P = P if args.partition_size is None else args.partition_size
     cfg = W.CONFIGS[name]
+    if args.block_size and args.block_size != cfg.block_size:
+        cfg = cfg.with_block_size(args.block_size)
     shard = None
     if args.shard:
         kind, _, n = args.shard.partition(":")
@@ -457,7 +462,9 @@ def main():
     kvb = wl.kv_bytes()
     family = "mfma" if (kernel == "mfma" or (kernel == "auto" and cfg.dtype != "f32"
                                              and cfg.group >= 4)) else "valu"
-    traffic = None if shard else counter_traffic(KERNEL_SOURCES[family], name)
+    # The recorded counters belong to the workload as defined (its block size, whole batch).
+    traffic = None if shard or cfg.block_size != W.CONFIGS[name].block_size \
+        else counter_traffic(KERNEL_SOURCES[family], name)
     value = kvb / (ms_step * 1e-3) / 1e9
     ukvb = wl.unique_kv_bytes() if has_copy else kvb
     # With shared prefix blocks the logical bytes count the prefix once per sequence, but it is

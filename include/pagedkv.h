@@ -24,7 +24,11 @@
  * Layouts (row-major, contiguous; T = the element type named by pkv_dtype):
  *   q, out         [B, H, D]        T
  *   k_cache        [N, Hkv, S, D]   T   -- token rows; a (block, kv head) tile is S*D contiguous
- *   v_cache        [N, Hkv, D, S]   T   -- head_dim rows of S positions; also one contiguous tile
+ *   v_cache        [N, Hkv, (S/VS)*D, VS]  T, VS = min(S, 32) -- column groups of VS positions,
+ *                                       each a [D, VS] tile (head_dim rows): position t, dim d of
+ *                                       a block at row (t / VS)*D + d, column t % VS; for
+ *                                       S <= 32 simply [N, Hkv, D, S]. A (block, kv head) tile is
+ *                                       S*D contiguous, like K
  *   key, value     [T_new, Hkv, D]  T   -- the new tokens of this step
  *   slot_mapping   [T_new]          int64, slot = block_id * S + position_in_block
  *   block_tables   [B, MB]          int32; entries at or past ceil(L_i / S) are never used
@@ -59,8 +63,10 @@
  * [0, NPmax]) and skip slots outside [0, N * S); the results for the affected sequences are
  * then undefined.
  *
- * Supported shapes: D in {64, 128}; S in {16, 32}; G = H / Hkv in {1, 2, 4, 8, 16}
- * (fp32 and the VALU kernel: G <= 8); partition_size 0 or a positive multiple of S.
+ * Supported shapes: D in {64, 128}; S in {16, 32, 64, 128, 256} (the range of block sizes that
+ * item 1-2 of the Qualiteg post calls best: larger blocks bring fragmentation back; prefill:
+ * S in {16, 32}); G = H / Hkv in {1, 2, 4, 8, 16} (fp32 and the VALU kernel: G <= 8);
+ * partition_size 0 or a positive multiple of S.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H

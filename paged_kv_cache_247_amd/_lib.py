@@ -169,14 +169,21 @@ def _dt(t: torch.Tensor) -> int:
         raise TypeError(f"unsupported dtype {t.dtype}") from None
 
 
+def v_block_shape(num_kv_heads: int, head_dim: int, block_size: int) -> tuple:
+    """Shape of one V block: column groups of VS = min(S, 32) positions, each a [D, VS] tile,
+    stacked as [Hkv, (S / VS) D, VS] (for S <= 32 that is [Hkv, D, S])."""
+    vs = min(block_size, 32)
+    return (num_kv_heads, block_size // vs * head_dim, vs)
+
+
 def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping):
     """Write new K/V rows [T, Hkv, D] into their slots of the pools (pkv_reshape_and_cache)."""
     _need(k_cache, "k_cache", ndim=4)
     dt = k_cache.dtype
     N, Hkv, S, D = k_cache.shape
     _need(v_cache, "v_cache", dt, 4, k_cache.device)
-    if tuple(v_cache.shape) != (N, Hkv, D, S):
-        raise ValueError(f"v_cache must be [N, Hkv, D, S] = {(N, Hkv, D, S)}")
+    if tuple(v_cache.shape) != (N, *v_block_shape(Hkv, D, S)):
+        raise ValueError(f"v_cache must be {(N, *v_block_shape(Hkv, D, S))}")
     _need(key, "key", dt, 3, k_cache.device)
     _need(value, "value", dt, 3, k_cache.device)
     T = key.shape[0]
@@ -231,8 +238,8 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     if Dk != D:
         raise ValueError("head_dim of q and k_cache differ")
     _need(v_cache, "v_cache", dt, 4, q.device)
-    if tuple(v_cache.shape) != (N, Hkv, D, S):
-        raise ValueError("v_cache must be [N, Hkv, D, S]")
+    if tuple(v_cache.shape) != (N, *v_block_shape(Hkv, D, S)):
+        raise ValueError(f"v_cache must be {(N, *v_block_shape(Hkv, D, S))}")
     _need(context_lens, "context_lens", torch.int32, 1, q.device)
     if block_tables is None:  # contiguous reservation: max_blocks_per_seq blocks per sequence
         if max_blocks_per_seq is None:
@@ -302,8 +309,8 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens
     if Dk != D:
         raise ValueError("head_dim of q and k_cache differ")
     _need(v_cache, "v_cache", dt, 4, q.device)
-    if tuple(v_cache.shape) != (N, Hkv, D, S):
-        raise ValueError("v_cache must be [N, Hkv, D, S]")
+    if tuple(v_cache.shape) != (N, *v_block_shape(Hkv, D, S)):
+        raise ValueError(f"v_cache must be {(N, *v_block_shape(Hkv, D, S))}")
     _need(block_tables, "block_tables", torch.int32, 2, q.device)
     B, MB = block_tables.shape
     _need(context_lens, "context_lens", torch.int32, 1, q.device)
@@ -345,7 +352,7 @@ def copy_blocks(k_caches, v_caches, block_mapping):
     for k, v in zip(k_caches, v_caches):
         _need(k, "k_cache", k0.dtype, 4, k0.device)
         _need(v, "v_cache", k0.dtype, 4, k0.device)
-        if tuple(k.shape) != (N, Hkv, S, D) or tuple(v.shape) != (N, Hkv, D, S):
+        if tuple(k.shape) != (N, Hkv, S, D) or tuple(v.shape) != (N, *v_block_shape(Hkv, D, S)):
             raise ValueError("every layer's pools must have the same shape")
     _need(block_mapping, "block_mapping", torch.int64, 2, k0.device)
     if block_mapping.shape[1] != 2:
@@ -421,8 +428,8 @@ class VmmPool:
         N = num_seqs * self.blocks_per_seq
         self.k = DeviceRegion(lib.pkv_vmm_pool_k(h), (N, num_kv_heads, block_size, head_dim),
                               dtype, dev)
-        self.v = DeviceRegion(lib.pkv_vmm_pool_v(h), (N, num_kv_heads, head_dim, block_size),
-                              dtype, dev)
+        self.v = DeviceRegion(lib.pkv_vmm_pool_v(h),
+                              (N, *v_block_shape(num_kv_heads, head_dim, block_size)), dtype, dev)
 
     @property
     def mapped_bytes(self) -> int:
@@ -436,14 +443,15 @@ class VmmPool:
 
     def write(self, seq: int, k_blocks: torch.Tensor, v_blocks: torch.Tensor):
         """Copy blocks [0, n) of sequence seq in from device tensors [n, Hkv, S, D] and
-        [n, Hkv, D, S] (on the current stream)."""
+        [n, *v_block_shape] (on the current stream)."""
         self._copy(seq, k_blocks, v_blocks, 1)
 
     def read(self, seq: int, num_blocks: int):
         """Blocks [0, num_blocks) of sequence seq, copied out into new tensors."""
         Hkv, S, D = self.block_shape
         k = torch.empty((num_blocks, Hkv, S, D), dtype=self.k.dtype, device=self.k.device)
-        v = torch.empty((num_blocks, Hkv, D, S), dtype=self.k.dtype, device=self.k.device)
+        v = torch.empty((num_blocks, *v_block_shape(Hkv, D, S)), dtype=self.k.dtype,
+                        device=self.k.device)
         self._copy(seq, k, v, 0)
         return k, v
 
@@ -452,8 +460,8 @@ class VmmPool:
         n = k.shape[0]
         _need(k, "k", self.k.dtype, 4, self.k.device)
         _need(v, "v", self.k.dtype, 4, self.k.device)
-        if tuple(k.shape) != (n, Hkv, S, D) or tuple(v.shape) != (n, Hkv, D, S):
-            raise ValueError("blocks must be [n, Hkv, S, D] and [n, Hkv, D, S]")
+        if tuple(k.shape) != (n, Hkv, S, D) or tuple(v.shape) != (n, *v_block_shape(Hkv, D, S)):
+            raise ValueError("blocks must be [n, Hkv, S, D] and [n, *v_block_shape]")
         _check(load().pkv_vmm_pool_copy(self._h, seq, n, _ptr(k), _ptr(v), to_pool, _stream(k)))
 
     def close(self):

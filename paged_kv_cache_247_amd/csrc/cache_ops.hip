@@ -13,7 +13,8 @@ namespace pkv {
 namespace {
 
 // One workgroup per new token. K rows are 16-byte vector stores into the [S][D] tile; V
-// elements go to column `pos` of the [D][S] tile.
+// elements go to column pos % VS of column group pos / VS, each group a [D][VS] tile
+// (VS = min(S, 32)).
 template <Dt DT, int D, int S>
 __global__ void __launch_bounds__(256) reshape_and_cache_kernel(const CacheWriteParams a) {
   using T = typename Elt<DT>::T;
@@ -34,12 +35,13 @@ __global__ void __launch_bounds__(256) reshape_and_cache_kernel(const CacheWrite
     const u32x4 x = *reinterpret_cast<const u32x4*>(key + ((size_t)h * D + d) * EB);
     *reinterpret_cast<u32x4*>(kc + ((((size_t)blk * Hkv + h) * S + pos) * D + d) * EB) = x;
   }
+  constexpr int VS = S < 32 ? S : 32;
   const T* val = reinterpret_cast<const T*>(a.value) + (size_t)t * Hkv * D;
-  T* vc = reinterpret_cast<T*>(a.v_cache);
+  T* vc = reinterpret_cast<T*>(a.v_cache) + (size_t)(pos / VS) * VS * D + pos % VS;
   for (int e = threadIdx.x; e < Hkv * D; e += blockDim.x) {
     const int h = e / D;
     const int d = e % D;
-    vc[(((size_t)blk * Hkv + h) * D + d) * S + pos] = val[e];
+    vc[((size_t)blk * Hkv + h) * S * D + (size_t)d * VS] = val[e];
   }
 }
 

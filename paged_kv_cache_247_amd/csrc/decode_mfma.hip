@@ -20,7 +20,8 @@
 //     head c, in order.
 //   output   O^T[d][h] = sum_t V^T[d][t] P^T[t][h]  A = V^T rows, B = softmax weights
 //     lane (r, c) loads V^T row d = 16 nt + c at positions 8r .. 8r+7 -- 16 contiguous bytes
-//     of the [D][S] tile -- and its B operand is exactly the eight weights it computed.
+//     of the chunk's [D][32] column group (two [D][16] tiles at block size 16) -- and its B
+//     operand is exactly the eight weights it computed.
 //   The accumulator of tile nt holds O^T[16 nt + 4r + i][c]: the head is the lane's own
 //   column, so the online-softmax rescale uses the lane's own running max; no exchange.
 #include <type_traits>
@@ -191,9 +192,11 @@ decode_mfma_kernel(const DecodeParams a) {
   // product), pieces 4 kk + r.
   const int k_tau = 8 * (c >> 2) + (c & 3);
   // V^T: row d = 16 nt + c, positions 8r .. 8r+7 of the chunk (in block 8r / S when a chunk
-  // spans two blocks).
+  // spans two blocks). A block stores V in column groups of VS positions, each a [D][VS]
+  // tile; a chunk of a larger block is exactly one group, ro D elements into the block.
+  constexpr int VS = S < CT ? S : CT;
   const int v_blk = (8 * r) / S;
-  const int v_off = c * S * EB + ((8 * r) % S) * EB;  // + nt * 16 rows
+  const int v_off = c * VS * EB + ((8 * r) % S) * EB;  // + nt * 16 rows
 
   struct Ids {
     int b0, b1;
@@ -202,10 +205,6 @@ decode_mfma_kernel(const DecodeParams a) {
     // more past vt are addressed from vt4 (= vt + 4 KiB, the reach of an immediate offset).
     const char* vt;
     const char* vt4;
-    // Blocks over 32 positions: the V^T rows are S elements apart, so the pieces span more
-    // than twice the immediate reach; they are loaded through a descriptor of the chunk's
-    // column range instead, the lane's offset in a VGPR and each row tile's in a scalar.
-    __amdgpu_buffer_rsrc_t vr;
   };
   auto clamp_id = [&](int id) { return min(max(id, 0), a.num_blocks - 1); };
   // Physical ids of local chunk m's blocks; a second block past the range reuses the first (its
@@ -231,14 +230,9 @@ decode_mfma_kernel(const DecodeParams a) {
       ids.b0 = clamp_id(contig0 + b0);
       ids.b1 = (BPC == 2 && b0 + 1 < blk_end) ? clamp_id(contig0 + b0 + 1) : ids.b0;
     }
-    if constexpr (CPK > 1) {
-      ids.vr = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<char*>(vpool + (size_t)ids.b0 * id_stride + (size_t)ids.ro * EB), 0,
-          (int)tile_bytes - ids.ro * EB, kBufferFlags);
-    } else {
-      ids.vt = vpool + (size_t)(v_blk ? ids.b1 : ids.b0) * id_stride + v_off;
-      ids.vt4 = ids.vt + 4096;
-    }
+    ids.vt = vpool + (size_t)(v_blk ? ids.b1 : ids.b0) * id_stride + (size_t)ids.ro * D * EB +
+             v_off;
+    ids.vt4 = ids.vt + 4096;
     return ids;
   };
 
@@ -275,13 +269,9 @@ decode_mfma_kernel(const DecodeParams a) {
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      constexpr int kStep = 16 * S * EB;
+      constexpr int kStep = 16 * VS * EB;
       const int off = nt * kStep;
-      if constexpr (CPK > 1)
-        R.v[nt] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(ids.vr, v_off, off, NTL ? 2 : 0));
-      else
-        R.v[nt] = load_kv<NTL, u32x4>(off < 4096 ? ids.vt + off : ids.vt4 + (off - 4096));
+      R.v[nt] = load_kv<NTL, u32x4>(off < 4096 ? ids.vt + off : ids.vt4 + (off - 4096));
     }
   };
   // Operand pieces of chunk K from the wave's slot. The reads are issued as inline LDS
@@ -461,10 +451,10 @@ decode_mfma_kernel(const DecodeParams a) {
     const int p = L - 1;
     const size_t tile = ((size_t)clamp_id(slot_blk) * Hkv + g) * S * D;
     T* kc = reinterpret_cast<T*>(a.k_cache) + tile + (size_t)(p % S) * D;
-    T* vc = reinterpret_cast<T*>(a.v_cache) + tile + (p % S);
+    T* vc = reinterpret_cast<T*>(a.v_cache) + tile + (size_t)((p % S) / VS) * VS * D + p % VS;
     if (lane < D * EB / 16) reinterpret_cast<u32x4*>(kc)[lane] = krow;
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) vc[(size_t)(lane + 64 * e) * S] = vrow[e];
+    for (int e = 0; e < D / 64; ++e) vc[(size_t)(lane + 64 * e) * VS] = vrow[e];
   }
 
   l = across16(l, OpAdd());

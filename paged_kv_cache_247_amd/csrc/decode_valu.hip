@@ -14,9 +14,10 @@
 // Lane geometry for the CS rows of a K tile [S][D] of a (block, kv head): a token row is LPR
 // lanes x 16 bytes, so one wave load covers ROWS = 64 / LPR rows; lane (r, c) with
 // r = lane / LPR and c = lane % LPR owns positions r*TPL .. r*TPL+TPL-1 of every step and the
-// 16-byte column piece c of the K row. For the V^T tile [D][S] the same lane reads, for each of
-// its VEC head-dim rows d = c + LPR*y, the TPL contiguous positions it owns; so the softmax
-// weights a lane needs for P.V are the ones it computed itself, with no exchange.
+// 16-byte column piece c of the K row. A block stores V in column groups of CS positions, each
+// a [D][CS] tile, so a step reads one group; the same lane reads, for each of its VEC head-dim
+// rows d = c + LPR*y, the TPL contiguous positions it owns; so the softmax weights a lane
+// needs for P.V are the ones it computed itself, with no exchange.
 #include "kernels.hpp"
 
 #ifndef PKV_BLOCK_SIZE
@@ -113,7 +114,7 @@ decode_valu_kernel(const DecodeParams a) {
   const char* kpool = reinterpret_cast<const char*>(a.k_cache) + (size_t)g * tile_bytes;
   const char* vpool = reinterpret_cast<const char*>(a.v_cache) + (size_t)g * tile_bytes;
   const int k_off = (r * TPL) * D * EB + c * 16;   // + x * D * EB
-  const int v_off = c * S * EB + r * TPL * EB;     // + y * LPR * S * EB
+  const int v_off = c * CS * EB + r * TPL * EB;    // + y * LPR * CS * EB
 
   struct Regs {
     uint32_t k[TPL][4];
@@ -124,11 +125,11 @@ decode_valu_kernel(const DecodeParams a) {
   auto load = [&](int id, int b, Regs& R) {
     const int ob = (b % SPB) * CS;  // first position of step b within its block
     const char* kt = kpool + (size_t)id * id_stride + (size_t)ob * D * EB + k_off;
-    const char* vt = vpool + (size_t)id * id_stride + ob * EB + v_off;
+    const char* vt = vpool + (size_t)id * id_stride + (size_t)ob * D * EB + v_off;
 #pragma unroll
     for (int x = 0; x < TPL; ++x) load_words<16, NTL>(kt + x * D * EB, R.k[x]);
 #pragma unroll
-    for (int y = 0; y < VEC; ++y) load_words<VB, NTL>(vt + y * LPR * S * EB, R.v[y]);
+    for (int y = 0; y < VEC; ++y) load_words<VB, NTL>(vt + y * LPR * CS * EB, R.v[y]);
   };
 
   auto compute = [&](int b, const Regs& R) {
@@ -270,10 +271,10 @@ decode_valu_kernel(const DecodeParams a) {
     const int p = L - 1;
     const size_t tile = ((size_t)clamp_id(slot_blk) * Hkv + g) * S * D;
     T* kc = reinterpret_cast<T*>(a.k_cache) + tile + (size_t)(p % S) * D;
-    T* vc = reinterpret_cast<T*>(a.v_cache) + tile + (p % S);
+    T* vc = reinterpret_cast<T*>(a.v_cache) + tile + (size_t)((p % S) / CS) * CS * D + p % CS;
     if (lane < D * EB / 16) reinterpret_cast<u32x4*>(kc)[lane] = krow;
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) vc[(size_t)(lane + 64 * e) * S] = vrow[e];
+    for (int e = 0; e < D / 64; ++e) vc[(size_t)(lane + 64 * e) * CS] = vrow[e];
   }
 
   // Sum each lane's positions over the row groups (lanes that share c hold the same columns).

@@ -62,13 +62,12 @@ class DecodeEngine:
         tdt = _TORCH[dtype]
         self.k = torch.zeros((num_blocks, num_kv_heads, block_size, head_dim), dtype=tdt,
                              device=self.device)
-        self.v = torch.zeros((num_blocks, num_kv_heads, head_dim, block_size), dtype=tdt,
-                             device=self.device)
+        vshape = L.v_block_shape(num_kv_heads, head_dim, block_size)
+        self.v = torch.zeros((num_blocks, *vshape), dtype=tdt, device=self.device)
         pin = self.device.type == "cuda"
         self.hk = torch.zeros((max(num_host_blocks, 1), num_kv_heads, block_size, head_dim),
                               dtype=tdt, pin_memory=pin)
-        self.hv = torch.zeros((max(num_host_blocks, 1), num_kv_heads, head_dim, block_size),
-                              dtype=tdt, pin_memory=pin)
+        self.hv = torch.zeros((max(num_host_blocks, 1), *vshape), dtype=tdt, pin_memory=pin)
         self.requests: dict[int, Request] = {}
         self.waiting: deque[int] = deque()
         self.running: list[int] = []
