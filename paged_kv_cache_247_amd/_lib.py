@@ -12,6 +12,8 @@ import os
 
 import torch
 
+from . import contract as _contract
+
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpagedkv.so")
 
@@ -80,6 +82,23 @@ class PagedKVError(RuntimeError):
         super().__init__(f"status {status}: {message}")
         self.status = status
         self.message = message
+
+
+def validating() -> bool:
+    """PKV_VALIDATE=1: check the contents of tables, lengths, slots and copy pairs on the host
+    before each call (a device-to-host copy per call; for debugging)."""
+    return os.environ.get("PKV_VALIDATE", "0") not in ("", "0")
+
+
+def _host(t):
+    return None if t is None else t.detach().cpu().numpy()
+
+
+def _contract_check(fn, *args, **kw):
+    try:
+        fn(*args, **kw)
+    except _contract.ContractError as e:
+        raise PagedKVError(1, f"caller contract: {e}") from None
 
 
 _lib = None
@@ -192,6 +211,8 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping):
     _need(slot_mapping, "slot_mapping", torch.int64, 1, k_cache.device)
     if slot_mapping.shape[0] != T:
         raise ValueError("slot_mapping must have one slot per token")
+    if validating():
+        _contract_check(_contract.check_slots, _host(slot_mapping), S, N)
     _check(load().pkv_reshape_and_cache(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
                                         _ptr(slot_mapping), T, Hkv, D, S, N, _dt(k_cache),
                                         _stream(k_cache)))
@@ -275,6 +296,10 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         _need(out, "out", dt, 3, q.device)
         if tuple(out.shape) != (B, H, D):
             raise ValueError("out must be [B, H, D]")
+    if validating():
+        _contract_check(_contract.check_decode, _host(block_tables), _host(context_lens),
+                        int(max_context_len), S, N, MB, int(partition_size), _host(work_items),
+                        new_key is not None)
     lib = load()
     opts = DecodeOptions(KERNELS[kernel], PKV_DECODE_CACHED_KV if cached_kv else 0,
                          None if new_key is None else new_key.data_ptr(),
@@ -319,6 +344,9 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens
         raise ValueError("context_lens [B] and query_start [B + 1] must match the tables")
     if work_items is not None:
         _need(work_items, "work_items", torch.int32, 1, q.device)
+    if validating():
+        _contract_check(_contract.check_prefill, _host(block_tables), _host(context_lens),
+                        _host(query_start), int(max_query_len), S, N, T)
     _check(load().pkv_paged_attention_prefill(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), MB,
         _ptr(context_lens), _ptr(query_start), int(max_query_len), _ptr(work_items),
@@ -357,6 +385,8 @@ def copy_blocks(k_caches, v_caches, block_mapping):
     _need(block_mapping, "block_mapping", torch.int64, 2, k0.device)
     if block_mapping.shape[1] != 2:
         raise ValueError("block_mapping must be [M, 2]")
+    if validating():
+        _contract_check(_contract.check_copy_pairs, _host(block_mapping), N)
     nl = len(k_caches)
     karr = (ctypes.c_void_p * nl)(*[k.data_ptr() for k in k_caches])
     varr = (ctypes.c_void_p * nl)(*[v.data_ptr() for v in v_caches])
