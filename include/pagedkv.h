@@ -64,8 +64,7 @@
  * then undefined.
  *
  * Supported shapes: D in {64, 128}; S in {16, 32, 64, 128, 256} (the range of block sizes that
- * item 1-2 of the Qualiteg post calls best: larger blocks bring fragmentation back; prefill:
- * S in {16, 32}); G = H / Hkv in {1, 2, 4, 8, 16} (fp32 and the VALU kernel: G <= 8);
+ * item 1-2 of the Qualiteg post calls best: larger blocks bring fragmentation back); G = H / Hkv in {1, 2, 4, 8, 16} (fp32 and the VALU kernel: G <= 8);
  * partition_size 0 or a positive multiple of S.
  */
 #ifndef PAGEDKV_H
@@ -212,7 +211,8 @@ size_t pkv_partition_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_
  * work_items / num_work_items: NULL (all B * NT units in index order; tiles past Q_i do
  * nothing) or a device int32 list of the units to run in dispatch order (each unit with tokens
  * exactly once; most positions first shortens the tail). fp16/bf16 only; D in {64, 128};
- * S in {16, 32}; G in {1, 2, 4, 8, 16}. Caller contract (not checked): Q_i <= L_i <= MB * S.
+ * S in {16, 32, 64, 128, 256}; G in {1, 2, 4, 8, 16}. Caller contract (not checked):
+ * Q_i <= L_i <= MB * S.
  * Rows are written only for real tokens. */
 pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
                                        const void* v_cache, const int32_t* block_tables,

@@ -288,10 +288,6 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
   const char* fn = "pkv_paged_attention_prefill";
   pkv_status st = check_tile(fn, num_kv_heads, head_dim, block_size, dtype);
   if (st != PKV_OK) return st;
-  // The prefill kernel stages whole [D][S] V^T tiles of a 32-position chunk with 1 KiB loads,
-  // which needs a chunk to span whole blocks.
-  if (block_size > 32)
-    return fail(PKV_ERR_UNSUPPORTED, "%s: block_size %d (supported: 16, 32)", fn, block_size);
   if (dtype == PKV_F32)
     return fail(PKV_ERR_UNSUPPORTED, "%s: fp32 inputs (the matrix-core kernel takes fp16/bf16)", fn);
   if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0 || num_work_items < 0)

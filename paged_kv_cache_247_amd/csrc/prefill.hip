@@ -79,7 +79,9 @@ prefill_kernel(const PrefillParams a) {
   constexpr int NW = kPrefillWaves;
   constexpr int EB = 2;
   constexpr int CT = 32;             // positions per chunk
-  constexpr int BPC = CT / S;        // blocks per chunk
+  constexpr int BPC = S < CT ? CT / S : 1;  // blocks per chunk
+  constexpr int CPK = S > CT ? S / CT : 1;  // chunks per block
+  constexpr int CS = S < CT ? S : CT;       // positions of a chunk in one block
   constexpr int KK = D / 32;         // k-steps of the logits product
   constexpr int NT = D / 16;         // 16-row tiles of the output product
   constexpr int RB = D * EB;         // bytes of one K row
@@ -88,12 +90,15 @@ prefill_kernel(const PrefillParams a) {
   constexpr int VB = CT * D * EB;    // V^T bytes of a chunk
   constexpr int STAGE = KB + VB;
   constexpr int TILE = S * D * EB;   // one (block, kv head) tile of K or V^T
+  // The part of a block's tile one chunk reads: the whole tile up to 32 positions, else 32 K
+  // rows and one 32-position V^T column group (V is stored in groups of min(S, 32)).
+  constexpr int CTILE = CS * D * EB;
   constexpr int NLK = KB / 1024;     // 1 KiB loads per chunk: K, then V^T
   constexpr int NLV = VB / 1024;
   constexpr int LPW = (NLK + NLV) / NW;  // loads per wave per chunk
-  constexpr int PPT = TILE / 1024;   // 1 KiB pieces of a V^T tile
+  constexpr int PPT = CTILE / 1024;  // 1 KiB pieces of a chunk's V^T tile
   static_assert((NLK + NLV) % NW == 0 && NLK % LPW == 0, "loads split evenly over the waves");
-  static_assert(S % (1024 / RB) == 0 && TILE % 1024 == 0, "a 1 KiB load stays within one block");
+  static_assert(S % (1024 / RB) == 0 && CTILE % 1024 == 0, "a 1 KiB load stays within one block");
   using M = PMfma<DT>;
   using V8 = typename M::V8;
   using T = typename Elt<DT>::T;
@@ -180,29 +185,33 @@ prefill_kernel(const PrefillParams a) {
   const size_t id_stride = (size_t)Hkv * TILE;
   const char* kpool = reinterpret_cast<const char*>(a.k_cache) + (size_t)g * TILE;
   const char* vpool = reinterpret_cast<const char*>(a.v_cache) + (size_t)g * TILE;
-  auto rsrc = [&](const char* pool, int id) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(pool + (size_t)id * id_stride), 0,
-                                             TILE, kBufferFlags);
+  // ro: bytes from the block's tile to the chunk's part (nonzero only for blocks over 32; K
+  // rows and V^T groups of a chunk are the same number of bytes in).
+  auto rsrc = [&](const char* pool, int id, int ro) {
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(pool + (size_t)id * id_stride + ro), 0, TILE - ro, kBufferFlags);
   };
   auto rot = [](int t) { return t + 4 * (t >> 4); };
 
   // This wave's share of chunk n's loads into stage st: LPW consecutive 1 KiB pieces, all of
   // K or all of V^T and all of one block (so one block id and one descriptor per chunk).
   // K pieces are rows of the chunk with their 16-byte parts rotated as in decode; V^T pieces
-  // are contiguous 1 KiB of a block's [D][S] tile.
-  static_assert(TILE % (LPW * 1024) == 0, "a wave's loads of a chunk stay within one block");
+  // are contiguous 1 KiB of a block's [D][S] tile (of a [D][32] column group past 32).
+  static_assert(CTILE % (LPW * 1024) == 0, "a wave's loads of a chunk stay within one block");
   const int x0 = wave * LPW;  // first piece: K pieces 0 .. NLK - 1, then V^T pieces
   const bool wave_k = x0 < NLK;
   const int xb = wave_k ? x0 : x0 - NLK;
-  const int wave_blk = xb * 1024 / TILE;  // block of the chunk these pieces come from
+  const int wave_blk = xb * 1024 / CTILE;  // block of the chunk these pieces come from
   auto issue = [&](int n, int st) {
-    if (n * BPC >= 64 * (id_kb + 1)) {
-      id_kb = (n * BPC) / 64;
+    const int lb = BPC == 2 ? n * BPC + wave_blk : n / CPK;  // logical block
+    if (lb >= 64 * (id_kb + 1)) {
+      id_kb = lb / 64;
       id_batch = load_id_batch(id_kb);
     }
     char* dst = smem + st * STAGE + (wave_k ? 0 : KB);
     // (A named descriptor: passed as a temporary, the host pass drops the kernel stub.)
-    const __amdgpu_buffer_rsrc_t rs = rsrc(wave_k ? kpool : vpool, block_id(n * BPC + wave_blk));
+    const __amdgpu_buffer_rsrc_t rs =
+        rsrc(wave_k ? kpool : vpool, block_id(lb), (n % CPK) * CT * RB);
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const int x = xb + j;
@@ -235,12 +244,12 @@ prefill_kernel(const PrefillParams a) {
     }
     // V^T rows d = 16 nt + c: the nt step is a constant, carried in the instruction's offset.
     const char* vp = (S == 16) ? vs + (r >> 1) * TILE + c * (S * EB) + (r & 1) * 16
-                               : vs + c * (S * EB) + r * 16;
+                               : vs + c * (CS * EB) + r * 16;
     const uint32_t vaddr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)vp;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
       asm volatile("ds_read_b128 %0, %1 offset:%2"
-                   : "=v"(vr[nt]) : "v"(vaddr), "i"(16 * nt * S * EB) : "memory");
+                   : "=v"(vr[nt]) : "v"(vaddr), "i"(16 * nt * CS * EB) : "memory");
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi)
@@ -395,6 +404,9 @@ hipError_t launch_d(int block_size, const PrefillParams& p, hipStream_t stream) 
   switch (block_size) {
     case 16: return launch_s<DT, D, 16>(p, stream);
     case 32: return launch_s<DT, D, 32>(p, stream);
+    case 64: return launch_s<DT, D, 64>(p, stream);
+    case 128: return launch_s<DT, D, 128>(p, stream);
+    case 256: return launch_s<DT, D, 256>(p, stream);
     default: return hipErrorNotSupported;
   }
 }

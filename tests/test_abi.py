@@ -166,7 +166,8 @@ def prefill(lib, **kw):
     (dict(dtype=0), UNSUPPORTED),  # fp32
     (dict(D=96), UNSUPPORTED),
     (dict(S=8), UNSUPPORTED),
-    (dict(S=64), UNSUPPORTED),  # decode takes 64..256; prefill stages whole 16/32 blocks
+    (dict(S=48), UNSUPPORTED),
+    (dict(S=512), UNSUPPORTED),
     (dict(H=6, Hkv=4), INVALID),
     (dict(H=64, Hkv=2), UNSUPPORTED),  # group 32
     (dict(q=None), INVALID),

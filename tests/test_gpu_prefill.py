@@ -56,14 +56,20 @@ CASES = [("p1", {}), ("p2", {}), ("p1", {"num_heads": 16}),  # G = 8
          ("p1", {"num_heads": 32}),  # G = 16
          ("p1", {"head_dim": 64, "dtype": "f16"}), ("p1", {"block_size": 32}),
          ("p2", {"block_size": 32, "head_dim": 64}), ("p1", {"query_len": 1}),
-         ("p1", {"query_len": 300})]
+         ("p1", {"query_len": 300}), ("p1", {"block_size": 64}), ("p2", {"block_size": 128}),
+         ("p1", {"block_size": 256, "head_dim": 64, "dtype": "f16"}),
+         ("p2", {"block_size": 256, "num_heads": 16})]
 
 
 @pytest.mark.parametrize("name,over", CASES,
                          ids=[f"{c[0]}-{'-'.join(f'{k}{v}' for k, v in c[1].items()) or 'base'}"
                               for c in CASES])
 def test_prefill_matches_oracle(name, over):
-    wl = W.generate(W.PREFILL_SMALL[name].replace(**over))
+    over = dict(over)
+    cfg = W.PREFILL_SMALL[name]
+    if "block_size" in over:
+        cfg = cfg.with_block_size(over.pop("block_size"))
+    wl = W.generate(cfg.replace(**over))
     got = out_f64(run_prefill(wl))
     _, ref = oracle_prefill(wl)
     err = oracle.max_abs_err(got, ref)
@@ -84,19 +90,21 @@ def test_prefill_work_list_and_permutation_are_bit_identical():
     assert torch.equal(run_prefill(wl).view(torch.uint8), base.view(torch.uint8))
 
 
-def test_prefill_edge_lengths():
+@pytest.mark.parametrize("S", [16, 128])
+def test_prefill_edge_lengths(S):
     """Whole prompts of 1 .. a few hundred positions: one-token prompts, block and chunk
     boundaries, several tiles."""
     lens = np.array([1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 257],
                     dtype=np.int32)
-    cfg = W.PREFILL_SMALL["p2"].replace(num_seqs=len(lens), num_blocks=int(lens.sum() // 16 + 40),
-                                        len_hi=300)
+    cfg = W.PREFILL_SMALL["p2"].replace(
+        num_seqs=len(lens), block_size=S, len_hi=300,
+        num_blocks=int(sum(-(-int(x) // S) for x in lens)) + 8)
     wl = W.generate(cfg, lens=lens)
     got = out_f64(run_prefill(wl))
     _, ref = oracle_prefill(wl)
     assert oracle.max_abs_err(got, ref) <= TOL["bf16"]
     # a one-position prompt is exactly its value row, in every head of the group
-    v0 = wl.v_cache[wl.block_tables[0, 0], :, :, 0]  # [Hkv, D] of position 0
+    v0 = wl.v_cache[wl.block_tables[0, 0], :, :cfg.head_dim, 0]  # [Hkv, D] of position 0
     first = run_prefill(wl).cpu()[0]
     expect = np.repeat(v0, cfg.group, axis=0)
     assert np.array_equal(first.view(torch.int16).numpy().view(np.uint16), expect)
