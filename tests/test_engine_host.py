@@ -72,12 +72,14 @@ def history_ref(eng, tok, rid, p0, cnt):
     S, Hkv, D = eng.S, eng.Hkv, eng.D
     n = p0 + cnt
     nb = -(-n // S)
+    VS = min(S, 32)  # V is stored in column groups of VS positions
     kc = np.zeros((nb, Hkv, S, D), dtype=np.uint16)
-    vc = np.zeros((nb, Hkv, D, S), dtype=np.uint16)
+    vc = np.zeros((nb, Hkv, S // VS * D, VS), dtype=np.uint16)
     for p in range(n):
         _, k, v = tok(rid, p)
         kc[p // S, :, p % S, :] = k
-        vc[p // S, :, :, p % S] = v
+        o = p % S
+        vc[p // S, :, (o // VS) * D:(o // VS + 1) * D, o % VS] = v
     q = np.stack([tok(rid, p)[0] for p in range(p0, n)])
     return oracle.prefill(q, kc, vc, np.arange(nb, dtype=np.int32)[None],
                           np.array([n], np.int32), np.array([0, cnt], np.int32), eng.scale,
@@ -119,7 +121,7 @@ def run_loop(block_size, num_blocks, chunk, prompts, seed):
 
 
 @pytest.mark.parametrize("block_size,num_blocks,chunk", [(16, 20, 0), (32, 9, 0), (16, 20, 24),
-                                                         (32, 9, 40)])
+                                                         (32, 9, 40), (64, 7, 0), (64, 7, 48)])
 def test_loop_keeps_every_sequence_consistent(block_size, num_blocks, chunk):
     st = run_loop(block_size, num_blocks, chunk, [0, 1, 15, 16, 17, 40, 63, 70], 7)
     assert st["swap_outs"] > 0 and st["swap_ins"] == st["swap_outs"] and st["cow_copies"] > 0
