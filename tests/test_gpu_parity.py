@@ -334,11 +334,14 @@ def test_partials_match_oracle(name, kernel, P):
 
 # ------------------------------------------------------------------ full-size workloads
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
-def test_full_size_sampled_against_oracle(name):
-    """The full workload in the launch configuration the benchmark times."""
+@pytest.mark.parametrize("name,P_over", [("c2", None), ("c3", None), ("c4", None), ("c5", None),
+                                         ("c5", 512)])
+def test_full_size_sampled_against_oracle(name, P_over):
+    """The full workload in the launch configuration the benchmark times (and the long-context
+    batch also in the 512-token partitions its statement names)."""
     from bench import LAUNCH
     kernel, P, cached = LAUNCH[name]
+    P = P if P_over is None else P_over
     cfg = W.CONFIGS[name]
     wl = W.generate(cfg)
     dev = upload(wl)
