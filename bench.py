@@ -43,6 +43,8 @@ LAUNCH = {
     "c5": ("auto", 2048, False),
 }
 
+BLOCK_SIZES = (16, 32, 64, 128, 256)  # block sizes the library takes
+
 # Sources the decode kernels are built from (a change to any invalidates counter figures).
 KERNEL_SOURCES = {"mfma": ["decode_mfma.hip", "common.hpp", "kernels.hpp"],
                   "valu": ["decode_valu.hip", "common.hpp", "kernels.hpp"]}
@@ -318,6 +320,10 @@ def main():
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the "
               "path runs on one GPU; --shard runs one GPU's share of a larger job)", file=sys.stderr)
+        sys.exit(2)
+    if args.block_size is not None and args.block_size not in BLOCK_SIZES:
+        print(f"--block-size {args.block_size}: supported block sizes are {BLOCK_SIZES}",
+              file=sys.stderr)
         sys.exit(2)
     if args.config in ("p1", "p2"):
         prefill_main(args)

@@ -1,5 +1,6 @@
 """bench.py's refusals, which happen before any data is generated or any GPU is touched: more
-than one GPU, and shard specifications that do not divide the workload."""
+than one GPU, shard specifications that do not divide the workload, unsupported block
+sizes."""
 from __future__ import annotations
 
 import os
@@ -25,3 +26,9 @@ def test_more_than_one_gpu_is_refused():
 def test_bad_shards_are_refused(spec):
     r = run("--config", "c3", "--shard", spec, "--no-cpu-baseline")
     assert r.returncode == 2 and "--shard" in r.stderr and not r.stdout
+
+
+@pytest.mark.parametrize("S", ["8", "48", "512"])
+def test_unsupported_block_sizes_are_refused(S):
+    r = run("--config", "c3", "--block-size", S, "--no-cpu-baseline")
+    assert r.returncode == 2 and "--block-size" in r.stderr and not r.stdout

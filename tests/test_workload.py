@@ -100,3 +100,26 @@ def test_permute_pool_moves_blocks_consistently():
         for j in range(nb):
             a, b = wl.block_tables[i, j], wp.block_tables[i, j]
             assert np.array_equal(wl.k_cache[a], wp.k_cache[b], equal_nan=True)
+
+
+@pytest.mark.parametrize("S", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
+def test_with_block_size_keeps_the_lengths(name, S):
+    """The same workload in blocks of S: the lengths are drawn first, so they do not change,
+    and the pool holds every sequence's blocks."""
+    base = W.SMALL[name].replace(partition_size=0)
+    if base.prefix_len:  # a prefix every block size divides
+        base = base.replace(prefix_len=256, num_blocks=64)
+    cfg = base.with_block_size(S)
+    assert cfg.block_size == S and cfg.num_blocks * S >= base.num_blocks * base.block_size
+    wl = W.generate(cfg)
+    assert np.array_equal(wl.context_lens, W.generate(base).context_lens)
+    used = -(-wl.context_lens.astype(np.int64) // S)
+    cols = np.arange(wl.block_tables.shape[1])[None, :]
+    live = wl.block_tables[cols < used[:, None]]
+    assert live.min() >= 0 and live.max() < cfg.num_blocks
+
+
+def test_with_block_size_refuses_a_prefix_it_does_not_divide():
+    with pytest.raises(ValueError):
+        W.SMALL["c4"].replace(prefix_len=48).with_block_size(32)
