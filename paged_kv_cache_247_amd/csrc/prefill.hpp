@@ -18,7 +18,7 @@ struct PrefillParams {
   void* out;                  // [T, H, D]
   const void* q;              // [T, H, D]
   const void* k_cache;        // [N, Hkv, S, D]
-  const void* v_cache;        // [N, Hkv, D, S]
+  const void* v_cache;        // [N, Hkv, (S / VS) D, VS], VS = min(S, 32)
   const int32_t* block_tables;  // [B, MB]
   const int32_t* context_lens;  // [B]
   const int32_t* query_start;   // [B + 1]
