@@ -164,6 +164,30 @@ pkv_status pkv_paged_attention_decode_ex(
     pkv_dtype dtype, int32_t partition_size, float* max_logits, float* exp_sums,
     float* tmp_out, void* stream);
 
+/* Partition 0 of sequences that share its blocks, one pass over each shared tile for the
+ * whole group. Requests that share a prompt prefix share its KV blocks (Hacker News discussion
+ * of PagedAttention, replies on prefix sharing); grouped-query attention already reuses a
+ * loaded tile for the G query heads of its kv head (vAttention section 3.1 names GQA), and
+ * this reuses it across the sequences as well: the matrix-core product's 16 columns hold
+ * G heads of each of up to 16 / G members.
+ * groups: device int32 [num_groups][4], 16-byte aligned; row u lists the sequences of group u,
+ * -1 for none; entries past min(4, 16 / G) are ignored. Writes max_logits, exp_sums and
+ * tmp_out of partition 0 (positions 0 .. partition_size - 1) of every member, exactly as
+ * pkv_paged_attention_decode in split-context mode would; the caller then decodes the
+ * members' other partitions (a work list of units i * NP + p with p >= 1) and merges with
+ * pkv_paged_attention_reduce. fp16/bf16; other arguments as for pkv_paged_attention_decode.
+ * Caller contract (not checked; PKV_VALIDATE=1 in the Python binding checks it): a sequence is
+ * in at most one group; every member has L_i >= partition_size and the same block ids in
+ * table entries 0 .. partition_size / S - 1 (the first member's table row and length are the
+ * ones read). */
+pkv_status pkv_paged_attention_decode_shared(
+    const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* groups,
+    int32_t num_groups, int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    pkv_dtype dtype, int32_t partition_size, float* max_logits, float* exp_sums,
+    float* tmp_out, void* stream);
+
 /* Merge split-context partitions: for each (i, h) with n = ceil(L_i / partition_size)
  * partitions, M = max_p max_logits, w_p = exp_sums_p * exp(max_logits_p - M),
  * out = sum_p w_p tmp_out_p / sum_p w_p (a zero row when n = 0). The merge is an exact

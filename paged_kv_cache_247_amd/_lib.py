@@ -39,6 +39,8 @@ SIGNATURES = {
                                         _I, _I, _F, _I, _I, _P, _P, _P, _P]),
     "pkv_paged_attention_decode_ex": (_I, [_OPT, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I,
                                            _I, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P]),
+    "pkv_paged_attention_decode_shared": (_I, [_P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I,
+                                               _I, _I, _I, _F, _I, _I, _P, _P, _P, _P]),
     "pkv_paged_attention_reduce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pkv_copy_blocks": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pkv_partition_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
@@ -312,6 +314,42 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         _stream(q)))
 
 
+def paged_attention_decode_shared(q, k_cache, v_cache, block_tables, context_lens, groups,
+                                  max_context_len, scale, partition_size, workspace):
+    """pkv_paged_attention_decode_shared: partition 0 of every member of each group of
+    sequences sharing its blocks (groups: device int32 [num_groups, 4], -1 pads), into
+    `workspace` = (max_logits, exp_sums, tmp_out) as split-context decode would write it."""
+    _need(q, "q", ndim=3)
+    dt = q.dtype
+    B, H, D = q.shape
+    _need(k_cache, "k_cache", dt, 4, q.device)
+    N, Hkv, S, Dk = k_cache.shape
+    if Dk != D:
+        raise ValueError("head_dim of q and k_cache differ")
+    _need(v_cache, "v_cache", dt, 4, q.device)
+    if tuple(v_cache.shape) != (N, *v_block_shape(Hkv, D, S)):
+        raise ValueError(f"v_cache must be {(N, *v_block_shape(Hkv, D, S))}")
+    _need(block_tables, "block_tables", torch.int32, 2, q.device)
+    MB = block_tables.shape[1]
+    _need(context_lens, "context_lens", torch.int32, 1, q.device)
+    _need(groups, "groups", torch.int32, 2, q.device)
+    if groups.shape[1] != 4 or block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("groups must be [num_groups, 4]; tables and lengths one row per sequence")
+    ml, es, to = workspace
+    NP = num_partitions(max_context_len, partition_size)
+    for t, shp in ((ml, (B, H, NP)), (es, (B, H, NP)), (to, (B, H, NP, D))):
+        _need(t, "workspace", torch.float32, len(shp), q.device)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"workspace part must be {shp}, got {tuple(t.shape)}")
+    if validating():
+        _contract_check(_contract.check_groups, _host(groups), _host(block_tables),
+                        _host(context_lens), int(partition_size), S, N, H // Hkv)
+    _check(load().pkv_paged_attention_decode_shared(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), MB, _ptr(context_lens),
+        _ptr(groups), groups.shape[0], int(max_context_len), B, H, Hkv, D, S, N, float(scale),
+        _dt(q), int(partition_size), _ptr(ml), _ptr(es), _ptr(to), _stream(q)))
+
+
 def prefill_tile_tokens(num_heads: int, num_kv_heads: int) -> int:
     """Query tokens per prefill work unit (pkv_prefill_tile_tokens)."""
     return load().pkv_prefill_tile_tokens(num_heads, num_kv_heads)
@@ -433,6 +471,26 @@ def paged_attention(out, q, k_cache, v_cache, block_tables, context_lens, max_co
     else:
         paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
                                max_context_len, scale, 0, None, **kw)
+    return out
+
+
+def paged_attention_shared(out, q, k_cache, v_cache, block_tables, context_lens,
+                           max_context_len, scale, groups, work_items, partition_size,
+                           workspace=None, new_key=None, new_value=None):
+    """A decode step over shared prefix blocks (see sharing.plan, which gives groups,
+    work_items and partition_size): partition 0 of the grouped sequences in one pass per
+    group, every other unit through split-context decode (with the fused newest-token write,
+    if rows are given), then the merge; on the current stream."""
+    B, H, D = q.shape
+    if workspace is None:
+        workspace = partition_workspace(B, H, D, max_context_len, partition_size, q.device)
+    paged_attention_decode_shared(q, k_cache, v_cache, block_tables, context_lens, groups,
+                                  max_context_len, scale, partition_size, workspace)
+    paged_attention_decode(None, q, k_cache, v_cache, block_tables, context_lens,
+                           max_context_len, scale, partition_size, workspace,
+                           work_items=work_items, cached_kv=True, new_key=new_key,
+                           new_value=new_value)
+    paged_attention_reduce(out, workspace, context_lens, partition_size)
     return out
 
 

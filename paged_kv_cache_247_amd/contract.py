@@ -117,6 +117,40 @@ def check_copy_pairs(block_mapping, num_blocks: int):
         _fail(f"block {int(both[0])} is both a source and a destination")
 
 
+def check_groups(groups, block_tables, context_lens, partition_size: int, block_size: int,
+                 num_blocks: int, group: int):
+    """Groups for the shared-prefix decode: [n, 4] sequence ids, -1 pads; the first entry of a
+    row is a sequence; a sequence in at most one group; every member's context covers the
+    shared partition and its table agrees with the first member's over it."""
+    gm = np.asarray(groups).astype(np.int64).reshape(-1, 4)
+    L = np.asarray(context_lens).astype(np.int64)
+    tables = np.asarray(block_tables).astype(np.int64)
+    B, P, S = len(L), int(partition_size), int(block_size)
+    width = max(1, min(4, 16 // max(int(group), 1)))
+    used = gm[:, :width]
+    if len(gm) and (gm[:, 0] < 0).any():
+        _fail(f"group {int(np.argmax(gm[:, 0] < 0))} has no first member")
+    if ((used < -1) | (used >= B)).any():
+        _fail("a group names a sequence outside the batch")
+    live = used[used >= 0]
+    u, counts = np.unique(live, return_counts=True)
+    if (counts > 1).any():
+        _fail(f"sequence {int(u[np.argmax(counts)])} is in more than one group")
+    nb = P // S
+    for k, row in enumerate(used.tolist()):
+        members = [m for m in row if m >= 0]
+        for m in members:
+            if L[m] < P:
+                _fail(f"group {k}: sequence {m} has {int(L[m])} positions, fewer than the "
+                      f"shared partition's {P}")
+            if not np.array_equal(tables[m, :nb], tables[members[0], :nb]):
+                _fail(f"group {k}: sequence {m}'s table differs from sequence {members[0]}'s "
+                      f"within the shared partition")
+        ids = tables[members[0], :nb]
+        if len(ids) and (ids.min() < 0 or ids.max() >= num_blocks):
+            _fail(f"group {k}: a shared table entry is not a pool block")
+
+
 def check_prefill(block_tables, context_lens, query_start, max_query_len: int, block_size: int,
                   num_blocks: int, num_tokens: int):
     L = np.asarray(context_lens).astype(np.int64)

@@ -75,8 +75,9 @@ pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, 
                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                        int32_t num_blocks, float scale, pkv_dtype dtype,
                        int32_t partition_size, float* max_logits, float* exp_sums,
-                       float* tmp_out, void* stream) {
-  const char* fn = "pkv_paged_attention_decode";
+                       float* tmp_out, void* stream, const int32_t* groups = nullptr,
+                       int32_t num_groups = 0) {
+  const char* fn = groups ? "pkv_paged_attention_decode_shared" : "pkv_paged_attention_decode";
   pkv_status st = check_tile(fn, num_kv_heads, head_dim, block_size, dtype);
   if (st != PKV_OK) return st;
   if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARGUMENT, "%s: num_seqs %d", fn, num_seqs);
@@ -132,11 +133,20 @@ pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, 
     return fail(PKV_ERR_UNSUPPORTED, "%s: the VALU kernel takes query groups up to 8", fn);
   if (!mfma && !block_tables)
     return fail(PKV_ERR_UNSUPPORTED, "%s: the table-free contiguous layout runs on the MFMA kernel only", fn);
+  if (groups) {
+    if (!partial || !block_tables || work_items || opt->new_key || !mfma)
+      return fail(PKV_ERR_INVALID_ARGUMENT, "%s: groups take partitions, block tables, no work "
+                  "list, no new rows and the MFMA kernel", fn);
+    if (num_groups < 0 || !aligned(groups, 16))
+      return fail(PKV_ERR_INVALID_ARGUMENT, "%s: groups pointer misaligned or num_groups %d", fn,
+                  num_groups);
+  }
 
   const int64_t ranges = partial ? ((int64_t)max_context_len + partition_size - 1) / partition_size : 1;
   if (work_items && num_work_items < 0)
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: num_work_items %d", fn, num_work_items);
-  const int64_t units = work_items ? (int64_t)num_work_items : (int64_t)num_seqs * ranges;
+  const int64_t units = groups ? (int64_t)num_groups
+                       : work_items ? (int64_t)num_work_items : (int64_t)num_seqs * ranges;
   if ((int64_t)num_seqs * ranges > INT32_MAX)
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: %lld units", fn, (long long)num_seqs * ranges);
   const int64_t grid = units * num_kv_heads;  // the MFMA kernel pads units to a multiple of 8
@@ -152,6 +162,7 @@ pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, 
   p.block_tables = block_tables;
   p.context_lens = context_lens;
   p.work_items = work_items;
+  p.group_members = groups;
   p.num_units = (int32_t)units;
   p.new_key = opt->new_key;
   p.new_value = opt->new_value;
@@ -232,6 +243,21 @@ pkv_status pkv_paged_attention_decode_ex(
                      num_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
                      partition_size, max_logits, exp_sums, tmp_out, stream);
+}
+
+pkv_status pkv_paged_attention_decode_shared(
+    const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* groups,
+    int32_t num_groups, int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    pkv_dtype dtype, int32_t partition_size, float* max_logits, float* exp_sums,
+    float* tmp_out, void* stream) {
+  static const pkv_decode_options mfma = {PKV_KERNEL_MFMA, 0u, nullptr, nullptr};
+  return decode_impl(&mfma, nullptr, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
+                     block_tables, max_blocks_per_seq, context_lens, nullptr, 0,
+                     max_context_len, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, scale, dtype, partition_size, max_logits, exp_sums, tmp_out,
+                     stream, groups, num_groups);
 }
 
 pkv_status pkv_paged_attention_reduce(void* out, const float* max_logits,

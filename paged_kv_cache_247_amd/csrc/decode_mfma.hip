@@ -71,9 +71,13 @@ __device__ __forceinline__ void wait_vm_le() {
 constexpr int kXcds = 8;  // XCDs of the MI355X, which take workgroups round robin
 constexpr int kBufferFlags = 0x00020000;
 
-template <Dt DT, int D, int S, int NW, bool PARTIAL, bool NTL, bool TBL>
+// GRP: a unit is a group of sequences whose block tables agree over the first range (a shared
+// prefix); column c of the products is head c % G of member c / G, so each shared tile is read
+// once for every member, and the range's partial state is written for each member.
+template <Dt DT, int D, int S, int NW, bool PARTIAL, bool NTL, bool TBL, bool GRP = false>
 __global__ void __launch_bounds__(NW * 64)
 decode_mfma_kernel(const DecodeParams a) {
+  static_assert(!GRP || (PARTIAL && TBL), "groups write partials through block tables");
   static_assert(DT == Dt::BF16 || DT == Dt::F16, "16-bit inputs only");
   constexpr int EB = 2;
   constexpr int CT = 32;        // positions per chunk
@@ -124,9 +128,14 @@ decode_mfma_kernel(const DecodeParams a) {
     slot = w / Hkv;
   }
   int unit = a.work_items ? a.work_items[slot] : slot;
-  unit = min(max(unit, 0), a.num_seqs * a.num_ranges - 1);
-  const int part = unit % a.num_ranges;
-  const int i = unit / a.num_ranges;
+  unit = min(max(unit, 0), (GRP ? a.num_units : a.num_seqs * a.num_ranges) - 1);
+  const int part = GRP ? 0 : unit % a.num_ranges;
+  // GRP: the first member's table row and length stand for the group's (they agree over the
+  // range by the caller's contract).
+  const int i = GRP ? min(max(a.group_members[4 * unit], 0), a.num_seqs - 1)
+                    : unit / a.num_ranges;
+  // Columns in use: the G heads, or G heads of each of up to 16 / G group members.
+  const int ncol = GRP ? 16 : G;
   const int lane = lane_id();
   const int wave = wave_id();
   const int r = lane >> 4;
@@ -171,15 +180,27 @@ decode_mfma_kernel(const DecodeParams a) {
   const int nch = max(end - start + CT - 1, 0) / CT;
   const int blk_end = (end + S - 1) / S;  // first logical block past the cached range
 
-  // q columns: lane (r, c) holds head c (zero beyond the group) at d = 32 kk + 8r .. +8.
+  // q columns: lane (r, c) holds head c (zero beyond the group) at d = 32 kk + 8r .. +8; in
+  // GRP mode head c % G of member c / G (zero where the group has no such member).
+  auto column_seq = [&](int col) {
+    if constexpr (GRP) {
+      const int s = col / G;
+      const int m = s < 4 ? a.group_members[4 * unit + s] : -1;
+      return m < a.num_seqs ? m : -1;
+    } else {
+      return col < G ? i : -1;
+    }
+  };
   V8 qb[KK];
   {
+    const int qs = column_seq(c);
     const char* qp = reinterpret_cast<const char*>(a.q) +
-                     (((size_t)i * H + (size_t)g * G + c) * D + 8 * r) * EB;
+                     (((size_t)max(qs, 0) * H + (size_t)g * G + (GRP ? c % G : c)) * D +
+                      8 * r) * EB;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (c < G) v = *reinterpret_cast<const u32x4*>(qp + kk * 64);
+      if (qs >= 0) v = *reinterpret_cast<const u32x4*>(qp + kk * 64);
       qb[kk] = __builtin_bit_cast(V8, v);
     }
   }
@@ -461,7 +482,7 @@ decode_mfma_kernel(const DecodeParams a) {
   l = across32(l, OpAdd());
 
   __syncthreads();  // every wave is done with its staging slots: the merge buffers reuse them
-  if (c < G) {
+  if (c < ncol) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -473,9 +494,11 @@ decode_mfma_kernel(const DecodeParams a) {
   }
   __syncthreads();
 
-  for (int e = threadIdx.x; e < G * D; e += NW * 64) {
-    const int h = e / D;
+  for (int e = threadIdx.x; e < ncol * D; e += NW * 64) {
+    const int h = e / D;  // column
     const int d = e % D;
+    const int seq = GRP ? column_seq(h) : i;
+    if (GRP && seq < 0) continue;
     float Mx = fused ? sh_new[h] : -INFINITY;
 #pragma unroll
     for (int v = 0; v < NW; ++v) Mx = fmaxf(Mx, sh_m[v][h]);
@@ -492,7 +515,7 @@ decode_mfma_kernel(const DecodeParams a) {
       den += f;
     }
     const float o = num / den;
-    const size_t row = (size_t)i * H + (size_t)g * G + h;
+    const size_t row = (size_t)seq * H + (size_t)g * G + (GRP ? h % G : h);
     if constexpr (PARTIAL) {
       const size_t rec = row * a.num_ranges + part;
       a.tmp_out[rec * D + d] = o;
@@ -520,8 +543,19 @@ hipError_t launch_p(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Groups sharing a prefix: partials, cached loads (a shared tile is read by every group of
+// the XCD its kv head maps to), one workgroup per (group, kv head).
+template <Dt DT, int D, int S>
+hipError_t launch_grouped(const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)p.num_units * (unsigned)p.num_kv_heads);
+  decode_mfma_kernel<DT, D, S, kMfmaWaves, true, false, true, true>
+      <<<grid, dim3(kMfmaWaves * 64), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
 template <Dt DT, int D, int S>
 hipError_t launch_s(bool partial, bool nt, const DecodeParams& p, hipStream_t stream) {
+  if (p.group_members) return partial ? launch_grouped<DT, D, S>(p, stream) : hipErrorNotSupported;
   if (partial) return nt ? launch_p<DT, D, S, true, true>(p, stream) : launch_p<DT, D, S, true, false>(p, stream);
   return nt ? launch_p<DT, D, S, false, true>(p, stream) : launch_p<DT, D, S, false, false>(p, stream);
 }

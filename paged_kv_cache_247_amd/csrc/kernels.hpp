@@ -19,6 +19,9 @@ struct DecodeParams {
   const int32_t* block_tables;
   const int32_t* context_lens;
   const int32_t* work_items;  // NULL = all units in index order; else unit = i * num_ranges + p
+  // NULL, or [num_units][4] sequences (-1 = none) sharing the blocks of range 0: each unit is
+  // such a group (MFMA kernel, partials only), written to partition 0 of every member
+  const int32_t* group_members;
   const void* new_key;        // NULL, or [B, Hkv, D]: position L-1 of each sequence, fused write
   const void* new_value;
   float* max_logits;

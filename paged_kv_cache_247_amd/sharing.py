@@ -1,0 +1,89 @@
+"""Host planning of a decode step over shared prefix blocks.
+
+Requests that share a prompt prefix share its KV blocks (Hacker News discussion of
+PagedAttention, replies on prefix sharing), so their block tables agree over the prefix. A
+decode step can then read each shared tile once for several sequences
+(pkv_paged_attention_decode_shared, up to 16 / G sequences per group) instead of once per
+sequence. The step becomes three launches over split-context partitions of P positions, with
+P a multiple of the block size inside the shared prefix:
+
+  1. partition 0 of every grouped sequence, one pass per group;
+  2. every other unit (i, p) with positions -- p >= 1 of grouped sequences, all partitions of
+     the others -- through pkv_paged_attention_decode, largest first;
+  3. the merge of the partitions (pkv_paged_attention_reduce).
+
+The result is the same attention (the merge is an exact rewriting of the softmax sum); only
+the order of the fp32 additions differs from a single pass.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+
+def common_prefix_blocks(block_tables: np.ndarray, context_lens: np.ndarray,
+                         block_size: int) -> int:
+    """Leading table entries that every sequence with a non-empty context holds in common
+    (entries wholly inside its context only)."""
+    L = np.asarray(context_lens).astype(np.int64)
+    rows = np.asarray(block_tables)[L > 0]
+    if not len(rows):
+        return 0
+    full = int((L[L > 0] // block_size).min())  # entries every sequence fills completely
+    same = np.all(rows[:, :full] == rows[:1, :full], axis=0)
+    return int(full if same.all() else np.argmin(same))
+
+
+@dataclasses.dataclass
+class SharedPlan:
+    partition_size: int       # P
+    num_partitions: int       # NP = ceil(max_context_len / P)
+    groups: np.ndarray        # int32 [num_groups, 4], -1 pads
+    work_items: np.ndarray    # int32 units i * NP + p for launch 2, largest first
+
+
+def plan(block_tables: np.ndarray, context_lens: np.ndarray, block_size: int,
+         max_context_len: int, group_size: int, prefix_blocks: int | None = None,
+         newest_outside: bool = True) -> SharedPlan | None:
+    """Groups of up to `group_size` (<= 4, and G * group_size <= 16) sequences whose tables
+    agree over the first prefix_blocks entries (default: the whole batch's common prefix).
+    A sequence joins a group only if its context reaches past the prefix (past it by one more
+    position when the step also writes the newest token: that token must not fall in the
+    shared partition). None if no two sequences can share."""
+    S = int(block_size)
+    L = np.asarray(context_lens).astype(np.int64)
+    tables = np.asarray(block_tables)
+    nb = common_prefix_blocks(tables, L, S) if prefix_blocks is None else int(prefix_blocks)
+    if nb <= 0:
+        return None
+    P = nb * S
+    need = P + (1 if newest_outside else 0)
+    eligible = np.flatnonzero(L >= need)
+    classes: dict[bytes, list[int]] = {}
+    for i in eligible.tolist():
+        classes.setdefault(tables[i, :nb].tobytes(), []).append(i)
+    width = max(1, min(4, int(group_size)))
+    groups = []
+    for members in classes.values():
+        if len(members) < 2:
+            continue
+        for k in range(0, len(members), width):
+            chunk = members[k:k + width]
+            groups.append(chunk + [-1] * (4 - len(chunk)))
+    if not groups:
+        return None
+    groups = np.asarray(groups, dtype=np.int32).reshape(-1, 4)
+    NP = -(-int(max_context_len) // P)
+    grouped = np.zeros(len(L), dtype=bool)
+    grouped[groups[groups >= 0]] = True
+    units, sizes = [], []
+    for i in range(len(L)):
+        for p in range(1 if grouped[i] else 0, NP):
+            n = min(P, int(L[i]) - p * P)
+            if n > 0:  # an empty context needs no unit: the merge writes zeros for it
+                units.append(i * NP + p)
+                sizes.append(n)
+    order = np.argsort(-np.asarray(sizes, dtype=np.int64), kind="stable")
+    items = np.asarray(units, dtype=np.int32)[order] if units else np.zeros(0, np.int32)
+    return SharedPlan(P, NP, groups, items)

@@ -1,0 +1,75 @@
+"""Host planning of a decode step over shared prefix blocks (CPU): the groups share their
+tables over the shared partition, and the grouped partition 0 plus the work list cover every
+unit with positions exactly once."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from paged_kv_cache_247_amd import contract as C
+from paged_kv_cache_247_amd import sharing
+from paged_kv_cache_247_amd import workload as W
+
+
+def _units(wl, P):
+    NP = -(-wl.max_context_len // P)
+    return {i * NP + p for i, L in enumerate(wl.context_lens.tolist())
+            for p in range(NP) if p * P < L}
+
+
+@pytest.mark.parametrize("heads,width", [(8, 4), (16, 2), (4, 4)])
+def test_plan_on_the_prefix_workload(heads, width):
+    cfg = W.SMALL["c4"].replace(num_heads=heads)
+    wl = W.generate(cfg)
+    S = cfg.block_size
+    plan = sharing.plan(wl.block_tables, wl.context_lens, S, wl.max_context_len, width)
+    # copy-on-write gives some sequences a private last prefix block: the shared part is
+    # the blocks before it
+    assert plan.partition_size == (cfg.prefix_len // S - 1) * S
+    g = plan.groups
+    assert g.shape[1] == 4 and ((g >= 0).sum(axis=1) <= width).all()
+    C.check_groups(g, wl.block_tables, wl.context_lens, plan.partition_size, S,
+                   cfg.num_blocks, cfg.group)
+    members = g[g >= 0]
+    assert len(members) == len(set(members.tolist())) == cfg.num_seqs
+    covered = {int(m) * plan.num_partitions for m in members}
+    items = set(plan.work_items.tolist())
+    assert len(items) == len(plan.work_items) and not covered & items
+    assert covered | items == _units(wl, plan.partition_size)
+    sizes = [min(plan.partition_size,
+                 int(wl.context_lens[u // plan.num_partitions])
+                 - (u % plan.num_partitions) * plan.partition_size) for u in plan.work_items]
+    assert sizes == sorted(sizes, reverse=True)
+
+
+def test_no_plan_without_shared_blocks():
+    wl = W.generate(W.SMALL["c3"])
+    assert sharing.plan(wl.block_tables, wl.context_lens, 16, wl.max_context_len, 4) is None
+
+
+def test_common_prefix_blocks():
+    t = np.array([[5, 6, 7, 8], [5, 6, 9, 1], [5, 6, 7, 2]], np.int32)
+    assert sharing.common_prefix_blocks(t, np.array([64, 64, 64]), 16) == 2
+    assert sharing.common_prefix_blocks(t, np.array([20, 64, 64]), 16) == 1  # one full block
+    assert sharing.common_prefix_blocks(t[[0, 2]], np.array([48, 64]), 16) == 3
+
+
+def test_group_contract_violations():
+    wl = W.generate(W.SMALL["c4"])
+    S, N = 16, wl.cfg.num_blocks
+    plan = sharing.plan(wl.block_tables, wl.context_lens, S, wl.max_context_len, 4)
+    P = plan.partition_size
+    ok = plan.groups
+
+    def bad(groups=ok, tables=wl.block_tables, lens=wl.context_lens):
+        with pytest.raises(C.ContractError):
+            C.check_groups(groups, tables, lens, P, S, N, 4)
+
+    g = ok.copy(); g[1, 0] = g[0, 1]
+    bad(groups=g)                                    # a sequence in two groups
+    g = ok.copy(); g[0, 0] = -1
+    bad(groups=g)                                    # no first member
+    t = wl.block_tables.copy(); t[ok[0, 1], 0] = t[ok[0, 1], 0] + 1
+    bad(tables=t)                                    # a member's table differs
+    L = wl.context_lens.copy(); L[ok[0, 2]] = P - 1
+    bad(lens=L)                                      # too short for the shared partition
