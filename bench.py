@@ -72,6 +72,9 @@ def parse():
                     help="repetitions of back-to-back launch timing per kernel")
     ap.add_argument("--launches", type=int, default=100,
                     help="back-to-back launches per repetition")
+    ap.add_argument("--shared-prefix", default="auto", choices=["auto", "on", "off"],
+                    help="decode blocks that sequences share once per group of sequences "
+                         "(auto: when the batch shares a prefix and runs single pass)")
     ap.add_argument("--block-size", type=int, default=None,
                     help="run the workload in blocks of this many positions (16..256); the "
                          "pool keeps at least its capacity")
@@ -170,9 +173,10 @@ def cpu_baseline(wl, one_s: float, all_s: float, workers: int):
 
 # ------------------------------------------------------------------ GPU helpers
 
-def counter_traffic(kernel_sources, workload):
+def counter_traffic(kernel_sources, workload, shared=False):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary, if the summary
-    was taken on the kernel sources as they are now (else None)."""
+    was taken on the kernel sources as they are now and in the same decode mode (the grouped
+    shared-prefix launches or not), else None."""
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(root, "profiles", f"decode_{workload}_counters.txt")
@@ -187,6 +191,8 @@ def counter_traffic(kernel_sources, workload):
     for src in kernel_sources:
         h.update(open(os.path.join(root, "paged_kv_cache_247_amd", "csrc", src), "rb").read())
     if vals.get("source_sha256") != h.hexdigest():
+        return None
+    if int(vals.get("shared_prefix", "0")) != int(bool(shared)):
         return None
     return int(float(vals["traffic_bytes_per_launch"]))
 
@@ -384,17 +390,37 @@ def main():
     key, value = dev(wl.key, bf), dev(wl.value, bf)
     slots, bt, lens = dev(wl.slot_mapping), dev(wl.block_tables), dev(wl.context_lens)
     mapping = dev(wl.block_mapping.reshape(-1, 2))
-    # Host-side scheduler input: the units with work, largest first.
-    order = dev(wl.work_items(P))
+    fused = not args.unfused
+    # Blocks shared by several sequences (a common prefix): plan groups that read each shared
+    # tile once for all their members (host scheduler input, like the work list).
+    plan = None
+    if args.shared_prefix == "on" or (args.shared_prefix == "auto" and cfg.prefix_len and not P):
+        from paged_kv_cache_247_amd import sharing
+        plan = sharing.plan(wl.block_tables, wl.context_lens, cfg.block_size,
+                            wl.max_context_len, max(1, 16 // cfg.group), newest_outside=fused)
+        if plan is None and args.shared_prefix == "on":
+            print("--shared-prefix on: no blocks are shared", file=sys.stderr)
+            sys.exit(2)
+    if plan is not None:
+        P, kernel, cached = plan.partition_size, "mfma", True
+        groups = dev(plan.groups)
+        order = dev(plan.work_items)
+    else:
+        # Host-side scheduler input: the units with work, largest first.
+        order = dev(wl.work_items(P))
     out = torch.empty((cfg.num_seqs, cfg.num_heads, cfg.head_dim), dtype=dt, device="cuda")
     ws = pk.partition_workspace(cfg.num_seqs, cfg.num_heads, cfg.head_dim, wl.max_context_len,
                                 P, q.device) if P else None
     maxlen = wl.max_context_len
     has_copy = len(wl.block_mapping) > 0
-    fused = not args.unfused
     ev = []
 
+    def decode_shared():
+        pk.paged_attention_decode_shared(q, kc, vc, bt, lens, groups, maxlen, cfg.scale, P, ws)
+
     def decode():
+        if plan is not None:
+            decode_shared()
         # With fused=True the decode launch also writes each sequence's newest K/V to its slot.
         pk.paged_attention_decode(None if P else out, q, kc, vc, bt, lens, maxlen, cfg.scale,
                                   P, ws, kernel=kernel, work_items=order, cached_kv=cached,
@@ -430,6 +456,10 @@ def main():
     kernels = {"paged_attention_decode": dict(
         launch_stats(torch, decode, args.launches, args.reps),
         kv_bytes=wl.kv_bytes())}
+    if plan is not None:  # the grouped launch alone (part of the decode above)
+        kernels["paged_attention_decode_shared"] = dict(
+            launch_stats(torch, decode_shared, args.launches, args.reps),
+            groups=len(plan.groups), partition_size=P)
     kernels["reshape_and_cache"] = dict(
         launch_stats(torch, lambda: pk.reshape_and_cache(key, value, kc, vc, slots),
                      args.launches, args.reps),
@@ -472,7 +502,7 @@ def main():
                                              and cfg.group >= 4)) else "valu"
     # The recorded counters belong to the workload as defined (its block size, whole batch).
     traffic = None if shard or cfg.block_size != W.CONFIGS[name].block_size \
-        else counter_traffic(KERNEL_SOURCES[family], name)
+        else counter_traffic(KERNEL_SOURCES[family], name, plan is not None)
     value = kvb / (ms_step * 1e-3) / 1e9
     ukvb = wl.unique_kv_bytes() if has_copy else kvb
     # With shared prefix blocks the logical bytes count the prefix once per sequence, but it is
@@ -497,6 +527,9 @@ def main():
                    "num_blocks": cfg.num_blocks, "seed": cfg.seed,
                    "context_tokens": wl.total_tokens, "max_context_len": maxlen,
                    "kernel": kernel, "partition_size": P, "cached_kv": cached,
+                   "shared_prefix": None if plan is None else {
+                       "groups": len(plan.groups), "partition_size": P,
+                       "members": int((plan.groups >= 0).sum())},
                    "fused_cache_write": fused, "kv_bytes": kvb,
                    "unique_kv_bytes": ukvb, "shard": shard},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
@@ -504,7 +537,9 @@ def main():
         "head_token_pairs_per_s": round(cfg.num_heads * wl.total_tokens / (ms_step * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": f"paged_attention_decode ({family})",
+                     "traffic": traffic,
+                     "kernel": ("paged_attention_decode_shared + " if plan is not None else "")
+                               + f"paged_attention_decode ({family})",
                      "ms_per_launch": round(dec_ms, 5), "bytes_per_launch": ukvb,
                      "logical_GB_per_s": round(kvb / (dec_ms * 1e-3) / 1e9, 2)},
         "kernels": kernels,

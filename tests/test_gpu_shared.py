@@ -99,3 +99,4 @@ def test_full_size_sampled_against_oracle():
     seqs = sorted({0, 63, 64, 255, *np.random.default_rng(0).choice(c.num_seqs, 4, replace=False)})
     err = oracle.max_abs_err(out[seqs], oracle_out(wl, seqs))
     assert err <= TOL[c.dtype], f"max abs err {err}"
+
