@@ -140,6 +140,7 @@ pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, 
     if (num_groups < 0 || !aligned(groups, 16))
       return fail(PKV_ERR_INVALID_ARGUMENT, "%s: groups pointer misaligned or num_groups %d", fn,
                   num_groups);
+    if (num_seqs == 0) return PKV_OK;  // no member can be named: nothing to write
   }
 
   const int64_t ranges = partial ? ((int64_t)max_context_len + partition_size - 1) / partition_size : 1;

@@ -134,6 +134,30 @@ def test_reduce_and_copy_validation(lib):
     assert c(None, arr, 2, A16, 3, 8, 128, 16, 64, 2, None) == INVALID
 
 
+def shared(lib, **kw):
+    a = dict(q=A16, k=A16, v=A16, bt=A16, MB=4, lens=A16, groups=A16, ng=2, maxlen=64, B=8,
+             H=8, Hkv=2, D=128, S=16, N=32, scale=0.125, dtype=2, P=32, ml=A16, es=A16, to=A16)
+    a.update(kw)
+    return lib.pkv_paged_attention_decode_shared(
+        a["q"], a["k"], a["v"], a["bt"], a["MB"], a["lens"], a["groups"], a["ng"], a["maxlen"],
+        a["B"], a["H"], a["Hkv"], a["D"], a["S"], a["N"], a["scale"], a["dtype"], a["P"],
+        a["ml"], a["es"], a["to"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=0, ml=None, es=None, to=None), INVALID),  # groups write partitions
+    (dict(bt=None), INVALID),                          # through block tables
+    (dict(groups=A16 + 4), INVALID),
+    (dict(ng=-1), INVALID),
+    (dict(dtype=0), UNSUPPORTED),                      # the matrix-core kernel: fp16/bf16
+    (dict(P=24), INVALID),                             # not a multiple of the block size
+    (dict(ng=0), OK),                                  # nothing to do, nothing enqueued
+    (dict(B=0), OK),
+])
+def test_decode_shared_validation(lib, kw, status):
+    assert shared(lib, **kw) == status
+
+
 def test_vmm_pool_validation(lib):
     """The virtual-memory pool rejects bad arguments before any HIP call; NULL pools are inert."""
     h = ctypes.c_void_p()
