@@ -154,6 +154,9 @@ pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, 
   if ((units + 7) / 8 * 8 * num_kv_heads > INT32_MAX)
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: grid of %lld workgroups", fn, (long long)grid);
   if (grid == 0) return PKV_OK;
+  // No (sequence, range) unit exists (no sequences, or split mode with no positions): nothing
+  // to write, and a work list could name none -- the kernels clamp work items into that range.
+  if (!groups && (int64_t)num_seqs * ranges == 0) return PKV_OK;
 
   pkv::DecodeParams p;
   p.out = out;

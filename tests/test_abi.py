@@ -98,6 +98,8 @@ def decode(lib, **kw):
     (dict(nk=A16), INVALID),  # new_key without new_value
     (dict(nk=A16, nv=A16 + 8), INVALID),  # misaligned new_value
     (dict(B=0), OK),  # nothing to do, nothing enqueued
+    (dict(B=0, order=A16, nitems=3), OK),  # a work list but no sequence to name
+    (dict(maxlen=0, P=32, out=None, ml=A16, es=A16, to=A16, order=A16, nitems=2), OK),
     (dict(bt=None, N=7), INVALID),  # table-free: the pool must hold B * MB blocks
     (dict(bt=None, kernel=1), UNSUPPORTED),  # table-free runs on the MFMA kernel only
     (dict(bt=None, kernel=2, B=0), OK),
