@@ -128,6 +128,7 @@ class OutOfBlocks(PagedKVError):
     """PKV_ERR_NO_BLOCKS: the block manager has too few free blocks (nothing was changed)."""
 
 
+PKV_ERR_HIP = 3
 PKV_ERR_NO_BLOCKS = 4
 
 
@@ -136,6 +137,13 @@ def _check(status: int):
         lib = load()
         cls = OutOfBlocks if status == PKV_ERR_NO_BLOCKS else PagedKVError
         raise cls(status, lib.pkv_last_error_message().decode())
+    if os.environ.get("PKV_SYNC", "0") not in ("", "0") and torch.cuda.is_available():
+        # Debugging: wait for the call's work so an asynchronous error is reported here, by
+        # the call that caused it, rather than at some later synchronization.
+        try:
+            torch.cuda.synchronize()
+        except RuntimeError as e:
+            raise PagedKVError(PKV_ERR_HIP, f"after the call: {e}") from None
 
 
 def _stream(t: torch.Tensor):
