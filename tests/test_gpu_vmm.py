@@ -54,7 +54,7 @@ def _decode(pool, dev, wc, P=0, fused=True, kernel="mfma"):
 
 
 CASES = [("c3", {}, (0, 64)), ("c3", {"block_size": 32}, (0,)), ("c5", {}, (64, 0)),
-         ("c3", {"head_dim": 64, "dtype": "f16"}, (0,))]
+         ("c3", {"head_dim": 64, "dtype": "f16"}, (0,)), ("c3", {"block_size": 128}, (0, 128))]
 
 
 @pytest.mark.parametrize("name,over,parts", CASES,
