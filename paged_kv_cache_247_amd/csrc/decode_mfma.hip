@@ -151,8 +151,9 @@ decode_mfma_kernel(const DecodeParams a) {
   // or 32 positions), or rows (n % CPK) CT .. + CT of logical block start / S + n / CPK (larger
   // blocks). The wave keeps the ids of CPB consecutive local chunks in one register, lane
   // BPC (m % CPB) + e holding block e of local chunk m, and picks them out with readlane. One
-  // coalesced vector load fills it every CPB chunks. (The block table cannot be read through the scalar cache inside the loop: the
-  // direct-to-LDS loads count as writes to unknown memory, which rules scalar loads out.)
+  // coalesced vector load fills it every CPB chunks. (The block table cannot be read through
+  // the scalar cache inside the loop: the direct-to-LDS loads count as writes to unknown
+  // memory, which rules scalar loads out.)
   // The first batch is loaded now, in parallel with the context length; any entry of the row
   // may be read and ids are clamped into the pool before use.
   constexpr int CPB = 64 / BPC;

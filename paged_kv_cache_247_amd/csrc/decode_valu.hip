@@ -51,9 +51,21 @@ decode_valu_kernel(const DecodeParams a) {
   const int Hkv = a.num_kv_heads;
   const int H = a.num_heads;
   const int MB = a.max_blocks_per_seq;
+  // Workgroups go to the XCDs round robin (w % 8). Unshared KV (non-temporal loads): every kv
+  // head of a unit on one XCD (groups of 8 Hkv workgroups hold 8 units, head g of the group's
+  // unit j at 8 g + j), so an XCD streams whole blocks of its sequences. Cached loads (shared
+  // prefix blocks): head g of every unit on XCD g % 8, so a shared tile stays in one L2.
   const int w = blockIdx.x;
-  const int g = w % Hkv;  // consecutive workgroups take different kv heads (XCD round robin)
-  const int slot = w / Hkv;
+  int g, slot;
+  if constexpr (NTL) {
+    constexpr int XC = 8;
+    g = (w % (XC * Hkv)) / XC;
+    slot = (w / (XC * Hkv)) * XC + w % XC;
+    if (slot >= a.num_units) return;  // the grid is padded to whole groups of 8 units
+  } else {
+    g = w % Hkv;
+    slot = w / Hkv;
+  }
   int unit = a.work_items ? a.work_items[slot] : slot;
   unit = min(max(unit, 0), a.num_seqs * a.num_ranges - 1);
   const int part = unit % a.num_ranges;
@@ -337,7 +349,8 @@ constexpr int kValuWaves = 4;
 
 template <Dt DT, int D, int S, int G>
 hipError_t launch_g(bool partial, bool nt, const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)p.num_units * p.num_kv_heads);
+  const unsigned units = nt ? (p.num_units + 7) / 8 * 8 : p.num_units;
+  const dim3 grid(units * (unsigned)p.num_kv_heads);
   const dim3 block(kValuWaves * 64);
   if (partial) {
     if (nt) decode_valu_kernel<DT, D, S, G, kValuWaves, true, true><<<grid, block, 0, stream>>>(p);
