@@ -397,7 +397,7 @@ def main():
     if args.shared_prefix == "on" or (args.shared_prefix == "auto" and cfg.prefix_len and not P):
         from paged_kv_cache_247_amd import sharing
         plan = sharing.plan(wl.block_tables, wl.context_lens, cfg.block_size,
-                            wl.max_context_len, max(1, 16 // cfg.group), newest_outside=fused)
+                            wl.max_context_len, cfg.group, newest_outside=fused)
         if plan is None and args.shared_prefix == "on":
             print("--shared-prefix on: no blocks are shared", file=sys.stderr)
             sys.exit(2)

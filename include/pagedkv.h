@@ -171,7 +171,8 @@ pkv_status pkv_paged_attention_decode_ex(
  * this reuses it across the sequences as well: the matrix-core product's 16 columns hold
  * G heads of each of up to 16 / G members.
  * groups: device int32 [num_groups][4], 16-byte aligned; row u lists the sequences of group u,
- * -1 for none; entries past min(4, 16 / G) are ignored. Writes max_logits, exp_sums and
+ * -1 for none; entries past min(4, 16 / G) must be -1 (the kernel does not read them, so a
+ * sequence listed there would get no partition 0). Writes max_logits, exp_sums and
  * tmp_out of partition 0 (positions 0 .. partition_size - 1) of every member, exactly as
  * pkv_paged_attention_decode in split-context mode would; the caller then decodes the
  * members' other partitions (a work list of units i * NP + p with p >= 1) and merges with

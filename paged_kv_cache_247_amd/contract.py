@@ -130,6 +130,8 @@ def check_groups(groups, block_tables, context_lens, partition_size: int, block_
     used = gm[:, :width]
     if len(gm) and (gm[:, 0] < 0).any():
         _fail(f"group {int(np.argmax(gm[:, 0] < 0))} has no first member")
+    if (gm[:, width:] != -1).any():
+        _fail(f"a group lists more than {width} sequences (16 columns over {group} heads)")
     if ((used < -1) | (used >= B)).any():
         _fail("a group names a sequence outside the batch")
     live = used[used >= 0]

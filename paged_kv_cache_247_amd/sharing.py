@@ -43,11 +43,18 @@ class SharedPlan:
     work_items: np.ndarray    # int32 units i * NP + p for launch 2, largest first
 
 
+def group_width(group: int) -> int:
+    """Sequences per group for a query group of G heads: the 16 product columns hold G heads
+    of each member (at most 4 members, the width of a group row)."""
+    return max(1, min(4, 16 // max(int(group), 1)))
+
+
 def plan(block_tables: np.ndarray, context_lens: np.ndarray, block_size: int,
-         max_context_len: int, group_size: int, prefix_blocks: int | None = None,
-         newest_outside: bool = True) -> SharedPlan | None:
-    """Groups of up to `group_size` (<= 4, and G * group_size <= 16) sequences whose tables
-    agree over the first prefix_blocks entries (default: the whole batch's common prefix).
+         max_context_len: int, group: int, max_members: int | None = None,
+         prefix_blocks: int | None = None, newest_outside: bool = True) -> SharedPlan | None:
+    """Groups of up to group_width(group) sequences (fewer if max_members says so), G = group
+    query heads per kv head, whose tables agree over the first prefix_blocks entries (default:
+    the whole batch's common prefix).
     A sequence joins a group only if its context reaches past the prefix (past it by one more
     position when the step also writes the newest token: that token must not fall in the
     shared partition). None if no two sequences can share."""
@@ -63,7 +70,9 @@ def plan(block_tables: np.ndarray, context_lens: np.ndarray, block_size: int,
     classes: dict[bytes, list[int]] = {}
     for i in eligible.tolist():
         classes.setdefault(tables[i, :nb].tobytes(), []).append(i)
-    width = max(1, min(4, int(group_size)))
+    width = group_width(group)
+    if max_members is not None:
+        width = max(1, min(width, int(max_members)))
     groups = []
     for members in classes.values():
         if len(members) < 2:

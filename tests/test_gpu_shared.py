@@ -52,7 +52,7 @@ def test_shared_step_matches_oracle(over, width):
     wl = W.generate(W.SMALL["c4"].replace(**over))
     c = wl.cfg
     plan = sharing.plan(wl.block_tables, wl.context_lens, c.block_size, wl.max_context_len,
-                        width)
+                        c.group, max_members=width)
     assert plan is not None and len(plan.groups)
     out, d = shared_step(wl, plan)
     kc, vc = oracle_pools(wl)
@@ -66,7 +66,8 @@ def test_grouped_partials_match_the_oracle():
     """Partition 0 of every grouped sequence: max logit, exp sum and partial output."""
     wl = W.generate(W.SMALL["c4"])
     c = wl.cfg
-    plan = sharing.plan(wl.block_tables, wl.context_lens, c.block_size, wl.max_context_len, 4)
+    plan = sharing.plan(wl.block_tables, wl.context_lens, c.block_size, wl.max_context_len,
+                        c.group)
     P = plan.partition_size
     ws = pk.partition_workspace(c.num_seqs, c.num_heads, c.head_dim, wl.max_context_len, P,
                                 torch.device("cuda"))
@@ -93,7 +94,7 @@ def test_full_size_sampled_against_oracle():
     wl = W.generate(W.CONFIGS["c4"])
     c = wl.cfg
     plan = sharing.plan(wl.block_tables, wl.context_lens, c.block_size, wl.max_context_len,
-                        16 // c.group)
+                        c.group)
     out = out_f64(shared_step(wl, plan)[0])
     assert np.isfinite(out).all()
     seqs = sorted({0, 63, 64, 255, *np.random.default_rng(0).choice(c.num_seqs, 4, replace=False)})

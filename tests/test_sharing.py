@@ -22,7 +22,8 @@ def test_plan_on_the_prefix_workload(heads, width):
     cfg = W.SMALL["c4"].replace(num_heads=heads)
     wl = W.generate(cfg)
     S = cfg.block_size
-    plan = sharing.plan(wl.block_tables, wl.context_lens, S, wl.max_context_len, width)
+    assert sharing.group_width(cfg.group) == width
+    plan = sharing.plan(wl.block_tables, wl.context_lens, S, wl.max_context_len, cfg.group)
     # copy-on-write gives some sequences a private last prefix block: the shared part is
     # the blocks before it
     assert plan.partition_size == (cfg.prefix_len // S - 1) * S
@@ -45,6 +46,7 @@ def test_plan_on_the_prefix_workload(heads, width):
 def test_no_plan_without_shared_blocks():
     wl = W.generate(W.SMALL["c3"])
     assert sharing.plan(wl.block_tables, wl.context_lens, 16, wl.max_context_len, 4) is None
+    assert sharing.group_width(16) == 1 and sharing.group_width(1) == 4
 
 
 def test_common_prefix_blocks():
@@ -69,6 +71,8 @@ def test_group_contract_violations():
     bad(groups=g)                                    # a sequence in two groups
     g = ok.copy(); g[0, 0] = -1
     bad(groups=g)                                    # no first member
+    with pytest.raises(C.ContractError):             # more members than 16 / G columns hold
+        C.check_groups(ok, wl.block_tables, wl.context_lens, P, S, N, 8)
     t = wl.block_tables.copy(); t[ok[0, 1], 0] = t[ok[0, 1], 0] + 1
     bad(tables=t)                                    # a member's table differs
     L = wl.context_lens.copy(); L[ok[0, 2]] = P - 1
