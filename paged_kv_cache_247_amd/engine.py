@@ -29,6 +29,7 @@ import numpy as np
 import torch
 
 from . import _lib as L
+from . import sharing
 from .workload import cast_from_f32
 
 _TORCH = {"bf16": torch.bfloat16, "f16": torch.float16}
@@ -48,13 +49,17 @@ class Request:
 class DecodeEngine:
     def __init__(self, num_blocks: int, num_host_blocks: int, num_heads: int, num_kv_heads: int,
                  head_dim: int, block_size: int, max_blocks_per_seq: int, dtype: str = "bf16",
-                 seed: int = 0, prefill_chunk: int = 0, device="cuda", ops=None):
+                 seed: int = 0, prefill_chunk: int = 0, device="cuda", ops=None,
+                 share_prefixes: bool = False):
         """ops: the kernel entry points (reshape_and_cache, copy_blocks, swap_blocks,
-        paged_attention, paged_attention_prefill); the HIP library by default. The block
-        manager is always the library's."""
+        paged_attention, paged_attention_prefill, paged_attention_shared); the HIP library by
+        default. The block manager is always the library's. share_prefixes: decode sequences
+        whose tables share leading blocks (forks) through shared-prefix groups, which read a
+        shared tile once per group (sharing.plan)."""
         self.H, self.Hkv, self.D, self.S = num_heads, num_kv_heads, head_dim, block_size
         self.MB, self.dtype, self.seed = max_blocks_per_seq, dtype, seed
         self.chunk = prefill_chunk
+        self.share = share_prefixes
         self.scale = 1.0 / float(np.sqrt(head_dim))
         self.ops = ops if ops is not None else L
         self.device = torch.device(device)
@@ -74,7 +79,7 @@ class DecodeEngine:
         self.swapped: deque[int] = deque()
         self.finished: list[int] = []
         self.stats = {"steps": 0, "swap_outs": 0, "swap_ins": 0, "cow_copies": 0,
-                      "admitted": 0, "prefill_chunks": 0, "short_chunks": 0}
+                      "admitted": 0, "prefill_chunks": 0, "short_chunks": 0, "shared_groups": 0}
 
     # ------------------------------------------------------------ synthetic tokens
     def _stream_owner(self, rid: int, pos: int) -> int:
@@ -243,10 +248,21 @@ class DecodeEngine:
             toks = [self.token(r, int(n) - 1) for r, n in zip(dec, lens)]
             out = torch.empty((len(dec), self.H, self.D), dtype=_TORCH[self.dtype],
                               device=self.device)
-            self.ops.paged_attention(out, self._dev(np.stack([x[0] for x in toks])), self.k, self.v,
-                              self._dev(t), self._dev(lens), int(lens.max()), self.scale, 0,
-                              new_key=self._dev(np.stack([x[1] for x in toks])),
-                              new_value=self._dev(np.stack([x[2] for x in toks])))
+            q = self._dev(np.stack([x[0] for x in toks]))
+            nk = self._dev(np.stack([x[1] for x in toks]))
+            nv = self._dev(np.stack([x[2] for x in toks]))
+            plan = (sharing.plan(t, lens, self.S, int(lens.max()), self.H // self.Hkv)
+                    if self.share else None)
+            if plan is not None:
+                self.ops.paged_attention_shared(
+                    out, q, self.k, self.v, self._dev(t), self._dev(lens), int(lens.max()),
+                    self.scale, self._dev(plan.groups), self._dev(plan.work_items),
+                    plan.partition_size, new_key=nk, new_value=nv)
+                self.stats["shared_groups"] += len(plan.groups)
+            else:
+                self.ops.paged_attention(out, q, self.k, self.v, self._dev(t), self._dev(lens),
+                                         int(lens.max()), self.scale, 0, new_key=nk,
+                                         new_value=nv)
             res["decode"] = {r: (k, int(n) - 1) for k, (r, n) in enumerate(zip(dec, lens))}
             res["decode_out"] = out
             # 5. finish

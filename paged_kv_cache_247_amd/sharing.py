@@ -35,6 +35,32 @@ def common_prefix_blocks(block_tables: np.ndarray, context_lens: np.ndarray,
     return int(full if same.all() else np.argmin(same))
 
 
+def _classes(tables: np.ndarray, L: np.ndarray, nb: int, need: int) -> list[list[int]]:
+    """Sequences with at least `need` positions, grouped by their first nb table entries."""
+    classes: dict[bytes, list[int]] = {}
+    for i in np.flatnonzero(L >= need).tolist():
+        classes.setdefault(tables[i, :nb].tobytes(), []).append(i)
+    return [m for m in classes.values() if len(m) >= 2]
+
+
+def best_prefix_blocks(block_tables: np.ndarray, context_lens: np.ndarray, block_size: int,
+                       width: int, newest_outside: bool = True) -> int:
+    """The shared partition length (in blocks) that saves the most tile reads: for nb blocks,
+    each class of sequences agreeing over nb entries reads them once per group of `width`
+    instead of once per sequence. 0 if no two sequences share a block."""
+    S = int(block_size)
+    L = np.asarray(context_lens).astype(np.int64)
+    tables = np.asarray(block_tables)
+    top = int((L // S).max()) if len(L) else 0
+    best, gain = 0, 0
+    for nb in range(1, top + 1):
+        g = sum((len(m) - -(-len(m) // width)) * nb
+                for m in _classes(tables, L, nb, nb * S + (1 if newest_outside else 0)))
+        if g > gain:
+            best, gain = nb, g
+    return best
+
+
 @dataclasses.dataclass
 class SharedPlan:
     partition_size: int       # P
@@ -54,29 +80,23 @@ def plan(block_tables: np.ndarray, context_lens: np.ndarray, block_size: int,
          prefix_blocks: int | None = None, newest_outside: bool = True) -> SharedPlan | None:
     """Groups of up to group_width(group) sequences (fewer if max_members says so), G = group
     query heads per kv head, whose tables agree over the first prefix_blocks entries (default:
-    the whole batch's common prefix).
+    the length that saves the most tile reads, see best_prefix_blocks).
     A sequence joins a group only if its context reaches past the prefix (past it by one more
     position when the step also writes the newest token: that token must not fall in the
     shared partition). None if no two sequences can share."""
     S = int(block_size)
     L = np.asarray(context_lens).astype(np.int64)
     tables = np.asarray(block_tables)
-    nb = common_prefix_blocks(tables, L, S) if prefix_blocks is None else int(prefix_blocks)
-    if nb <= 0:
-        return None
-    P = nb * S
-    need = P + (1 if newest_outside else 0)
-    eligible = np.flatnonzero(L >= need)
-    classes: dict[bytes, list[int]] = {}
-    for i in eligible.tolist():
-        classes.setdefault(tables[i, :nb].tobytes(), []).append(i)
     width = group_width(group)
     if max_members is not None:
         width = max(1, min(width, int(max_members)))
+    nb = (best_prefix_blocks(tables, L, S, width, newest_outside) if prefix_blocks is None
+          else int(prefix_blocks))
+    if nb <= 0:
+        return None
+    P = nb * S
     groups = []
-    for members in classes.values():
-        if len(members) < 2:
-            continue
+    for members in _classes(tables, L, nb, P + (1 if newest_outside else 0)):
         for k in range(0, len(members), width):
             chunk = members[k:k + width]
             groups.append(chunk + [-1] * (4 - len(chunk)))

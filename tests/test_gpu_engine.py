@@ -57,18 +57,19 @@ def expected_chunk(eng, tok, rid, p0, cnt):
                           np.array([0, cnt], np.int32), eng.scale, eng.Hkv, eng.dtype)
 
 
-@pytest.mark.parametrize("block_size,num_blocks,chunk",
-                         [(16, 24, 0), (32, 13, 0), (16, 24, 24), (32, 13, 40), (64, 7, 0),
-                          (64, 7, 48)],
+@pytest.mark.parametrize("block_size,num_blocks,chunk,share",
+                         [(16, 24, 0, False), (32, 13, 0, False), (16, 24, 24, False),
+                          (32, 13, 40, False), (64, 7, 0, False), (64, 7, 48, False),
+                          (16, 24, 0, True), (32, 20, 24, True)],
                          ids=["S16", "S32", "S16-chunked-prefill", "S32-chunked-prefill", "S64",
-                              "S64-chunked-prefill"])
-def test_live_loop_matches_oracle(block_size, num_blocks, chunk):
+                              "S64-chunked-prefill", "S16-shared-prefix", "S32-shared-prefix"])
+def test_live_loop_matches_oracle(block_size, num_blocks, chunk, share):
     from paged_kv_cache_247_amd.engine import DecodeEngine
 
     rng = np.random.default_rng(block_size)
     eng = DecodeEngine(num_blocks=num_blocks, num_host_blocks=96, num_heads=8, num_kv_heads=2,
                        head_dim=128, block_size=block_size, max_blocks_per_seq=12, seed=5,
-                       prefill_chunk=chunk)
+                       prefill_chunk=chunk, share_prefixes=share)
     tok = functools.lru_cache(maxsize=None)(eng.token)
     prompts = [0, 1, 15, 16, 17, 40, 63, 70]
     for rid, P in enumerate(prompts):
@@ -112,6 +113,8 @@ def test_live_loop_matches_oracle(block_size, num_blocks, chunk):
         if chunk and r.origin < 0:
             assert prefilled[rid] == list(range(r.prompt_len)), rid
     st = eng.stats
+    if share:  # forks decoded through shared-prefix groups
+        assert st["shared_groups"] > 0
     assert st["swap_outs"] > 0 and st["swap_ins"] == st["swap_outs"] and st["cow_copies"] > 0
     if chunk:
         assert st["prefill_chunks"] > len(prompts)  # some prompt took more than one chunk
