@@ -155,8 +155,9 @@ pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, 
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: grid of %lld workgroups", fn, (long long)grid);
   if (grid == 0) return PKV_OK;
   // No (sequence, range) unit exists (no sequences, or split mode with no positions): nothing
-  // to write, and a work list could name none -- the kernels clamp work items into that range.
-  if (!groups && (int64_t)num_seqs * ranges == 0) return PKV_OK;
+  // to write, and a work list could name none -- the kernels clamp work items into that range
+  // (and groups would have no partition record to write).
+  if ((int64_t)num_seqs * ranges == 0) return PKV_OK;
 
   pkv::DecodeParams p;
   p.out = out;

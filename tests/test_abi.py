@@ -155,6 +155,7 @@ def shared(lib, **kw):
     (dict(P=24), INVALID),                             # not a multiple of the block size
     (dict(ng=0), OK),                                  # nothing to do, nothing enqueued
     (dict(B=0), OK),
+    (dict(maxlen=0), OK),                              # no partition to write
 ])
 def test_decode_shared_validation(lib, kw, status):
     assert shared(lib, **kw) == status
