@@ -415,13 +415,14 @@ def main():
     has_copy = len(wl.block_mapping) > 0
     ev = []
 
-    def decode_shared():
-        pk.paged_attention_decode_shared(q, kc, vc, bt, lens, groups, maxlen, cfg.scale, P, ws)
-
     def decode():
-        if plan is not None:
-            decode_shared()
         # With fused=True the decode launch also writes each sequence's newest K/V to its slot.
+        if plan is not None:  # the groups and every other unit in one launch
+            pk.paged_attention_decode_shared(q, kc, vc, bt, lens, groups, maxlen, cfg.scale, P,
+                                             ws, work_items=order,
+                                             new_key=key if fused else None,
+                                             new_value=value if fused else None)
+            return
         pk.paged_attention_decode(None if P else out, q, kc, vc, bt, lens, maxlen, cfg.scale,
                                   P, ws, kernel=kernel, work_items=order, cached_kv=cached,
                                   new_key=key if fused else None,
@@ -456,10 +457,6 @@ def main():
     kernels = {"paged_attention_decode": dict(
         launch_stats(torch, decode, args.launches, args.reps),
         kv_bytes=wl.kv_bytes())}
-    if plan is not None:  # the grouped launch alone (part of the decode above)
-        kernels["paged_attention_decode_shared"] = dict(
-            launch_stats(torch, decode_shared, args.launches, args.reps),
-            groups=len(plan.groups), partition_size=P)
     kernels["reshape_and_cache"] = dict(
         launch_stats(torch, lambda: pk.reshape_and_cache(key, value, kc, vc, slots),
                      args.launches, args.reps),
@@ -538,8 +535,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": ("paged_attention_decode_shared + " if plan is not None else "")
-                               + f"paged_attention_decode ({family})",
+                     "kernel": ("paged_attention_decode_shared (mfma: groups and other units)"
+                                if plan is not None else f"paged_attention_decode ({family})"),
                      "ms_per_launch": round(dec_ms, 5), "bytes_per_launch": ukvb,
                      "logical_GB_per_s": round(kvb / (dec_ms * 1e-3) / 1e9, 2)},
         "kernels": kernels,

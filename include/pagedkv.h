@@ -174,20 +174,27 @@ pkv_status pkv_paged_attention_decode_ex(
  * -1 for none; entries past min(4, 16 / G) must be -1 (the kernel does not read them, so a
  * sequence listed there would get no partition 0). Writes max_logits, exp_sums and
  * tmp_out of partition 0 (positions 0 .. partition_size - 1) of every member, exactly as
- * pkv_paged_attention_decode in split-context mode would; the caller then decodes the
- * members' other partitions (a work list of units i * NP + p with p >= 1) and merges with
- * pkv_paged_attention_reduce. fp16/bf16; other arguments as for pkv_paged_attention_decode.
+ * pkv_paged_attention_decode in split-context mode would. The step's other units (the
+ * members' partitions p >= 1 and every partition of the other sequences) can run in the same
+ * launch: work_items (device int32 [num_work_items], units i * NP + p, or NULL with
+ * num_work_items 0) lists them, and new_key/new_value (both NULL or both set; only with a
+ * work list) give the fused newest-position write, all exactly as pkv_paged_attention_decode
+ * with partitions, PKV_DECODE_CACHED_KV and those options would run them. The caller then
+ * merges with pkv_paged_attention_reduce. k_cache and v_cache are written only by the fused
+ * write. fp16/bf16; other arguments as for pkv_paged_attention_decode.
  * Caller contract (not checked; PKV_VALIDATE=1 in the Python binding checks it): a sequence is
- * in at most one group; every member has L_i >= partition_size and the same block ids in
- * table entries 0 .. partition_size / S - 1 (the first member's table row and length are the
- * ones read). */
+ * in at most one group; every member has L_i >= partition_size (L_i > partition_size with new
+ * rows) and the same block ids in table entries 0 .. partition_size / S - 1 (the first
+ * member's table row and length are the ones read); no listed unit is partition 0 of a
+ * member, and the work list holds no unit twice. */
 pkv_status pkv_paged_attention_decode_shared(
-    const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+    const void* q, void* k_cache, void* v_cache, const int32_t* block_tables,
     int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* groups,
-    int32_t num_groups, int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
-    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
-    pkv_dtype dtype, int32_t partition_size, float* max_logits, float* exp_sums,
-    float* tmp_out, void* stream);
+    int32_t num_groups, const int32_t* work_items, int32_t num_work_items,
+    const void* new_key, const void* new_value, int32_t max_context_len, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, float scale, pkv_dtype dtype, int32_t partition_size,
+    float* max_logits, float* exp_sums, float* tmp_out, void* stream);
 
 /* Merge split-context partitions: for each (i, h) with n = ceil(L_i / partition_size)
  * partitions, M = max_p max_logits, w_p = exp_sums_p * exp(max_logits_p - M),

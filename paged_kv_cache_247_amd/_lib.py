@@ -39,8 +39,9 @@ SIGNATURES = {
                                         _I, _I, _F, _I, _I, _P, _P, _P, _P]),
     "pkv_paged_attention_decode_ex": (_I, [_OPT, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I,
                                            _I, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P, _P]),
-    "pkv_paged_attention_decode_shared": (_I, [_P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I,
-                                               _I, _I, _I, _F, _I, _I, _P, _P, _P, _P]),
+    "pkv_paged_attention_decode_shared": (_I, [_P, _P, _P, _P, _I, _P, _P, _I, _P, _I, _P, _P,
+                                               _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P,
+                                               _P, _P]),
     "pkv_paged_attention_reduce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pkv_copy_blocks": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pkv_partition_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
@@ -323,10 +324,14 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
 
 
 def paged_attention_decode_shared(q, k_cache, v_cache, block_tables, context_lens, groups,
-                                  max_context_len, scale, partition_size, workspace):
+                                  max_context_len, scale, partition_size, workspace,
+                                  work_items=None, new_key=None, new_value=None):
     """pkv_paged_attention_decode_shared: partition 0 of every member of each group of
     sequences sharing its blocks (groups: device int32 [num_groups, 4], -1 pads), into
-    `workspace` = (max_logits, exp_sums, tmp_out) as split-context decode would write it."""
+    `workspace` = (max_logits, exp_sums, tmp_out) as split-context decode would write it; in
+    the same launch the units of `work_items` (device int32, units i * NP + p), with the fused
+    newest-position write when new_key/new_value [B, Hkv, D] are given, as
+    paged_attention_decode(..., work_items=work_items, cached_kv=True) would run them."""
     _need(q, "q", ndim=3)
     dt = q.dtype
     B, H, D = q.shape
@@ -349,13 +354,32 @@ def paged_attention_decode_shared(q, k_cache, v_cache, block_tables, context_len
         _need(t, "workspace", torch.float32, len(shp), q.device)
         if tuple(t.shape) != shp:
             raise ValueError(f"workspace part must be {shp}, got {tuple(t.shape)}")
+    if work_items is not None:
+        _need(work_items, "work_items", torch.int32, 1, q.device)
+    if (new_key is None) != (new_value is None):
+        raise ValueError("new_key and new_value go together")
+    if new_key is not None:
+        if work_items is None:
+            raise ValueError("new rows are written by the listed units: give work_items")
+        for t, nm in ((new_key, "new_key"), (new_value, "new_value")):
+            _need(t, nm, dt, 3, q.device)
+            if tuple(t.shape) != (B, Hkv, D):
+                raise ValueError(f"{nm} must be {(B, Hkv, D)}")
     if validating():
+        listed = None if work_items is None else _host(work_items)
+        if listed is not None:
+            _contract_check(_contract.check_decode, _host(block_tables), _host(context_lens),
+                            int(max_context_len), S, N, MB, int(partition_size), listed,
+                            new_key is not None)
         _contract_check(_contract.check_groups, _host(groups), _host(block_tables),
-                        _host(context_lens), int(partition_size), S, N, H // Hkv)
+                        _host(context_lens), int(partition_size), S, N, H // Hkv,
+                        work_items=listed, num_partitions=NP, fused_write=new_key is not None)
+    nw = 0 if work_items is None else work_items.shape[0]
     _check(load().pkv_paged_attention_decode_shared(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), MB, _ptr(context_lens),
-        _ptr(groups), groups.shape[0], int(max_context_len), B, H, Hkv, D, S, N, float(scale),
-        _dt(q), int(partition_size), _ptr(ml), _ptr(es), _ptr(to), _stream(q)))
+        _ptr(groups), groups.shape[0], _ptr(work_items), nw, _ptr(new_key), _ptr(new_value),
+        int(max_context_len), B, H, Hkv, D, S, N, float(scale), _dt(q), int(partition_size),
+        _ptr(ml), _ptr(es), _ptr(to), _stream(q)))
 
 
 def prefill_tile_tokens(num_heads: int, num_kv_heads: int) -> int:
@@ -486,18 +510,15 @@ def paged_attention_shared(out, q, k_cache, v_cache, block_tables, context_lens,
                            max_context_len, scale, groups, work_items, partition_size,
                            workspace=None, new_key=None, new_value=None):
     """A decode step over shared prefix blocks (see sharing.plan, which gives groups,
-    work_items and partition_size): partition 0 of the grouped sequences in one pass per
-    group, every other unit through split-context decode (with the fused newest-token write,
-    if rows are given), then the merge; on the current stream."""
+    work_items and partition_size): one launch runs partition 0 of the grouped sequences in
+    one pass per group beside every other unit of split-context decode (with the fused
+    newest-token write, if rows are given), then the merge; on the current stream."""
     B, H, D = q.shape
     if workspace is None:
         workspace = partition_workspace(B, H, D, max_context_len, partition_size, q.device)
     paged_attention_decode_shared(q, k_cache, v_cache, block_tables, context_lens, groups,
-                                  max_context_len, scale, partition_size, workspace)
-    paged_attention_decode(None, q, k_cache, v_cache, block_tables, context_lens,
-                           max_context_len, scale, partition_size, workspace,
-                           work_items=work_items, cached_kv=True, new_key=new_key,
-                           new_value=new_value)
+                                  max_context_len, scale, partition_size, workspace,
+                                  work_items=work_items, new_key=new_key, new_value=new_value)
     paged_attention_reduce(out, workspace, context_lens, partition_size)
     return out
 

@@ -118,10 +118,13 @@ def check_copy_pairs(block_mapping, num_blocks: int):
 
 
 def check_groups(groups, block_tables, context_lens, partition_size: int, block_size: int,
-                 num_blocks: int, group: int):
+                 num_blocks: int, group: int, work_items=None, num_partitions: int = 1,
+                 fused_write: bool = False):
     """Groups for the shared-prefix decode: [n, 4] sequence ids, -1 pads; the first entry of a
     row is a sequence; a sequence in at most one group; every member's context covers the
-    shared partition and its table agrees with the first member's over it."""
+    shared partition (reaches past it with the fused newest-position write) and its table
+    agrees with the first member's over it; a work list run in the same launch (units
+    i * num_partitions + p) holds no member's partition 0."""
     gm = np.asarray(groups).astype(np.int64).reshape(-1, 4)
     L = np.asarray(context_lens).astype(np.int64)
     tables = np.asarray(block_tables).astype(np.int64)
@@ -139,18 +142,24 @@ def check_groups(groups, block_tables, context_lens, partition_size: int, block_
     if (counts > 1).any():
         _fail(f"sequence {int(u[np.argmax(counts)])} is in more than one group")
     nb = P // S
+    need = P + (1 if fused_write else 0)
     for k, row in enumerate(used.tolist()):
         members = [m for m in row if m >= 0]
         for m in members:
-            if L[m] < P:
-                _fail(f"group {k}: sequence {m} has {int(L[m])} positions, fewer than the "
-                      f"shared partition's {P}")
+            if L[m] < need:
+                _fail(f"group {k}: sequence {m} has {int(L[m])} positions, the shared "
+                      f"partition needs {need}")
             if not np.array_equal(tables[m, :nb], tables[members[0], :nb]):
                 _fail(f"group {k}: sequence {m}'s table differs from sequence {members[0]}'s "
                       f"within the shared partition")
         ids = tables[members[0], :nb]
         if len(ids) and (ids.min() < 0 or ids.max() >= num_blocks):
             _fail(f"group {k}: a shared table entry is not a pool block")
+    if work_items is not None and len(live):
+        first = np.asarray(work_items).astype(np.int64)
+        both = np.intersect1d(first, live * max(int(num_partitions), 1))
+        if len(both):
+            _fail(f"work item {int(both[0])} is partition 0 of a grouped sequence")
 
 
 def check_prefill(block_tables, context_lens, query_start, max_query_len: int, block_size: int,

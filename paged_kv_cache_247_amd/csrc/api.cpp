@@ -134,9 +134,9 @@ pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, 
   if (!mfma && !block_tables)
     return fail(PKV_ERR_UNSUPPORTED, "%s: the table-free contiguous layout runs on the MFMA kernel only", fn);
   if (groups) {
-    if (!partial || !block_tables || work_items || opt->new_key || !mfma)
-      return fail(PKV_ERR_INVALID_ARGUMENT, "%s: groups take partitions, block tables, no work "
-                  "list, no new rows and the MFMA kernel", fn);
+    if (!partial || !block_tables || !mfma || (opt->new_key && !work_items))
+      return fail(PKV_ERR_INVALID_ARGUMENT, "%s: groups take partitions, block tables, the MFMA "
+                  "kernel, and new rows only with a work list", fn);
     if (num_groups < 0 || !aligned(groups, 16))
       return fail(PKV_ERR_INVALID_ARGUMENT, "%s: groups pointer misaligned or num_groups %d", fn,
                   num_groups);
@@ -146,12 +146,13 @@ pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, 
   const int64_t ranges = partial ? ((int64_t)max_context_len + partition_size - 1) / partition_size : 1;
   if (work_items && num_work_items < 0)
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: num_work_items %d", fn, num_work_items);
-  const int64_t units = groups ? (int64_t)num_groups
-                       : work_items ? (int64_t)num_work_items : (int64_t)num_seqs * ranges;
+  const int64_t listed = work_items ? (int64_t)num_work_items : 0;
+  const int64_t units = groups ? (int64_t)num_groups + listed
+                       : work_items ? listed : (int64_t)num_seqs * ranges;
   if ((int64_t)num_seqs * ranges > INT32_MAX)
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: %lld units", fn, (long long)num_seqs * ranges);
   const int64_t grid = units * num_kv_heads;  // the MFMA kernel pads units to a multiple of 8
-  if ((units + 7) / 8 * 8 * num_kv_heads > INT32_MAX)
+  if ((units + 15) / 8 * 8 * num_kv_heads > INT32_MAX)
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: grid of %lld workgroups", fn, (long long)grid);
   if (grid == 0) return PKV_OK;
   // No (sequence, range) unit exists (no sequences, or split mode with no positions): nothing
@@ -168,7 +169,7 @@ pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, 
   p.context_lens = context_lens;
   p.work_items = work_items;
   p.group_members = groups;
-  p.num_units = (int32_t)units;
+  p.num_units = (int32_t)(groups ? num_groups : units);
   p.new_key = opt->new_key;
   p.new_value = opt->new_value;
   p.max_logits = max_logits;
@@ -183,6 +184,19 @@ pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, 
   p.num_ranges = (int32_t)ranges;
   p.scale_log2e = scale * pkv::kLog2e;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (groups && listed > 0) {
+    // The groups and the listed units in one launch; the groups write no new rows.
+    pkv::DecodeParams rest = p;
+    rest.group_members = nullptr;
+    rest.num_units = (int32_t)listed;
+    p.work_items = nullptr;
+    p.new_key = p.new_value = nullptr;
+    return hip_status(pkv::launch_decode_mfma_shared(to_dt(dtype), head_dim, block_size, p,
+                                                     rest, s), fn);
+  }
+  p.work_items = groups ? nullptr : work_items;
+  p.new_key = groups ? nullptr : opt->new_key;
+  p.new_value = groups ? nullptr : opt->new_value;
   const bool nt = !(opt->flags & PKV_DECODE_CACHED_KV);
   const hipError_t e =
       mfma ? pkv::launch_decode_mfma(to_dt(dtype), head_dim, block_size, partial, nt, p, s)
@@ -251,15 +265,18 @@ pkv_status pkv_paged_attention_decode_ex(
 }
 
 pkv_status pkv_paged_attention_decode_shared(
-    const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+    const void* q, void* k_cache, void* v_cache, const int32_t* block_tables,
     int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* groups,
-    int32_t num_groups, int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
-    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
-    pkv_dtype dtype, int32_t partition_size, float* max_logits, float* exp_sums,
-    float* tmp_out, void* stream) {
-  static const pkv_decode_options mfma = {PKV_KERNEL_MFMA, 0u, nullptr, nullptr};
-  return decode_impl(&mfma, nullptr, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
-                     block_tables, max_blocks_per_seq, context_lens, nullptr, 0,
+    int32_t num_groups, const int32_t* work_items, int32_t num_work_items,
+    const void* new_key, const void* new_value, int32_t max_context_len, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, float scale, pkv_dtype dtype, int32_t partition_size,
+    float* max_logits, float* exp_sums, float* tmp_out, void* stream) {
+  if (!groups)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "pkv_paged_attention_decode_shared: groups is NULL");
+  const pkv_decode_options mfma = {PKV_KERNEL_MFMA, 0u, new_key, new_value};
+  return decode_impl(&mfma, nullptr, q, k_cache, v_cache,
+                     block_tables, max_blocks_per_seq, context_lens, work_items, num_work_items,
                      max_context_len, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                      num_blocks, scale, dtype, partition_size, max_logits, exp_sums, tmp_out,
                      stream, groups, num_groups);

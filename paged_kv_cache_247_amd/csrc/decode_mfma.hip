@@ -71,12 +71,22 @@ __device__ __forceinline__ void wait_vm_le() {
 constexpr int kXcds = 8;  // XCDs of the MI355X, which take workgroups round robin
 constexpr int kBufferFlags = 0x00020000;
 
+// LDS of a decode workgroup: two K staging slots per wave (after the chunk loop the merge
+// buffers), the newest position's logits and its V row.
+template <int D, int NW>
+struct DecodeLds {
+  __attribute__((aligned(16))) char stage[NW * 2 * 32 * D * 2];
+  float new_logit[16];
+  float new_v[D];
+};
+
+// One workgroup's unit: w is its index in the launch's numbering (below).
 // GRP: a unit is a group of sequences whose block tables agree over the first range (a shared
 // prefix); column c of the products is head c % G of member c / G, so each shared tile is read
 // once for every member, and the range's partial state is written for each member.
-template <Dt DT, int D, int S, int NW, bool PARTIAL, bool NTL, bool TBL, bool GRP = false>
-__global__ void __launch_bounds__(NW * 64)
-decode_mfma_kernel(const DecodeParams a) {
+template <Dt DT, int D, int S, int NW, bool PARTIAL, bool NTL, bool TBL, bool GRP>
+__device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
+                                            DecodeLds<D, NW>& lds) {
   static_assert(!GRP || (PARTIAL && TBL), "groups write partials through block tables");
   static_assert(DT == Dt::BF16 || DT == Dt::F16, "16-bit inputs only");
   constexpr int EB = 2;
@@ -101,9 +111,10 @@ decode_mfma_kernel(const DecodeParams a) {
   // sixteen different head rows, which must not share banks.
   constexpr int DP = D + 4;
   static_assert((NW * 16 * DP + 2 * NW * 16) * 4 <= NW * 2 * SLOT, "merge fits the staging area");
-  __shared__ __attribute__((aligned(16))) char smem[NW * 2 * SLOT];
-  __shared__ float sh_new[16];
-  __shared__ float sh_vnew[D];
+  static_assert(sizeof(lds.stage) == NW * 2 * SLOT, "staging slots");
+  char* const smem = lds.stage;
+  float* const sh_new = lds.new_logit;
+  float* const sh_vnew = lds.new_v;
   auto sh_acc = reinterpret_cast<float (*)[16][DP]>(smem);
   auto sh_m = reinterpret_cast<float (*)[16]>(smem + NW * 16 * DP * 4);
   auto sh_l = reinterpret_cast<float (*)[16]>(smem + (NW * 16 * DP + NW * 16) * 4);
@@ -116,7 +127,6 @@ decode_mfma_kernel(const DecodeParams a) {
   // XCD (groups of 8 Hkv workgroups hold 8 units, head g of the group's unit j at 8 g + j), so
   // an XCD streams whole blocks of its sequences. Shared prefix blocks (cached loads): head g of
   // every unit on XCD g % 8, so a shared block's head tile stays in one XCD's L2.
-  const int w = blockIdx.x;
   int g, slot;
   if constexpr (NTL) {
     constexpr int XC = kXcds;
@@ -126,6 +136,7 @@ decode_mfma_kernel(const DecodeParams a) {
   } else {
     g = w % Hkv;
     slot = w / Hkv;
+    if (slot >= a.num_units) return;  // a combined grid pads each kind to whole groups of 8
   }
   int unit = a.work_items ? a.work_items[slot] : slot;
   unit = min(max(unit, 0), (GRP ? a.num_units : a.num_seqs * a.num_ranges) - 1);
@@ -530,6 +541,37 @@ decode_mfma_kernel(const DecodeParams a) {
   }
 }
 
+template <Dt DT, int D, int S, int NW, bool PARTIAL, bool NTL, bool TBL, bool GRP = false>
+__global__ void __launch_bounds__(NW * 64)
+decode_mfma_kernel(const DecodeParams a) {
+  __shared__ DecodeLds<D, NW> lds;
+  decode_unit<DT, D, S, NW, PARTIAL, NTL, TBL, GRP>(a, blockIdx.x, lds);
+}
+
+// A decode step over shared prefix blocks in one grid: the groups (grp, GRP units) and the
+// step's other units (rest, a work list of (sequence, partition) units), both writing
+// partials with cached loads. The grid is cut into pieces of 8 units (8 Hkv workgroups, head
+// g of the piece's unit j at j Hkv + g: a kv head keeps the XCDs it has in the separate
+// launches); pieces of groups and of other units alternate while both last, so the groups,
+// which read their tiles from L2, run beside units that stream from HBM.
+template <Dt DT, int D, int S, int NW>
+__global__ void __launch_bounds__(NW * 64)
+decode_mfma_shared_kernel(const DecodeParams grp, const DecodeParams rest) {
+  __shared__ DecodeLds<D, NW> lds;
+  const int per = kXcds * grp.num_kv_heads;  // workgroups per piece
+  const int ng = (grp.num_units + kXcds - 1) / kXcds;
+  const int nr = (rest.num_units + kXcds - 1) / kXcds;
+  const int both = min(ng, nr);
+  const int b = blockIdx.x / per;
+  const int u = blockIdx.x - b * per;
+  const bool grouped = b < 2 * both ? (b & 1) == 0 : ng > nr;
+  const int kb = b < 2 * both ? b >> 1 : b - both;  // piece index within its kind
+  if (grouped)
+    decode_unit<DT, D, S, NW, true, false, true, true>(grp, kb * per + u, lds);
+  else
+    decode_unit<DT, D, S, NW, true, false, true, false>(rest, kb * per + u, lds);
+}
+
 constexpr int kMfmaWaves = 4;
 
 template <Dt DT, int D, int S, bool PARTIAL, bool NTL>
@@ -551,6 +593,17 @@ hipError_t launch_grouped(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)p.num_units * (unsigned)p.num_kv_heads);
   decode_mfma_kernel<DT, D, S, kMfmaWaves, true, false, true, true>
       <<<grid, dim3(kMfmaWaves * 64), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+template <Dt DT, int D, int S>
+hipError_t launch_combined(const DecodeParams& grp, const DecodeParams& rest,
+                           hipStream_t stream) {
+  const unsigned pieces = (unsigned)(grp.num_units + kXcds - 1) / kXcds +
+                          (unsigned)(rest.num_units + kXcds - 1) / kXcds;
+  const dim3 grid(pieces * kXcds * (unsigned)grp.num_kv_heads);
+  decode_mfma_shared_kernel<DT, D, S, kMfmaWaves>
+      <<<grid, dim3(kMfmaWaves * 64), 0, stream>>>(grp, rest);
   return hipGetLastError();
 }
 
@@ -583,7 +636,26 @@ hipError_t launch_decode_mfma_bs(Dt dt, int head_dim, bool partial, bool nt,
   }
 }
 
+template <int S>
+hipError_t launch_decode_mfma_shared_bs(Dt dt, int head_dim, const DecodeParams& grp,
+                                        const DecodeParams& rest, hipStream_t stream) {
+  switch (dt) {
+    case Dt::F16:
+      return head_dim == 64 ? launch_combined<Dt::F16, 64, S>(grp, rest, stream)
+             : head_dim == 128 ? launch_combined<Dt::F16, 128, S>(grp, rest, stream)
+                               : hipErrorNotSupported;
+    case Dt::BF16:
+      return head_dim == 64 ? launch_combined<Dt::BF16, 64, S>(grp, rest, stream)
+             : head_dim == 128 ? launch_combined<Dt::BF16, 128, S>(grp, rest, stream)
+                               : hipErrorNotSupported;
+    default: return hipErrorNotSupported;
+  }
+}
+
 template hipError_t launch_decode_mfma_bs<PKV_BLOCK_SIZE>(Dt, int, bool, bool,
                                                           const DecodeParams&, hipStream_t);
+template hipError_t launch_decode_mfma_shared_bs<PKV_BLOCK_SIZE>(Dt, int, const DecodeParams&,
+                                                                 const DecodeParams&,
+                                                                 hipStream_t);
 
 }  // namespace pkv

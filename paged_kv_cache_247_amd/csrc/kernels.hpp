@@ -85,11 +85,18 @@ hipError_t launch_decode_valu_bs(Dt dt, int head_dim, int group, bool partial, b
 template <int S>
 hipError_t launch_decode_mfma_bs(Dt dt, int head_dim, bool partial, bool nt,
                                  const DecodeParams& p, hipStream_t stream);
+// Groups sharing a prefix (grp) and the step's other units (rest, with a work list) in one
+// launch of the MFMA kernel, both as partials with cached loads.
+template <int S>
+hipError_t launch_decode_mfma_shared_bs(Dt dt, int head_dim, const DecodeParams& grp,
+                                        const DecodeParams& rest, hipStream_t stream);
 #define PKV_DECODE_BLOCK_SIZE(S)                                                              \
   extern template hipError_t launch_decode_valu_bs<S>(Dt, int, int, bool, bool,              \
                                                       const DecodeParams&, hipStream_t);     \
   extern template hipError_t launch_decode_mfma_bs<S>(Dt, int, bool, bool,                   \
-                                                      const DecodeParams&, hipStream_t);
+                                                      const DecodeParams&, hipStream_t);     \
+  extern template hipError_t launch_decode_mfma_shared_bs<S>(                                \
+      Dt, int, const DecodeParams&, const DecodeParams&, hipStream_t);
 PKV_DECODE_BLOCK_SIZE(16)
 PKV_DECODE_BLOCK_SIZE(32)
 PKV_DECODE_BLOCK_SIZE(64)
@@ -118,6 +125,19 @@ inline hipError_t launch_decode_mfma(Dt dt, int head_dim, int block_size, bool p
     case 64: return launch_decode_mfma_bs<64>(dt, head_dim, partial, nt, p, stream);
     case 128: return launch_decode_mfma_bs<128>(dt, head_dim, partial, nt, p, stream);
     case 256: return launch_decode_mfma_bs<256>(dt, head_dim, partial, nt, p, stream);
+    default: return hipErrorNotSupported;
+  }
+}
+
+inline hipError_t launch_decode_mfma_shared(Dt dt, int head_dim, int block_size,
+                                            const DecodeParams& grp, const DecodeParams& rest,
+                                            hipStream_t stream) {
+  switch (block_size) {
+    case 16: return launch_decode_mfma_shared_bs<16>(dt, head_dim, grp, rest, stream);
+    case 32: return launch_decode_mfma_shared_bs<32>(dt, head_dim, grp, rest, stream);
+    case 64: return launch_decode_mfma_shared_bs<64>(dt, head_dim, grp, rest, stream);
+    case 128: return launch_decode_mfma_shared_bs<128>(dt, head_dim, grp, rest, stream);
+    case 256: return launch_decode_mfma_shared_bs<256>(dt, head_dim, grp, rest, stream);
     default: return hipErrorNotSupported;
   }
 }

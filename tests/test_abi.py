@@ -137,25 +137,34 @@ def test_reduce_and_copy_validation(lib):
 
 
 def shared(lib, **kw):
-    a = dict(q=A16, k=A16, v=A16, bt=A16, MB=4, lens=A16, groups=A16, ng=2, maxlen=64, B=8,
-             H=8, Hkv=2, D=128, S=16, N=32, scale=0.125, dtype=2, P=32, ml=A16, es=A16, to=A16)
+    a = dict(q=A16, k=A16, v=A16, bt=A16, MB=4, lens=A16, groups=A16, ng=2, wi=None, nw=0,
+             nk=None, nv=None, maxlen=64, B=8, H=8, Hkv=2, D=128, S=16, N=32, scale=0.125,
+             dtype=2, P=32, ml=A16, es=A16, to=A16)
     a.update(kw)
     return lib.pkv_paged_attention_decode_shared(
-        a["q"], a["k"], a["v"], a["bt"], a["MB"], a["lens"], a["groups"], a["ng"], a["maxlen"],
-        a["B"], a["H"], a["Hkv"], a["D"], a["S"], a["N"], a["scale"], a["dtype"], a["P"],
-        a["ml"], a["es"], a["to"], None)
+        a["q"], a["k"], a["v"], a["bt"], a["MB"], a["lens"], a["groups"], a["ng"], a["wi"],
+        a["nw"], a["nk"], a["nv"], a["maxlen"], a["B"], a["H"], a["Hkv"], a["D"], a["S"],
+        a["N"], a["scale"], a["dtype"], a["P"], a["ml"], a["es"], a["to"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(P=0, ml=None, es=None, to=None), INVALID),  # groups write partitions
     (dict(bt=None), INVALID),                          # through block tables
+    (dict(groups=None), INVALID),
     (dict(groups=A16 + 4), INVALID),
     (dict(ng=-1), INVALID),
     (dict(dtype=0), UNSUPPORTED),                      # the matrix-core kernel: fp16/bf16
     (dict(P=24), INVALID),                             # not a multiple of the block size
+    (dict(nk=A16, nv=A16), INVALID),                   # new rows belong to listed units
+    (dict(wi=A16, nw=4, nk=A16, nv=None), INVALID),    # new rows come in pairs
+    (dict(wi=A16, nw=-1), INVALID),
+    (dict(wi=A16 + 2, nw=4), INVALID),                 # misaligned work list
     (dict(ng=0), OK),                                  # nothing to do, nothing enqueued
+    (dict(ng=0, wi=A16, nw=0), OK),
     (dict(B=0), OK),
+    (dict(B=0, wi=A16, nw=4, nk=A16, nv=A16), OK),
     (dict(maxlen=0), OK),                              # no partition to write
+    (dict(maxlen=0, wi=A16, nw=4), OK),
 ])
 def test_decode_shared_validation(lib, kw, status):
     assert shared(lib, **kw) == status

@@ -101,3 +101,62 @@ def test_full_size_sampled_against_oracle():
     err = oracle.max_abs_err(out[seqs], oracle_out(wl, seqs))
     assert err <= TOL[c.dtype], f"max abs err {err}"
 
+
+
+def _workspace(wl, P):
+    c = wl.cfg
+    ws = pk.partition_workspace(c.num_seqs, c.num_heads, c.head_dim, wl.max_context_len, P,
+                                torch.device("cuda"))
+    for t in ws:
+        t.fill_(float("nan"))
+    return ws
+
+
+ONE_LAUNCH = [("small", {}, None), ("small", {"dtype": "f16", "head_dim": 64}, None),
+              ("small", {"block_size": 32, "prefix_len": 64, "num_blocks": 24}, None),
+              ("full", {}, None), ("full", {}, 20)]
+
+
+@pytest.mark.parametrize("size,over,listed", ONE_LAUNCH,
+                         ids=[f"{s}-{'-'.join(f'{k}{v}' for k, v in o.items()) or 'base'}-{n}"
+                              for s, o, n in ONE_LAUNCH])
+def test_one_launch_equals_two_launches(size, over, listed):
+    """The groups and the step's other units in one launch write the same bits as the grouped
+    launch followed by split-context decode of the work list: each unit is the same arithmetic
+    either way. `listed` cuts the work list short (fewer pieces of other units than of
+    groups)."""
+    base = W.SMALL["c4"] if size == "small" else W.CONFIGS["c4"]
+    wl = W.generate(base.replace(**over))
+    c = wl.cfg
+    plan = sharing.plan(wl.block_tables, wl.context_lens, c.block_size, wl.max_context_len,
+                        c.group)
+    P = plan.partition_size
+    items = to_dev(plan.work_items if listed is None else plan.work_items[:listed])
+    groups = to_dev(plan.groups)
+    print(f"[gpu] one launch: {size} {over} groups={len(plan.groups)} "
+          f"units={int(items.shape[0])}", file=sys.stderr, flush=True)
+    runs = []
+    for one in (False, True):
+        d = upload(wl)
+        if len(wl.block_mapping):
+            pk.copy_blocks([d.k], [d.v], d.mapping)
+        ws = _workspace(wl, P)
+        if one:
+            pk.paged_attention_decode_shared(d.q, d.k, d.v, d.bt, d.lens, groups,
+                                             wl.max_context_len, c.scale, P, ws,
+                                             work_items=items, new_key=d.key,
+                                             new_value=d.value)
+        else:
+            pk.paged_attention_decode_shared(d.q, d.k, d.v, d.bt, d.lens, groups,
+                                             wl.max_context_len, c.scale, P, ws)
+            pk.paged_attention_decode(None, d.q, d.k, d.v, d.bt, d.lens, wl.max_context_len,
+                                      c.scale, P, ws, work_items=items, cached_kv=True,
+                                      new_key=d.key, new_value=d.value)
+        torch.cuda.synchronize()
+        runs.append((ws, d))
+    (wa, da), (wb, db) = runs
+    for a, b in zip(wa, wb):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(da.k.view(torch.int16), db.k.view(torch.int16))
+    assert torch.equal(da.v.view(torch.int16), db.v.view(torch.int16))
+    assert not torch.isnan(wb[0]).all(), "the launch wrote partials"

@@ -77,3 +77,23 @@ def test_group_contract_violations():
     bad(tables=t)                                    # a member's table differs
     L = wl.context_lens.copy(); L[ok[0, 2]] = P - 1
     bad(lens=L)                                      # too short for the shared partition
+
+
+def test_group_contract_with_the_work_list():
+    """Groups run in one launch with the step's work list: the list must not name a member's
+    partition 0, and with the fused newest-position write each member reaches past the shared
+    partition."""
+    wl = W.generate(W.SMALL["c4"])
+    S, N = 16, wl.cfg.num_blocks
+    plan = sharing.plan(wl.block_tables, wl.context_lens, S, wl.max_context_len, 4)
+    P, NP, g = plan.partition_size, plan.num_partitions, plan.groups
+    C.check_groups(g, wl.block_tables, wl.context_lens, P, S, N, 4,
+                   work_items=plan.work_items, num_partitions=NP, fused_write=True)
+    with pytest.raises(C.ContractError, match="partition 0"):
+        C.check_groups(g, wl.block_tables, wl.context_lens, P, S, N, 4,
+                       work_items=np.append(plan.work_items, g[1, 1] * NP), num_partitions=NP)
+    L = wl.context_lens.copy(); L[g[0, 1]] = P
+    C.check_groups(g, wl.block_tables, L, P, S, N, 4)  # reaches the partition's end
+    with pytest.raises(C.ContractError):             # but the newest position would be in it
+        C.check_groups(g, wl.block_tables, L, P, S, N, 4, work_items=plan.work_items,
+                       num_partitions=NP, fused_write=True)
