@@ -4,13 +4,13 @@ Requests that share a prompt prefix share its KV blocks (Hacker News discussion 
 PagedAttention, replies on prefix sharing), so their block tables agree over the prefix. A
 decode step can then read each shared tile once for several sequences
 (pkv_paged_attention_decode_shared, up to 16 / G sequences per group) instead of once per
-sequence. The step becomes three launches over split-context partitions of P positions, with
-P a multiple of the block size inside the shared prefix:
+sequence. The step works on split-context partitions of P positions, with P a multiple of the
+block size inside the shared prefix, in two launches:
 
-  1. partition 0 of every grouped sequence, one pass per group;
-  2. every other unit (i, p) with positions -- p >= 1 of grouped sequences, all partitions of
-     the others -- through pkv_paged_attention_decode, largest first;
-  3. the merge of the partitions (pkv_paged_attention_reduce).
+  1. partition 0 of every grouped sequence, one pass per group, and in the same launch every
+     other unit (i, p) with positions -- p >= 1 of grouped sequences, all partitions of the
+     others -- as split-context decode runs them, from a work list ordered largest first;
+  2. the merge of the partitions (pkv_paged_attention_reduce).
 
 The result is the same attention (the merge is an exact rewriting of the softmax sum); only
 the order of the fp32 additions differs from a single pass.
