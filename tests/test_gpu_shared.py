@@ -42,7 +42,8 @@ def shared_step(wl, plan, workspace=None):
 
 CASES = [({}, 4), ({"num_heads": 16}, 2), ({"num_heads": 4}, 4), ({"dtype": "f16"}, 4),
          ({"head_dim": 64}, 4), ({"block_size": 32, "prefix_len": 64, "num_blocks": 24}, 4),
-         ({}, 3)]
+         ({"block_size": 64, "prefix_len": 192, "num_blocks": 16}, 4),
+         ({"block_size": 256, "prefix_len": 512, "num_blocks": 16}, 4), ({}, 3)]
 
 
 @pytest.mark.parametrize("over,width", CASES,
@@ -114,6 +115,8 @@ def _workspace(wl, P):
 
 ONE_LAUNCH = [("small", {}, None), ("small", {"dtype": "f16", "head_dim": 64}, None),
               ("small", {"block_size": 32, "prefix_len": 64, "num_blocks": 24}, None),
+              ("small", {"block_size": 64, "prefix_len": 192, "num_blocks": 16}, None),
+              ("small", {"block_size": 128, "prefix_len": 256, "num_blocks": 16}, None),
               ("full", {}, None), ("full", {}, 20)]
 
 
