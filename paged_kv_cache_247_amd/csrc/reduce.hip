@@ -21,6 +21,26 @@ __global__ void __launch_bounds__(64) reduce_kernel(const ReduceParams a) {
   const int lane = lane_id();
   T* o = reinterpret_cast<T*>(a.out) + ((size_t)i * H + h) * D;
 
+  // The records of the first 64 partitions and the first U partial rows lie inside the
+  // workspace whatever the length, so they are loaded together with it: the wave waits for
+  // memory once instead of once per step. Entries past the sequence's last partition are
+  // never used.
+  const size_t rec0 = ((size_t)i * H + h) * a.max_num_partitions;
+  const float* ml = a.max_logits + rec0;
+  const float* es = a.exp_sums + rec0;
+  const float* to = a.tmp_out + rec0 * D + lane;
+  const int pre = min(64, a.max_num_partitions);
+  float ml0 = -INFINITY, es0 = 0.0f;
+  if (lane < pre) {
+    ml0 = ml[lane];
+    es0 = es[lane];
+  }
+  float t0[U][PER];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int e = 0; e < PER; ++e) t0[u][e] = u < pre ? to[(size_t)u * D + 64 * e] : 0.0f;
+
   const int L = max(a.context_lens[i], 0);
   const int n = min((int)(((int64_t)L + a.partition_size - 1) / a.partition_size),
                     a.max_num_partitions);
@@ -29,17 +49,12 @@ __global__ void __launch_bounds__(64) reduce_kernel(const ReduceParams a) {
     for (int e = 0; e < PER; ++e) o[lane + 64 * e] = from_f32<DT>(0.0f);
     return;
   }
-  const size_t rec0 = ((size_t)i * H + h) * a.max_num_partitions;
-  const float* ml = a.max_logits + rec0;
-  const float* es = a.exp_sums + rec0;
-  const float* to = a.tmp_out + rec0 * D + lane;
 
-  // Lane p handles partition p (of each group of 64): M and the weight total first.
-  float M = -INFINITY;
-  for (int p = lane; p < n; p += 64) M = fmaxf(M, ml[p]);
+  float M = lane < n ? fmaxf(-INFINITY, ml0) : -INFINITY;
+  for (int p = lane + 64; p < n; p += 64) M = fmaxf(M, ml[p]);
   M = group_reduce<64>(M, OpMax());
-  float den = 0.0f;
-  for (int p = lane; p < n; p += 64) den += es[p] * __builtin_amdgcn_exp2f((ml[p] - M) * kLog2e);
+  float den = lane < n ? es0 * __builtin_amdgcn_exp2f((ml0 - M) * kLog2e) : 0.0f;
+  for (int p = lane + 64; p < n; p += 64) den += es[p] * __builtin_amdgcn_exp2f((ml[p] - M) * kLog2e);
   den = group_reduce<64>(den, OpAdd());
 
   float acc[PER];
@@ -47,11 +62,23 @@ __global__ void __launch_bounds__(64) reduce_kernel(const ReduceParams a) {
   for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
   for (int p0 = 0; p0 < n; p0 += 64) {
     const int cnt = min(64, n - p0);
-    // Normalised weight of this lane's partition; w / den is exactly 1 for a lone partition.
     float w = 0.0f;
-    if (lane < cnt) w = es[p0 + lane] * __builtin_amdgcn_exp2f((ml[p0 + lane] - M) * kLog2e) / den;
+    if (lane < cnt)
+      w = p0 == 0 ? es0 * __builtin_amdgcn_exp2f((ml0 - M) * kLog2e) / den
+                  : es[p0 + lane] * __builtin_amdgcn_exp2f((ml[p0 + lane] - M) * kLog2e) / den;
     const float* row = to + (size_t)p0 * D;
     int p = 0;
+    if (p0 == 0) {  // the rows loaded up front
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (u < cnt) {
+          const float wp = bits_f((uint32_t)__builtin_amdgcn_readlane((int)f_bits(w), u));
+#pragma unroll
+          for (int e = 0; e < PER; ++e) acc[e] = fmaf(wp, t0[u][e], acc[e]);
+        }
+      }
+      p = min(U, cnt);
+    }
     for (; p + U <= cnt; p += U) {
       float t[U][PER];
 #pragma unroll
