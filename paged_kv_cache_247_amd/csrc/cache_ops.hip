@@ -7,6 +7,8 @@
 // blocks). Requests that share a prefix share its blocks (Hacker News discussion of
 // PagedAttention, replies on shared prefixes); a block is copied before a sequence writes into
 // a shared one.
+#include <limits.h>
+
 #include "kernels.hpp"
 
 namespace pkv {
@@ -45,9 +47,15 @@ __global__ void __launch_bounds__(256) reshape_and_cache_kernel(const CacheWrite
   }
 }
 
-// One workgroup per (pair, layer, pool): a block of one pool is one contiguous tile.
-__global__ void __launch_bounds__(256) copy_blocks_kernel(const CopyParams a) {
-  const int pair = blockIdx.x;
+// A block of one pool is one contiguous tile. Workgroup (pair, piece) of (layer, pool) copies
+// 4 KiB of it, one 16-byte vector per thread, so that a copy of a few blocks still spreads
+// over the GPU and each thread waits for memory once.
+constexpr int kCopyThreads = 256;
+constexpr int kCopyPiece = kCopyThreads * 16;  // bytes per workgroup
+
+__global__ void __launch_bounds__(kCopyThreads) copy_blocks_kernel(const CopyParams a) {
+  const int pair = blockIdx.x / a.pieces;
+  const int piece = blockIdx.x - pair * a.pieces;
   const int layer = blockIdx.y;
   const int64_t src = a.block_mapping[2 * pair];
   const int64_t dst = a.block_mapping[2 * pair + 1];
@@ -55,8 +63,8 @@ __global__ void __launch_bounds__(256) copy_blocks_kernel(const CopyParams a) {
   char* base = reinterpret_cast<char*>(blockIdx.z == 0 ? a.k[layer] : a.v[layer]);
   const u32x4* s = reinterpret_cast<const u32x4*>(base + src * a.tile_bytes);
   u32x4* d = reinterpret_cast<u32x4*>(base + dst * a.tile_bytes);
-  const int64_t n = a.tile_bytes / 16;
-  for (int64_t e = threadIdx.x; e < n; e += blockDim.x) d[e] = s[e];
+  const int64_t e = (int64_t)piece * kCopyThreads + threadIdx.x;
+  if (e < a.tile_bytes / 16) d[e] = s[e];
 }
 
 template <Dt DT, int D>
@@ -95,8 +103,11 @@ hipError_t launch_reshape_and_cache(Dt dt, int head_dim, int block_size,
 }
 
 hipError_t launch_copy_blocks(int num_layers, const CopyParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)p.num_pairs, (unsigned)num_layers, 2);
-  copy_blocks_kernel<<<grid, 256, 0, stream>>>(p);
+  CopyParams q = p;
+  q.pieces = (int32_t)((p.tile_bytes + kCopyPiece - 1) / kCopyPiece);
+  if ((int64_t)p.num_pairs * q.pieces > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(p.num_pairs * q.pieces), (unsigned)num_layers, 2);
+  copy_blocks_kernel<<<grid, kCopyThreads, 0, stream>>>(q);
   return hipGetLastError();
 }
 

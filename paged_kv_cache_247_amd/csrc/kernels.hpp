@@ -59,6 +59,7 @@ struct CopyParams {
   int32_t num_pairs;
   int32_t num_blocks;
   int64_t tile_bytes;  // Hkv * S * D * elt: one block of one pool
+  int32_t pieces;      // workgroups per tile (set by the launcher)
 };
 
 struct CacheWriteParams {
