@@ -368,7 +368,7 @@ size_t pkv_vmm_pool_mapped_bytes(const pkv_vmm_pool* pool); /* K + V physically 
 const char* pkv_status_string(pkv_status s);
 int pkv_last_hip_error(void);              /* hipError_t behind the last PKV_ERR_HIP */
 const char* pkv_last_error_message(void);  /* thread-local text of the last failure */
-int pkv_abi_version(void);                 /* 1 */
+int pkv_abi_version(void);                 /* 2: decode_shared takes a work list and new rows */
 
 #ifdef __cplusplus
 }

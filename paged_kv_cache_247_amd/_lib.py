@@ -120,6 +120,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    if lib.pkv_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{p} implements ABI {lib.pkv_abi_version()}, this binding ABI "
+                           f"{ABI_VERSION}: rebuild it (`python -m paged_kv_cache_247_amd.build`)")
     if path is None:
         _lib = lib
     return lib
@@ -131,6 +134,7 @@ class OutOfBlocks(PagedKVError):
 
 PKV_ERR_HIP = 3
 PKV_ERR_NO_BLOCKS = 4
+ABI_VERSION = 2  # the argument lists in SIGNATURES
 
 
 def _check(status: int):

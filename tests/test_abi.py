@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES), "binding prototypes out of step with the header"
-    assert lib.pkv_abi_version() == 1
+    assert lib.pkv_abi_version() == 2
 
 
 def test_status_strings(lib):
