@@ -239,3 +239,11 @@ def test_auto_partition_policy():
     assert pk.auto_partition_size(32, 8, 32, num_cus=256) == 2048
     assert pk.auto_partition_size(1, 1, 16, num_cus=256) == 2048
     assert pk.auto_partition_size(2048, 32, 16, num_cus=256) == 0
+
+
+def test_binding_refuses_another_abi(monkeypatch):
+    """The argument lists the binding declares belong to one ABI version: a library built from
+    other sources is refused at load instead of being called with the wrong arguments."""
+    monkeypatch.setattr(_lib, "ABI_VERSION", _lib.ABI_VERSION + 1)
+    with pytest.raises(RuntimeError, match="ABI"):
+        _lib.load(_lib.LIB_PATH)
