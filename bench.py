@@ -1,7 +1,7 @@
 """Paged decode benchmark on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3] [--kernel auto]
-                    [--partition-size P] [--unfused] [--no-cpu-baseline]
+                    [--partition-size P] [--unfused] [--layout paged] [--no-cpu-baseline]
 
 One step is one pass of the whole hot path over one batch: copy-on-write block copies (when
 the workload has them), the cache write of each sequence's newest token, paged decode, and the
@@ -12,9 +12,16 @@ before timing starts.
 Prints one JSON line: KV-read GB/s over the step (value), attended tokens/s, the decode
 kernel's roofline figures (timed per launch with HIP events on the launch stream), repetition
 statistics of back-to-back launches of each kernel on its own (decode, cache write, block copy,
-merge), and the oracle's CPU throughput on the same workload at one thread and at all cores.
-The oracle is timed first, before anything touches the GPU, so its worker processes are plain
-CPU processes.
+merge), the oracle's CPU throughput on the same workload at one thread and at all cores, and
+the largest difference between the timed step's output and the oracle's over every sequence
+(the run exits with status 3 if it is above tolerance). The default run (the grouped-query
+batch) adds the other four workloads in their own launch configurations (`configs`), what the
+block table costs against the contiguous reservation (`paging_cost`), and the read bandwidth
+HBM gives a kernel that only loads (`read_ceiling`).
+
+The oracle runs only in the CPU-baseline leg: its timed passes are over the step's own input
+pools, and the last pass is the expected output. The main workload's oracle is timed first,
+before anything touches the GPU, so its worker processes are plain CPU processes.
 """
 from __future__ import annotations
 
@@ -25,23 +32,36 @@ import os
 import platform
 import sys
 import time
+from types import SimpleNamespace
 
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published peak
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix-core peak, AMD published
+TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2}  # max |gpu - oracle|, fp32 accumulation
+
+# The pages' only figure on the kernel's speed; another machine's, quoted as context.
+PAGES_CLAIM = {
+    "claim": "a paged attention kernel was up to 2.85x slower than its FlashAttention "
+             "counterpart for grouped-query attention",
+    "source": "vAttention paper, section 3.1 (its Figure 9b, not reproduced on the page)",
+    "hardware": "not stated on the page"}
 
 # Launch configuration the benchmark uses for each workload: (kernel family, partition size,
 # cached K/V loads). With longest-first dispatch, single-pass decode is fastest up to 4k-token
-# contexts; the lognormal long-context batch (up to ~31k tokens) splits into 2048-token
-# partitions; the prefix-shared batch keeps K/V in cache so the shared prefix is reused.
+# contexts; the lognormal long-context batch (up to ~31k tokens) splits into the 512-token
+# partitions its statement names; the prefix-shared batch keeps K/V in cache so the shared
+# prefix is reused.
 LAUNCH = {
     "c1": ("auto", 0, False),
     "c2": ("auto", 0, False),
     "c3": ("auto", 0, False),
     "c4": ("auto", 0, True),
-    "c5": ("auto", 2048, False),
+    "c5": ("auto", 512, False),
 }
+# The other workloads reported beside the default one: (workload, partition size override).
+# The long-context batch also in 2048-token partitions (an option, not its stated launch).
+CONFIG_BLOCK = [("c1", None), ("c2", None), ("c4", None), ("c5", None), ("c5", 2048)]
 
 BLOCK_SIZES = (16, 32, 64, 128, 256)  # block sizes the library takes
 
@@ -61,7 +81,17 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--unfused", action="store_true",
                     help="write new tokens with a separate reshape_and_cache launch")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layout", default="paged",
+                    help="paged (scattered blocks, block tables); contiguous (each sequence's "
+                         "blocks in order, read without tables); contiguous-table (the same "
+                         "layout read through identity tables); vmm:<page bytes> (the "
+                         "contiguous layout in HIP virtual memory mapped in pages of that size)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle (and with it the check of the output)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="default run without the other workloads, the paging cost and the "
+                         "read ceiling (the other workloads also need the oracle: they are "
+                         "left out with --no-cpu-baseline)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time to spend timing the oracle on one thread")
     ap.add_argument("--cpu-all-seconds", type=float, default=3.0,
@@ -83,24 +113,49 @@ def parse():
                          "1/N of the kv heads (and their q heads), seq:N 1/N of the sequences")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    layout = args.layout
+    if not (layout in ("paged", "contiguous", "contiguous-table") or
+            (layout.startswith("vmm:") and layout[4:].isdigit())):
+        ap.error(f"--layout {layout}: expected paged, contiguous, contiguous-table or "
+                 "vmm:<page bytes>")
+    return args
 
 
 # ------------------------------------------------------------------ oracle on the CPU
 
-_WL = None  # the workload, inherited by forked oracle workers
+_POOLS = None  # (workload, k pool, v pool) of the step, inherited by forked oracle workers
+
+
+def step_pools(wl):
+    """The pools one step decodes over: the copy-on-write copies and the newest tokens' cache
+    writes applied by the oracle (untimed: this is the step's input, not its decode)."""
+    import oracle
+    c = wl.cfg
+    kc, vc = oracle.write_cache(wl.k_cache, wl.v_cache, wl.key, wl.value, wl.slot_mapping,
+                                c.block_size)
+    if len(wl.block_mapping):
+        (kc,), (vc,) = oracle.copy_blocks([kc], [vc], wl.block_mapping)
+    return kc, vc
+
+
+def _oracle_decode(wl, kc, vc, idx=None):
+    import oracle
+    c = wl.cfg
+    if idx is None:
+        return oracle.decode(wl.q, kc, vc, wl.block_tables, wl.context_lens, c.scale,
+                             c.num_kv_heads, c.dtype)
+    return oracle.decode(wl.q[idx], kc, vc, wl.block_tables[idx], wl.context_lens[idx],
+                         c.scale, c.num_kv_heads, c.dtype)
 
 
 def _oracle_part(idx):
     """One worker's share of an oracle pass: decode of the sequences idx on one thread."""
     from threadpoolctl import threadpool_limits
-
-    import oracle
-    c = _WL.cfg
+    wl, kc, vc = _POOLS
     with threadpool_limits(limits=1):
-        oracle.decode(_WL.q[idx], _WL.k_cache, _WL.v_cache, _WL.block_tables[idx],
-                      _WL.context_lens[idx], c.scale, c.num_kv_heads, c.dtype)
-    return int(_WL.context_lens[idx].sum())
+        _oracle_decode(wl, kc, vc, idx)
+    return int(wl.context_lens[idx].sum())
 
 
 def _shares(lens, n):
@@ -126,33 +181,33 @@ def cpu_model() -> str:
 
 
 def cpu_baseline(wl, one_s: float, all_s: float, workers: int):
-    """The oracle's decode (fp64 numpy) over whole passes of the workload: first on one thread
-    for about one_s seconds, then split over `workers` forked processes (one thread each) for
-    about all_s seconds of wall time."""
-    global _WL
+    """The oracle's decode (fp64 numpy) over whole passes of the step's pools: first on one
+    thread for about one_s seconds (at least one pass), then split over `workers` forked
+    processes (one thread each) for about all_s seconds of wall time. Returns the figures and
+    the last one-thread pass's output (the expected output of the step)."""
+    global _POOLS
     from threadpoolctl import threadpool_limits
-
-    import oracle
     c = wl.cfg
-    elt = 4 if c.dtype == "f32" else 2
-    per_tok = c.num_kv_heads * c.head_dim * elt * 2
+    kc, vc = step_pools(wl)
+    per_tok = c.num_kv_heads * c.head_dim * (4 if c.dtype == "f32" else 2) * 2
     passes, toks, dt = 0, 0, 0.0
+    expected = None
     with threadpool_limits(limits=1):
-        while dt < one_s:
+        while passes == 0 or dt < one_s:
             t0 = time.perf_counter()
-            oracle.decode(wl.q, wl.k_cache, wl.v_cache, wl.block_tables, wl.context_lens,
-                          c.scale, c.num_kv_heads, c.dtype)
+            expected = _oracle_decode(wl, kc, vc)
             dt += time.perf_counter() - t0
             passes += 1
             toks += wl.total_tokens
+    what = "pass" if passes == 1 else "passes"
     res = {"value": round(toks * per_tok / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
            "kind": "oracle",
-           "sample": f"{passes} whole passes over all {c.num_seqs} sequences ({wl.total_tokens} "
+           "sample": f"{passes} whole {what} over all {c.num_seqs} sequences ({wl.total_tokens} "
                      f"context tokens each), fp64 numpy decode on one thread, {dt:.1f} s",
            "attended_tokens_per_s": round(toks / dt, 1),
            "cpu": cpu_model(), "host_cpus": os.cpu_count()}
     if workers > 1 and all_s > 0:
-        _WL = wl
+        _POOLS = (wl, kc, vc)
         shares = _shares(wl.context_lens, workers)
         with mp.get_context("fork").Pool(len(shares)) as pool:
             pool.map(_oracle_part, shares)  # start-up and first touch, untimed
@@ -162,13 +217,22 @@ def cpu_baseline(wl, one_s: float, all_s: float, workers: int):
                 toks += sum(pool.map(_oracle_part, shares))
                 passes += 1
             dt = time.perf_counter() - t0
-        _WL = None
+        _POOLS = None
         res["all_cores"] = {
             "value": round(toks * per_tok / dt / 1e9, 4), "unit": "GB/s", "cores": len(shares),
             "sample": f"{passes} whole passes split over {len(shares)} processes (one thread "
                       f"each, sequences balanced by length), {dt:.1f} s wall",
             "attended_tokens_per_s": round(toks / dt, 1)}
-    return res
+    return res, expected
+
+
+def parity(out, expected, dtype: str, what: str) -> dict:
+    """Largest |gpu - oracle| over every element of the step's output."""
+    got = out.detach().float().cpu().numpy().astype(np.float64)
+    d = np.abs(got - expected)
+    err = float("inf") if np.isnan(d).any() else float(d.max()) if d.size else 0.0
+    return {"max_abs_err": err, "tol": TOL[dtype], "ok": bool(err <= TOL[dtype]),
+            "compared": what, "oracle": "fp64 numpy, the cpu_baseline leg's last pass"}
 
 
 # ------------------------------------------------------------------ GPU helpers
@@ -217,14 +281,267 @@ def launch_stats(torch, fn, launches: int, reps: int, warmup: int = 10):
             "max_us": round(per[-1], 3), "launches": launches, "reps": reps}
 
 
+def kernel_family(kernel, cfg, table_free=False):
+    if kernel == "mfma" or table_free:
+        return "mfma"
+    if kernel == "auto" and cfg.dtype != "f32" and cfg.group >= 4:
+        return "mfma"
+    return "valu"
+
+
+def build_step(torch, pk, wl, kernel, P, cached, shared_prefix="auto", fused=True,
+               layout="paged"):
+    """Device copies of a workload and the closures of one decode step.
+
+    layout "paged" decodes through the block tables; "contiguous" and "vmm:<bytes>" expect the
+    contiguous layout (workload.contiguous_layout) and decode without tables, the latter from a
+    virtual-memory pool; "contiguous-table" reads the contiguous layout through its identity
+    tables."""
+    cfg = wl.cfg
+    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
+
+    def dev(a, bf=cfg.dtype == "bf16"):
+        a = np.ascontiguousarray(a)
+        if bf:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    s = SimpleNamespace(cfg=cfg, wl=wl, kernel=kernel, P=P, cached=cached, fused=fused,
+                        layout=layout, plan=None, pool=None)
+    s.q, s.key, s.value = dev(wl.q), dev(wl.key), dev(wl.value)
+    s.kc, s.vc = dev(wl.k_cache), dev(wl.v_cache)
+    s.slots = dev(wl.slot_mapping, False)
+    s.bt, s.lens = dev(wl.block_tables, False), dev(wl.context_lens, False)
+    s.mapping = dev(wl.block_mapping.reshape(-1, 2), False)
+    table_free = layout == "contiguous" or layout.startswith("vmm:")
+    MB = wl.block_tables.shape[1]
+    if table_free:
+        s.kernel = kernel = "mfma"  # the table-free reservation runs on the matrix-core kernel
+        if not fused:
+            raise ValueError("the table-free layouts take the fused newest-token write")
+    if layout.startswith("vmm:"):
+        s.pool = pk.VmmPool(cfg.num_seqs, wl.max_context_len, cfg.num_kv_heads, cfg.head_dim,
+                            cfg.block_size, dt, page_bytes=int(layout[4:]))
+        for i in range(cfg.num_seqs):
+            L = int(wl.context_lens[i])
+            nb = -(-L // cfg.block_size)
+            s.pool.map(i, L)
+            if nb:
+                s.pool.write(i, s.kc[i * MB:i * MB + nb], s.vc[i * MB:i * MB + nb])
+        torch.cuda.synchronize()
+        s.kc = s.vc = None
+        torch.cuda.empty_cache()
+        kpool, vpool, MB = s.pool.k, s.pool.v, s.pool.blocks_per_seq
+    else:
+        kpool, vpool = s.kc, s.vc
+    s.family = kernel_family(kernel, cfg, table_free)
+    # Blocks shared by several sequences (a common prefix): plan groups that read each shared
+    # tile once for all their members (host scheduler input, like the work list).
+    if shared_prefix == "on" or (shared_prefix == "auto" and cfg.prefix_len and not P):
+        from paged_kv_cache_247_amd import sharing
+        s.plan = sharing.plan(wl.block_tables, wl.context_lens, cfg.block_size,
+                              wl.max_context_len, cfg.group, newest_outside=fused)
+        if s.plan is None and shared_prefix == "on":
+            raise ValueError("--shared-prefix on: no blocks are shared")
+    if s.plan is not None:
+        s.P, s.kernel, s.cached, s.family = s.plan.partition_size, "mfma", True, "mfma"
+        s.groups = dev(s.plan.groups, False)
+        s.order = dev(s.plan.work_items, False)
+    else:
+        # Host-side scheduler input: the units with work, largest first.
+        s.order = dev(wl.work_items(P), False)
+    P = s.P
+    s.out = torch.empty((cfg.num_seqs, cfg.num_heads, cfg.head_dim), dtype=dt, device="cuda")
+    s.ws = pk.partition_workspace(cfg.num_seqs, cfg.num_heads, cfg.head_dim,
+                                  wl.max_context_len, P, s.q.device) if P else None
+    s.has_copy = len(wl.block_mapping) > 0
+    maxlen = wl.max_context_len
+    nk, nv = (s.key, s.value) if fused else (None, None)
+    bt = None if table_free else s.bt
+
+    def decode():
+        # With fused=True the decode launch also writes each sequence's newest K/V to its slot.
+        if s.plan is not None:  # the groups and every other unit in one launch
+            pk.paged_attention_decode_shared(s.q, kpool, vpool, s.bt, s.lens, s.groups, maxlen,
+                                             cfg.scale, P, s.ws, work_items=s.order,
+                                             new_key=nk, new_value=nv)
+            return
+        pk.paged_attention_decode(None if P else s.out, s.q, kpool, vpool, bt, s.lens, maxlen,
+                                  cfg.scale, P, s.ws, kernel=s.kernel, work_items=s.order,
+                                  cached_kv=s.cached, new_key=nk, new_value=nv,
+                                  max_blocks_per_seq=MB if table_free else None)
+
+    def reduce():
+        pk.paged_attention_reduce(s.out, s.ws, s.lens, P)
+
+    def step(events=None):
+        if s.has_copy:
+            pk.copy_blocks([kpool], [vpool], s.mapping)
+        if not fused:
+            pk.reshape_and_cache(s.key, s.value, kpool, vpool, s.slots)
+        if events is not None:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        decode()
+        if events is not None:
+            e1.record()
+            events.append((e0, e1))
+        if P:
+            reduce()
+
+    def release():
+        if s.pool is not None:
+            s.pool.close()
+        for k in ("q", "key", "value", "kc", "vc", "slots", "bt", "lens", "mapping", "out",
+                  "ws", "order", "groups"):
+            setattr(s, k, None)
+        torch.cuda.empty_cache()
+
+    s.decode, s.reduce, s.step, s.release = decode, reduce, step, release
+    s.kpool, s.vpool = kpool, vpool
+    return s
+
+
+def roofline_bytes(wl):
+    """Bytes the decode launch must read: the KV bytes, or with shared blocks the distinct
+    tiles (the shared prefix is served from cache after its first read), without the
+    copy-on-write copies (a launch of their own)."""
+    return wl.unique_kv_bytes(include_copies=False) if len(wl.block_mapping) or \
+        wl.cfg.prefix_len else wl.kv_bytes()
+
+
+def config_entry(torch, pk, name, P_over, reps, launches):
+    """One workload in its own launch configuration: step and decode-launch timing, the
+    roofline fraction, the output against the oracle and a one-pass CPU baseline."""
+    from paged_kv_cache_247_amd import workload as W
+    kernel, P, cached = LAUNCH[name]
+    P = P if P_over is None else P_over
+    cfg = W.CONFIGS[name]
+    t0 = time.time()
+    wl = W.generate(cfg, poison="zero")
+    cpu, expected = cpu_baseline(wl, 0.0, 0.0, 1)
+    print(f"[bench] {name} P={P}: generated and oracle in {time.time() - t0:.1f}s",
+          file=sys.stderr, flush=True)
+    s = build_step(torch, pk, wl, kernel, P, cached)
+    dec = launch_stats(torch, s.decode, launches, reps)
+    stp = launch_stats(torch, s.step, launches, reps)
+    s.step()
+    torch.cuda.synchronize()
+    chk = parity(s.out, expected, cfg.dtype,
+                 f"all {cfg.num_seqs} sequences x {cfg.num_heads} heads x {cfg.head_dim}")
+    kvb, rb = wl.kv_bytes(), roofline_bytes(wl)
+    entry = {
+        "workload": f"{name}: {cfg.description}", "seed": cfg.seed,
+        "context_tokens": wl.total_tokens, "kv_bytes": kvb,
+        "kernel": ("paged_attention_decode_shared (mfma)" if s.plan is not None
+                   else f"paged_attention_decode ({s.family})"),
+        "partition_size": s.P, "cached_kv": s.cached,
+        "step_us": stp["median_us"],
+        "GB_per_s": round(kvb / (stp["median_us"] * 1e-6) / 1e9, 2),
+        "attended_tokens_per_s": round(wl.total_tokens / (stp["median_us"] * 1e-6), 1),
+        "decode_us": dec["median_us"],
+        "roofline": {"bound": "hbm", "bytes_per_launch": rb,
+                     "achieved": round(rb / (dec["median_us"] * 1e-6) / 1e9, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(rb / (dec["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "max_abs_err": chk["max_abs_err"], "tol": chk["tol"], "parity_ok": chk["ok"],
+        "cpu_baseline": {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
+    }
+    if P_over is not None:
+        entry["note"] = f"partition size {P} is an option; the workload states {LAUNCH[name][1]}"
+    s.release()
+    return entry
+
+
+def paging_cost(torch, pk, wl, paged_us, paged_out, reps, launches):
+    """The same batch, kernel and work list in the conventional contiguous reservation read
+    without block tables: what the block table costs the decode launch here."""
+    from paged_kv_cache_247_amd import workload as W
+    kernel, P, cached = LAUNCH[wl.cfg.name] if wl.cfg.name in LAUNCH else ("auto", 0, False)
+    wc = W.contiguous_layout(wl)
+    s = build_step(torch, pk, wc, kernel, P, cached, layout="contiguous")
+    st = launch_stats(torch, s.decode, launches, reps)
+    s.step()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(s.out.view(torch.uint8), paged_out.view(torch.uint8)))
+    s.release()
+    return {"paged_us": paged_us, "contiguous_no_table_us": st["median_us"],
+            "paged_over_contiguous": round(paged_us / st["median_us"], 4),
+            "outputs_bit_identical": same,
+            "what": "decode launch, median of back-to-back launches; same kernel, inputs and "
+                    "work list, blocks scattered through the pool and read through block "
+                    "tables against each sequence's blocks in order read without them "
+                    "(bench.py --layout contiguous|vmm:<page bytes> runs either as the step)",
+            "pages_context": PAGES_CLAIM}
+
+
+def read_ceiling(torch, pk, wl, reps, launches, seed=7):
+    """What HBM delivers to kernels that only load: one streaming read of a buffer the size of
+    the workload's two pools, and random gathers of whole tiles -- the (block, kv head) tiles
+    decode reads (S * D * elt bytes), in random order -- and of 8 KiB tiles."""
+    c = wl.cfg
+    elt = 4 if c.dtype == "f32" else 2
+    tile = c.block_size * c.head_dim * elt
+    pool_bytes = c.num_blocks * c.num_kv_heads * tile
+    total = (2 * pool_bytes) // 32768 * 32768
+    buf = torch.empty(total, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    res = {"buffer_bytes": total}
+
+    def gbps(nbytes, us):
+        return round(nbytes / (us * 1e-6) / 1e9, 2)
+
+    for nt in (True, False):
+        st = launch_stats(torch, lambda: pk.probe_stream_read(buf, sink, nontemporal=nt),
+                          launches, reps, warmup=3)
+        res[f"stream{'_nt' if nt else ''}_GB_per_s"] = gbps(total, st["median_us"])
+    rng = np.random.default_rng(seed)
+    if tile in (4096, 8192):
+        # the tiles decode reads: K and V of every used (block, kv head), in random order
+        S = c.block_size
+        offs = []
+        for i, L in enumerate(wl.context_lens):
+            nb = -(-int(L) // S)
+            b = wl.block_tables[i, :nb].astype(np.int64)
+            t = (b[:, None] * c.num_kv_heads + np.arange(c.num_kv_heads)[None, :]).ravel()
+            offs.append(t * tile)
+            offs.append(pool_bytes + t * tile)
+        offs = np.concatenate(offs)
+        offs = offs[rng.permutation(len(offs))]
+        n_bytes = len(offs) * tile
+        d_offs = torch.from_numpy(offs).cuda()
+        for nt in (True, False):
+            st = launch_stats(torch, lambda: pk.probe_tile_gather(buf, d_offs, tile, sink,
+                                                                  nontemporal=nt),
+                              launches, reps, warmup=3)
+            res[f"gather_{tile // 1024}KiB{'_nt' if nt else ''}_GB_per_s"] = \
+                gbps(n_bytes, st["median_us"])
+        res["gather_tiles"] = len(offs)
+    # 8 KiB tiles at random distinct 8 KiB-aligned places, the same number of bytes
+    n8 = max(1, min(total // 8192, (len(offs) * tile if tile in (4096, 8192) else total // 2)
+                    // 8192))
+    offs8 = rng.choice(total // 8192, size=n8, replace=False).astype(np.int64) * 8192
+    d8 = torch.from_numpy(offs8).cuda()
+    st = launch_stats(torch, lambda: pk.probe_tile_gather(buf, d8, 8192, sink, nontemporal=True),
+                      launches, reps, warmup=3)
+    res["gather_8KiB_random_nt_GB_per_s"] = gbps(n8 * 8192, st["median_us"])
+    del buf, d8
+    torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------------ prefill
+
 def prefill_cpu_baseline(wl, one_s: float):
     """The prefill oracle (fp64 numpy, one thread) over whole sequences of the workload,
-    longest contexts first, until about one_s seconds have run."""
+    longest contexts first, until about one_s seconds have run. Returns the figures and the
+    expected output rows of the sequences it ran."""
     from threadpoolctl import threadpool_limits
 
     import oracle
     c = wl.cfg
     done, flops, dt = 0, 0, 0.0
+    expected = {}
     with threadpool_limits(limits=1):
         for i in np.argsort(-wl.context_lens, kind="stable"):
             if dt >= one_s:
@@ -232,16 +549,17 @@ def prefill_cpu_baseline(wl, one_s: float):
             L, Q = int(wl.context_lens[i]), int(wl.query_lens[i])
             r0 = int(wl.query_start[i])
             t0 = time.perf_counter()
-            oracle.prefill(wl.q_prefill[r0:r0 + Q], wl.k_cache, wl.v_cache,
-                           wl.block_tables[i:i + 1], wl.context_lens[i:i + 1],
-                           np.array([0, Q], dtype=np.int32), c.scale, c.num_kv_heads, c.dtype)
+            expected[int(i)] = oracle.prefill(
+                wl.q_prefill[r0:r0 + Q], wl.k_cache, wl.v_cache, wl.block_tables[i:i + 1],
+                wl.context_lens[i:i + 1], np.array([0, Q], dtype=np.int32), c.scale,
+                c.num_kv_heads, c.dtype)
             dt += time.perf_counter() - t0
             done += 1
             flops += (2 * (L - Q) + Q + 1) * Q // 2 * c.num_heads * c.head_dim * 4
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} of {c.num_seqs} sequences (longest contexts first), fp64 numpy "
                       f"prefill on one thread, {dt:.1f} s",
-            "cpu": cpu_model(), "host_cpus": os.cpu_count()}
+            "cpu": cpu_model(), "host_cpus": os.cpu_count()}, expected
 
 
 def prefill_main(args):
@@ -256,7 +574,8 @@ def prefill_main(args):
     if args.block_size and args.block_size != cfg.block_size:
         cfg = cfg.with_block_size(args.block_size)
     wl = W.generate(cfg, poison="zero")
-    cpu = None if args.no_cpu_baseline else prefill_cpu_baseline(wl, args.cpu_seconds)
+    cpu, expected = (None, None) if args.no_cpu_baseline else \
+        prefill_cpu_baseline(wl, args.cpu_seconds)
     pk.load()
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -316,10 +635,27 @@ def prefill_main(args):
                      "ms_per_launch": round(launch_ms, 5), "flops_per_launch": fl},
         "kernels": kernels,
     }
+    ok = True
     if cpu is not None:
         line["cpu_baseline"] = cpu
+        got = out.float().cpu().numpy().astype(np.float64)
+        err = 0.0
+        for i, ref in expected.items():
+            r0, Q = int(wl.query_start[i]), int(wl.query_lens[i])
+            d = np.abs(got[r0:r0 + Q] - ref)
+            err = max(err, float("inf") if np.isnan(d).any() else float(d.max()))
+        ok = err <= TOL[cfg.dtype]
+        line["parity"] = {"max_abs_err": err, "tol": TOL[cfg.dtype], "ok": bool(ok),
+                          "compared": f"every query row of the {len(expected)} sequences the "
+                                      "cpu_baseline leg ran",
+                          "oracle": "fp64 numpy, the cpu_baseline leg"}
     print(json.dumps(line), flush=True)
+    if not ok:
+        print("[bench] output differs from the oracle beyond tolerance", file=sys.stderr)
+        sys.exit(3)
 
+
+# ------------------------------------------------------------------ decode
 
 def main():
     args = parse()
@@ -346,7 +682,7 @@ def main():
     shard = None
     if args.shard:
         kind, _, n = args.shard.partition(":")
-        n = int(n)
+        n = int(n) if n.isdigit() else 0
         if kind == "kv" and n >= 1 and cfg.num_kv_heads % n == 0:
             cfg = cfg.replace(num_heads=cfg.num_heads // n, num_kv_heads=cfg.num_kv_heads // n)
         elif kind == "seq" and n >= 1 and cfg.num_seqs % n == 0:
@@ -359,16 +695,23 @@ def main():
         cfg = cfg.replace(description=f"{cfg.description}; one GPU's share of {args.shard} "
                                       f"({cfg.num_seqs} seqs, {cfg.num_heads}/"
                                       f"{cfg.num_kv_heads} heads)")
+    if args.layout != "paged" and (cfg.prefix_len or args.unfused):
+        print(f"--layout {args.layout}: the contiguous layouts hold no shared blocks and take "
+              "the fused cache write", file=sys.stderr)
+        sys.exit(2)
     t0 = time.time()
     wl = W.generate(cfg, poison="zero")
-    print(f"[bench] generated {name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    if args.layout != "paged":
+        wl = W.contiguous_layout(wl)
+    print(f"[bench] generated {name} ({args.layout}) in {time.time() - t0:.1f}s",
+          file=sys.stderr, flush=True)
 
-    cpu = None
+    cpu = expected = None
     if not args.no_cpu_baseline:
         workers = args.cpu_workers or min(16, os.cpu_count() or 1)
         print(f"[bench] timing the oracle on the CPU (1 thread, then {workers} processes)",
               file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, args.cpu_seconds, args.cpu_all_seconds, workers)
+        cpu, expected = cpu_baseline(wl, args.cpu_seconds, args.cpu_all_seconds, workers)
 
     import torch
 
@@ -377,76 +720,20 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
-    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
 
-    def dev(a, bf=False):
-        a = np.ascontiguousarray(a)
-        if bf:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(a).cuda()
-
-    bf = cfg.dtype == "bf16"
-    q, kc, vc = dev(wl.q, bf), dev(wl.k_cache, bf), dev(wl.v_cache, bf)
-    key, value = dev(wl.key, bf), dev(wl.value, bf)
-    slots, bt, lens = dev(wl.slot_mapping), dev(wl.block_tables), dev(wl.context_lens)
-    mapping = dev(wl.block_mapping.reshape(-1, 2))
     fused = not args.unfused
-    # Blocks shared by several sequences (a common prefix): plan groups that read each shared
-    # tile once for all their members (host scheduler input, like the work list).
-    plan = None
-    if args.shared_prefix == "on" or (args.shared_prefix == "auto" and cfg.prefix_len and not P):
-        from paged_kv_cache_247_amd import sharing
-        plan = sharing.plan(wl.block_tables, wl.context_lens, cfg.block_size,
-                            wl.max_context_len, cfg.group, newest_outside=fused)
-        if plan is None and args.shared_prefix == "on":
-            print("--shared-prefix on: no blocks are shared", file=sys.stderr)
-            sys.exit(2)
-    if plan is not None:
-        P, kernel, cached = plan.partition_size, "mfma", True
-        groups = dev(plan.groups)
-        order = dev(plan.work_items)
-    else:
-        # Host-side scheduler input: the units with work, largest first.
-        order = dev(wl.work_items(P))
-    out = torch.empty((cfg.num_seqs, cfg.num_heads, cfg.head_dim), dtype=dt, device="cuda")
-    ws = pk.partition_workspace(cfg.num_seqs, cfg.num_heads, cfg.head_dim, wl.max_context_len,
-                                P, q.device) if P else None
+    try:
+        s = build_step(torch, pk, wl, kernel, P, cached, args.shared_prefix, fused, args.layout)
+    except ValueError as e:
+        print(str(e), file=sys.stderr)
+        sys.exit(2)
+    P, kernel, cached = s.P, s.kernel, s.cached
     maxlen = wl.max_context_len
-    has_copy = len(wl.block_mapping) > 0
-    ev = []
-
-    def decode():
-        # With fused=True the decode launch also writes each sequence's newest K/V to its slot.
-        if plan is not None:  # the groups and every other unit in one launch
-            pk.paged_attention_decode_shared(q, kc, vc, bt, lens, groups, maxlen, cfg.scale, P,
-                                             ws, work_items=order,
-                                             new_key=key if fused else None,
-                                             new_value=value if fused else None)
-            return
-        pk.paged_attention_decode(None if P else out, q, kc, vc, bt, lens, maxlen, cfg.scale,
-                                  P, ws, kernel=kernel, work_items=order, cached_kv=cached,
-                                  new_key=key if fused else None,
-                                  new_value=value if fused else None)
-
     # When the step is the decode launch alone, one event pair brackets the whole timed region
     # and the mean launch duration is its span over the steps: events between the launches
     # would cost the loop time of their own (about 7 us per step on the GQA batch).
-    alone = fused and not has_copy and not P
-
-    def step(record):
-        if has_copy:
-            pk.copy_blocks([kc], [vc], mapping)
-        if not fused:
-            pk.reshape_and_cache(key, value, kc, vc, slots)
-        if record and not alone:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-        decode()
-        if record and not alone:
-            e1.record()
-            ev.append((e0, e1))
-        if P:
-            pk.paged_attention_reduce(out, ws, lens, P)
+    alone = fused and not s.has_copy and not P
+    ev = []
 
     # Each kernel on its own, back to back (all of them are idempotent on these inputs). This
     # runs first: its ~0.1 s of sustained launches also brings the GPU out of idle before the
@@ -455,34 +742,34 @@ def main():
     tile = cfg.num_kv_heads * cfg.block_size * cfg.head_dim * elt
     n_new = int((wl.slot_mapping >= 0).sum())
     kernels = {"paged_attention_decode": dict(
-        launch_stats(torch, decode, args.launches, args.reps),
-        kv_bytes=wl.kv_bytes())}
-    kernels["reshape_and_cache"] = dict(
-        launch_stats(torch, lambda: pk.reshape_and_cache(key, value, kc, vc, slots),
-                     args.launches, args.reps),
-        bytes=n_new * cfg.num_kv_heads * cfg.head_dim * elt * 2 * 2)
-    if has_copy:
+        launch_stats(torch, s.decode, args.launches, args.reps), kv_bytes=wl.kv_bytes())}
+    if args.layout == "paged":
+        kernels["reshape_and_cache"] = dict(
+            launch_stats(torch, lambda: pk.reshape_and_cache(s.key, s.value, s.kc, s.vc,
+                                                             s.slots),
+                         args.launches, args.reps),
+            bytes=n_new * cfg.num_kv_heads * cfg.head_dim * elt * 2 * 2)
+    if s.has_copy:
         kernels["copy_blocks"] = dict(
-            launch_stats(torch, lambda: pk.copy_blocks([kc], [vc], mapping), args.launches,
-                         args.reps),
+            launch_stats(torch, lambda: pk.copy_blocks([s.kc], [s.vc], s.mapping),
+                         args.launches, args.reps),
             bytes=len(wl.block_mapping) * tile * 2 * 2)
     if P:
         kernels["paged_attention_reduce"] = dict(
-            launch_stats(torch, lambda: pk.paged_attention_reduce(out, ws, lens, P),
-                         args.launches, args.reps))
-    for k, s in kernels.items():
-        b = s.get("kv_bytes", s.get("bytes"))
+            launch_stats(torch, s.reduce, args.launches, args.reps))
+    for k, st in kernels.items():
+        b = st.get("kv_bytes", st.get("bytes"))
         if b:
-            s["GB_per_s"] = round(b / (s["median_us"] * 1e-6) / 1e9, 2)
+            st["GB_per_s"] = round(b / (st["median_us"] * 1e-6) / 1e9, 2)
 
     for _ in range(args.warmup):
-        step(False)
+        s.step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     span = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     span[0].record()
     for _ in range(args.steps):
-        step(True)
+        s.step(None if alone else ev)
     span[1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -493,18 +780,26 @@ def main():
         dec_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
     print(f"[bench] {args.steps} steps, {ms_step:.4f} ms/step, decode {dec_ms:.4f} ms/launch",
           file=sys.stderr, flush=True)
+    check = None
+    if expected is not None:
+        check = parity(s.out, expected, cfg.dtype,
+                       f"the timed step's output, all {cfg.num_seqs} sequences x "
+                       f"{cfg.num_heads} heads x {cfg.head_dim}")
+        print(f"[bench] max abs err against the oracle {check['max_abs_err']:.3g} "
+              f"(tolerance {check['tol']})", file=sys.stderr, flush=True)
 
     kvb = wl.kv_bytes()
-    family = "mfma" if (kernel == "mfma" or (kernel == "auto" and cfg.dtype != "f32"
-                                             and cfg.group >= 4)) else "valu"
-    # The recorded counters belong to the workload as defined (its block size, whole batch).
-    traffic = None if shard or cfg.block_size != W.CONFIGS[name].block_size \
-        else counter_traffic(KERNEL_SOURCES[family], name, plan is not None)
+    # The recorded counters belong to the workload as defined (its block size, whole batch,
+    # paged layout).
+    traffic = None if shard or args.layout != "paged" or \
+        cfg.block_size != W.CONFIGS[name].block_size \
+        else counter_traffic(KERNEL_SOURCES[s.family], name, s.plan is not None)
     value = kvb / (ms_step * 1e-3) / 1e9
-    ukvb = wl.unique_kv_bytes() if has_copy else kvb
+    rb = roofline_bytes(wl)
     # With shared prefix blocks the logical bytes count the prefix once per sequence, but it is
-    # served from cache after the first read: the HBM roofline takes the unique bytes.
-    achieved = ukvb / (dec_ms * 1e-3) / 1e9
+    # served from cache after the first read: the HBM roofline takes the unique bytes (without
+    # the copy-on-write copies, which are a launch of their own).
+    achieved = rb / (dec_ms * 1e-3) / 1e9
     line = {
         "metric": "paged decode KV-read GB/s (% of MI355X HBM peak) + attended tokens/s",
         "value": round(value, 2),
@@ -524,11 +819,12 @@ def main():
                    "num_blocks": cfg.num_blocks, "seed": cfg.seed,
                    "context_tokens": wl.total_tokens, "max_context_len": maxlen,
                    "kernel": kernel, "partition_size": P, "cached_kv": cached,
-                   "shared_prefix": None if plan is None else {
-                       "groups": len(plan.groups), "partition_size": P,
-                       "members": int((plan.groups >= 0).sum())},
+                   "layout": args.layout,
+                   "shared_prefix": None if s.plan is None else {
+                       "groups": len(s.plan.groups), "partition_size": P,
+                       "members": int((s.plan.groups >= 0).sum())},
                    "fused_cache_write": fused, "kv_bytes": kvb,
-                   "unique_kv_bytes": ukvb, "shard": shard},
+                   "unique_kv_bytes": wl.unique_kv_bytes(), "shard": shard},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "attended_tokens_per_s": round(wl.total_tokens / (ms_step * 1e-3), 1),
         "head_token_pairs_per_s": round(cfg.num_heads * wl.total_tokens / (ms_step * 1e-3), 1),
@@ -536,11 +832,42 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
                      "kernel": ("paged_attention_decode_shared (mfma: groups and other units)"
-                                if plan is not None else f"paged_attention_decode ({family})"),
-                     "ms_per_launch": round(dec_ms, 5), "bytes_per_launch": ukvb,
+                                if s.plan is not None
+                                else f"paged_attention_decode ({s.family})"),
+                     "ms_per_launch": round(dec_ms, 5), "bytes_per_launch": rb,
                      "logical_GB_per_s": round(kvb / (dec_ms * 1e-3) / 1e9, 2)},
         "kernels": kernels,
+        "parity": check,
     }
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+
+    default_run = (name == "c3" and args.layout == "paged" and not shard and not args.unfused
+                   and args.block_size in (None, W.CONFIGS[name].block_size)
+                   and args.kernel is None and args.partition_size is None)
+    if default_run and not args.no_extras:
+        paged_out = s.out.clone()
+        paged_us = kernels["paged_attention_decode"]["median_us"]
+        s.release()
+        reps, launches = 3, 50
+        print("[bench] read ceiling", file=sys.stderr, flush=True)
+        ceil = read_ceiling(torch, pk, wl, reps, 20)
+        g = ceil.get("gather_4KiB_nt_GB_per_s")
+        ceil["decode_frac_of_gather_ceiling"] = round(achieved / g, 4) if g else None
+        ceil["decode_frac_of_stream_ceiling"] = round(achieved / ceil["stream_nt_GB_per_s"], 4)
+        line["read_ceiling"] = ceil
+        print("[bench] paging cost", file=sys.stderr, flush=True)
+        line["paging_cost"] = paging_cost(torch, pk, wl, paged_us, paged_out, reps, launches)
+        del paged_out
+        wl = None
+        if not args.no_cpu_baseline:  # each workload's output is checked against the oracle
+            line["configs"] = {}
+            for cname, p_over in CONFIG_BLOCK:
+                key = cname if p_over is None else f"{cname}_p{p_over}"
+                line["configs"][key] = config_entry(torch, pk, cname, p_over, reps, launches)
+            line["configs"]["c3"] = "the headline figures of this line"
+    else:
+        s.release()
     if args.copy_calibration_gib > 0:
         n = int(args.copy_calibration_gib * (1 << 30)) // 4
         a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -548,9 +875,14 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         line["copy_calibration_bytes"] = n * 4
-    if cpu is not None:
-        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
+    bad = [k for k, e in line.get("configs", {}).items()
+           if isinstance(e, dict) and not e["parity_ok"]]
+    if (check is not None and not check["ok"]) or bad:
+        print(f"[bench] output differs from the oracle beyond tolerance "
+              f"({'main' if check is not None and not check['ok'] else ''} {' '.join(bad)})",
+              file=sys.stderr)
+        sys.exit(3)
 
 
 if __name__ == "__main__":

@@ -365,10 +365,34 @@ int32_t pkv_vmm_pool_blocks_per_seq(const pkv_vmm_pool* pool);
 size_t pkv_vmm_pool_page_bytes(const pkv_vmm_pool* pool);
 size_t pkv_vmm_pool_mapped_bytes(const pkv_vmm_pool* pool); /* K + V physically backed */
 
+/* ---- Read-bandwidth probes (measurement only) ----
+ *
+ * A paged KV read fetches whole (block, kv head) tiles of S * D contiguous elements from
+ * blocks anywhere in the pool (Qualiteg post, item 1-2; vAttention section 3.1: the kernel
+ * reads non-contiguous KV-cache blocks). These kernels do those loads and nothing else, so
+ * their bandwidth is the ceiling a paged decode can approach on this device. Neither reads
+ * anything back to the host: time them with events on `stream`. sink: device, 4-byte
+ * aligned, one word that is written only if the folded data equals a fixed pattern (it
+ * keeps the loads from being optimised away). nontemporal != 0 uses the streaming cache
+ * policy of the decode kernels' K/V loads. workgroups: grid size (256 threads each; a few
+ * per compute unit fills the device). */
+/* Read bytes (a positive multiple of 32768) of buf (device, 16-byte aligned) once, in 32 KiB
+ * chunks spread round-robin over the workgroups. */
+pkv_status pkv_probe_stream_read(const void* buf, size_t bytes, int32_t nontemporal,
+                                 int32_t workgroups, uint32_t* sink, void* stream);
+/* Read num_tiles tiles of tile_bytes (4096 or 8192) at the byte offsets tile_offsets
+ * (device int64 [num_tiles]) into base (device, base_bytes long), eight tiles in flight per
+ * workgroup, in list order. A tile that does not lie inside [0, base_bytes) or whose offset is
+ * not a multiple of 16 is skipped. */
+pkv_status pkv_probe_tile_gather(const void* base, size_t base_bytes,
+                                 const int64_t* tile_offsets, int32_t num_tiles,
+                                 int32_t tile_bytes, int32_t nontemporal, int32_t workgroups,
+                                 uint32_t* sink, void* stream);
+
 const char* pkv_status_string(pkv_status s);
 int pkv_last_hip_error(void);              /* hipError_t behind the last PKV_ERR_HIP */
 const char* pkv_last_error_message(void);  /* thread-local text of the last failure */
-int pkv_abi_version(void);                 /* 2: decode_shared takes a work list and new rows */
+int pkv_abi_version(void);                 /* 3: read-bandwidth probes */
 
 #ifdef __cplusplus
 }

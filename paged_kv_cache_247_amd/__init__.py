@@ -8,11 +8,13 @@ from ._lib import (KERNELS, BlockManager, DeviceRegion, OutOfBlocks, PagedKVErro
                    num_partitions, paged_attention, paged_attention_decode,
                    paged_attention_decode_shared, paged_attention_shared,
                    paged_attention_prefill, paged_attention_reduce, partition_workspace,
-                   prefill_tile_tokens, reshape_and_cache, v_block_shape)
+                   prefill_tile_tokens, probe_stream_read, probe_tile_gather,
+                   reshape_and_cache, v_block_shape)
 
 __all__ = ["KERNELS", "BlockManager", "DeviceRegion", "OutOfBlocks", "PagedKVError", "VmmPool",
            "auto_partition_size", "copy_blocks", "load", "swap_blocks",
            "num_partitions", "paged_attention", "paged_attention_decode",
            "paged_attention_decode_shared", "paged_attention_shared",
            "paged_attention_prefill", "paged_attention_reduce", "partition_workspace",
-           "prefill_tile_tokens", "reshape_and_cache", "v_block_shape"]
+           "prefill_tile_tokens", "probe_stream_read", "probe_tile_gather",
+           "reshape_and_cache", "v_block_shape"]

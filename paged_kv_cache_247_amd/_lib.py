@@ -77,6 +77,8 @@ SIGNATURES = {
     "pkv_vmm_pool_blocks_per_seq": (_I, [_P]),
     "pkv_vmm_pool_page_bytes": (_Z, [_P]),
     "pkv_vmm_pool_mapped_bytes": (_Z, [_P]),
+    "pkv_probe_stream_read": (_I, [_P, _Z, _I, _I, _P, _P]),
+    "pkv_probe_tile_gather": (_I, [_P, _Z, _P, _I, _I, _I, _I, _P, _P]),
 }
 
 
@@ -134,7 +136,7 @@ class OutOfBlocks(PagedKVError):
 
 PKV_ERR_HIP = 3
 PKV_ERR_NO_BLOCKS = 4
-ABI_VERSION = 2  # the argument lists in SIGNATURES
+ABI_VERSION = 3  # the argument lists in SIGNATURES
 
 
 def _check(status: int):
@@ -693,3 +695,27 @@ def swap_blocks(src_k, src_v, dst_k, dst_v, pairs, to_device: bool):
     _check(load().pkv_swap_blocks(_ptr(src_k), _ptr(src_v), src_k.shape[0], _ptr(dst_k),
                                   _ptr(dst_v), dst_k.shape[0], pairs.ctypes.data, len(pairs),
                                   block_bytes, 1 if to_device else 0, _stream(dev)))
+
+
+def probe_stream_read(buf: torch.Tensor, sink: torch.Tensor, nontemporal: bool = True,
+                      workgroups: int = 2048):
+    """pkv_probe_stream_read over all of buf (a contiguous device tensor whose size in bytes is
+    a multiple of 32 KiB). sink: a device int32 tensor of at least one element."""
+    _need(buf, "buf")
+    _need(sink, "sink", torch.int32, 1, buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _check(load().pkv_probe_stream_read(_ptr(buf), nbytes, int(bool(nontemporal)),
+                                        int(workgroups), _ptr(sink), _stream(buf)))
+
+
+def probe_tile_gather(buf: torch.Tensor, offsets: torch.Tensor, tile_bytes: int,
+                      sink: torch.Tensor, nontemporal: bool = True, workgroups: int = 2048):
+    """pkv_probe_tile_gather: read the tiles of tile_bytes at the byte offsets (device int64
+    [n]) into buf, in list order."""
+    _need(buf, "buf")
+    _need(offsets, "offsets", torch.int64, 1, buf.device)
+    _need(sink, "sink", torch.int32, 1, buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _check(load().pkv_probe_tile_gather(_ptr(buf), nbytes, _ptr(offsets), offsets.shape[0],
+                                        int(tile_bytes), int(bool(nontemporal)),
+                                        int(workgroups), _ptr(sink), _stream(buf)))

@@ -284,8 +284,10 @@ class Workload:
         c = self.cfg
         return self.total_tokens * c.num_kv_heads * c.head_dim * elt_bytes(c.dtype) * 2
 
-    def unique_kv_bytes(self) -> int:
-        """Distinct valid (block, kv head) rows touched by decode, K and V, plus CoW copies."""
+    def unique_kv_bytes(self, include_copies: bool = True) -> int:
+        """Distinct valid (block, kv head) rows touched by decode, K and V; by default plus the
+        bytes the copy-on-write copies read (a step's unique reads), without them the decode
+        launch's own unique reads."""
         c = self.cfg
         S = c.block_size
         seen = {}
@@ -296,7 +298,7 @@ class Workload:
                 rows = S if j < nb - 1 else int(L) - S * (nb - 1)
                 seen[b] = max(seen.get(b, 0), rows)
         row_bytes = c.num_kv_heads * c.head_dim * elt_bytes(c.dtype) * 2
-        copy_bytes = len(self.block_mapping) * S * row_bytes
+        copy_bytes = len(self.block_mapping) * S * row_bytes if include_copies else 0
         return sum(seen.values()) * row_bytes + copy_bytes
 
 

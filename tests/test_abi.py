@@ -32,11 +32,11 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
-    assert len(names) == 37, names
+    assert len(names) == 39, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES), "binding prototypes out of step with the header"
-    assert lib.pkv_abi_version() == 2
+    assert lib.pkv_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -219,6 +219,22 @@ def prefill(lib, **kw):
 ])
 def test_prefill_validation(lib, kw, status):
     assert prefill(lib, **kw) == status
+
+
+def test_probe_validation(lib):
+    """The read-bandwidth probes reject bad sizes and pointers before any HIP call."""
+    st, g = lib.pkv_probe_stream_read, lib.pkv_probe_tile_gather
+    assert st(A16, 0, 1, 64, A16, None) == INVALID
+    assert st(A16, 32768 + 16, 1, 64, A16, None) == INVALID  # not whole 32 KiB chunks
+    assert st(A16, 32768, 1, 0, A16, None) == INVALID
+    assert st(A16 + 4, 32768, 1, 64, A16, None) == INVALID
+    assert st(A16, 32768, 1, 64, None, None) == INVALID
+    assert g(A16, 1 << 20, A16, 4, 2048, 1, 64, A16, None) == UNSUPPORTED
+    assert g(A16, 1 << 20, A16, -1, 4096, 1, 64, A16, None) == INVALID
+    assert g(A16, 1 << 20, A16, 4, 4096, 1, 0, A16, None) == INVALID
+    assert g(A16, 1 << 20, A16 + 4, 4, 4096, 1, 64, A16, None) == INVALID
+    assert g(A16, 1 << 20, A16, 4, 8192, 1, 64, None, None) == INVALID
+    assert g(A16, 1 << 20, A16, 0, 4096, 1, 64, A16, None) == OK  # nothing to read
 
 
 def test_prefill_tile_tokens(lib):

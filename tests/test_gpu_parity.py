@@ -327,7 +327,9 @@ def test_partials_match_oracle(name, kernel, P):
     written = ~np.isnan(em)
     assert np.array_equal(written, ~np.isnan(gm)), "written partitions differ from the oracle's"
     tol = TOL[c.dtype]
-    assert np.abs(gm[written] - em[written]).max() <= 1e-4
+    err_m = np.abs(gm[written] - em[written]).max()
+    print(f"[gpu] max_logits max abs err {err_m:.3g}", file=sys.stderr, flush=True)
+    assert err_m <= 1e-5  # the partition maximum is a logit, not a rounded output
     assert (np.abs(gl[written] - el[written]) / el[written]).max() <= max(tol, 1e-5)
     assert np.abs(go[written] - eo[written]).max() <= tol
 
@@ -335,10 +337,11 @@ def test_partials_match_oracle(name, kernel, P):
 # ------------------------------------------------------------------ full-size workloads
 
 @pytest.mark.parametrize("name,P_over", [("c2", None), ("c3", None), ("c4", None), ("c5", None),
-                                         ("c5", 512)])
-def test_full_size_sampled_against_oracle(name, P_over):
-    """The full workload in the launch configuration the benchmark times (and the long-context
-    batch also in the 512-token partitions its statement names)."""
+                                         ("c5", 2048)])
+def test_full_size_against_oracle(name, P_over):
+    """The full workload in the launch configuration the benchmark times (the long-context
+    batch in the 512-token partitions its statement names, and also in 2048-token ones), with
+    every sequence and head compared with the oracle."""
     from bench import LAUNCH
     kernel, P, cached = LAUNCH[name]
     P = P if P_over is None else P_over
@@ -347,14 +350,16 @@ def test_full_size_sampled_against_oracle(name, P_over):
     dev = upload(wl)
     out = out_f64(run_step(dev, wl, kernel=kernel, partition_size=P, order=wl.work_items(P),
                            fused=True, cached_kv=cached))
-    assert np.isfinite(out).all()
-    L = wl.context_lens
-    rng = np.random.default_rng(0)
-    seqs = sorted({int(L.argmax()), int(L.argmin()), *rng.choice(len(L), 6, replace=False)})
     del dev
-    ref = oracle_out(wl, seqs)
-    err = oracle.max_abs_err(out[seqs], ref)
-    assert err <= TOL[cfg.dtype], f"{name}: {err}"
+    ref = oracle_out(wl)
+    per_seq = np.abs(out - ref).reshape(cfg.num_seqs, -1).max(axis=1)
+    worst = int(np.nanargmax(np.where(np.isnan(per_seq), np.inf, per_seq)))
+    L = wl.context_lens
+    detail = (f"{name} P={P}: worst sequence {worst} (L={int(L[worst])}) err {per_seq[worst]}; "
+              f"longest {int(L.argmax())} err {per_seq[L.argmax()]}, shortest "
+              f"{int(L.argmin())} err {per_seq[L.argmin()]}")
+    print(f"[gpu] {detail}", file=sys.stderr, flush=True)
+    assert oracle.max_abs_err(out, ref) <= TOL[cfg.dtype], detail
 
 
 def test_auto_partition_size_matches_oracle():

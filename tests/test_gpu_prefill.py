@@ -111,13 +111,13 @@ def test_prefill_edge_lengths(S):
 
 
 @pytest.mark.parametrize("name", ["p1", "p2"])
-def test_full_size_sampled_against_oracle(name):
-    """The full-size workload in the benchmark's launch (largest units first), checked on
-    sampled sequences."""
+def test_full_size_against_oracle(name):
+    """The full-size workload in the benchmark's launch (largest units first), every query
+    token of every sequence compared with the oracle."""
     wl = W.generate(W.PREFILL[name])
     tile = pk.prefill_tile_tokens(wl.cfg.num_heads, wl.cfg.num_kv_heads)
     got = out_f64(run_prefill(wl, order=wl.prefill_work_items(tile)))
-    assert not np.isnan(got).any()
-    seqs = np.random.default_rng(1).choice(wl.cfg.num_seqs, size=2, replace=False)
-    rows, ref = oracle_prefill(wl, seqs)
-    assert oracle.max_abs_err(got[rows], ref) <= TOL[wl.cfg.dtype]
+    rows, ref = oracle_prefill(wl)
+    err = oracle.max_abs_err(got[rows], ref)
+    print(f"[gpu] {name}: {len(rows)} query rows, max abs err {err}", file=sys.stderr, flush=True)
+    assert err <= TOL[wl.cfg.dtype]

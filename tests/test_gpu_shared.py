@@ -85,23 +85,28 @@ def test_grouped_partials_match_the_oracle():
     gm, gl, go = (t.cpu().numpy().astype(np.float64) for t in ws)
     members = plan.groups[plan.groups >= 0]
     assert np.isfinite(gm[members, :, 0]).all()
-    assert np.abs(gm[members, :, 0] - em[members, :, 0]).max() <= 1e-4
+    err_m = np.abs(gm[members, :, 0] - em[members, :, 0]).max()
+    print(f"[gpu] grouped max_logits max abs err {err_m:.3g}", file=sys.stderr, flush=True)
+    assert err_m <= 1e-5
     assert (np.abs(gl[members, :, 0] - el[members, :, 0]) / el[members, :, 0]).max() <= TOL["bf16"]
     assert np.abs(go[members, :, 0] - eo[members, :, 0]).max() <= TOL["bf16"]
     assert np.isnan(gm[:, :, 1:]).all(), "only partition 0 is written"
 
 
-def test_full_size_sampled_against_oracle():
+def test_full_size_against_oracle():
+    """The prefix-shared batch in the benchmark's launch (groups beside the other units), every
+    sequence compared with the oracle."""
     wl = W.generate(W.CONFIGS["c4"])
     c = wl.cfg
     plan = sharing.plan(wl.block_tables, wl.context_lens, c.block_size, wl.max_context_len,
                         c.group)
     out = out_f64(shared_step(wl, plan)[0])
-    assert np.isfinite(out).all()
-    seqs = sorted({0, 63, 64, 255, *np.random.default_rng(0).choice(c.num_seqs, 4, replace=False)})
-    err = oracle.max_abs_err(out[seqs], oracle_out(wl, seqs))
-    assert err <= TOL[c.dtype], f"max abs err {err}"
-
+    ref = oracle_out(wl)
+    per_seq = np.abs(out - ref).reshape(c.num_seqs, -1).max(axis=1)
+    worst = int(np.nanargmax(np.where(np.isnan(per_seq), np.inf, per_seq)))
+    detail = f"worst sequence {worst} (L={int(wl.context_lens[worst])}) err {per_seq[worst]}"
+    print(f"[gpu] c4 grouped: {detail}", file=sys.stderr, flush=True)
+    assert oracle.max_abs_err(out, ref) <= TOL[c.dtype], detail
 
 
 def _workspace(wl, P):
