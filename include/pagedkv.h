@@ -196,6 +196,32 @@ pkv_status pkv_paged_attention_decode_shared(
     int32_t num_blocks, float scale, pkv_dtype dtype, int32_t partition_size,
     float* max_logits, float* exp_sums, float* tmp_out, void* stream);
 
+/* Bytes of the library-owned partition workspace of pkv_paged_attention_decode_static (each
+ * device the library runs on holds its own copy until the process ends). */
+#define PKV_STATIC_WORKSPACE_BYTES ((size_t)80 << 20)
+
+/* For callers that cannot allocate device memory -- code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc: split-context decode followed by the merge, exactly
+ * pkv_paged_attention_decode with partition_size > 0 and then pkv_paged_attention_reduce into
+ * `out`, with the partition workspace (max_logits | exp_sums | tmp_out, each part 256-byte
+ * aligned) in a static device array of PKV_STATIC_WORKSPACE_BYTES instead of caller memory.
+ * It calls no hipMalloc or hipFree; the first call on a device looks up that device's array.
+ * Arguments as for pkv_paged_attention_decode (kernel family AUTO, no options); partition_size
+ * must be > 0. A shape whose workspace (2 * round_up(4 * B * H * NP, 256) + 4 * B * H * NP * D
+ * bytes, NP = ceil(max_context_len / partition_size)) exceeds PKV_STATIC_WORKSPACE_BYTES is
+ * rejected with PKV_ERR_INVALID_ARGUMENT before anything is enqueued (the long-context batch of
+ * 32 sequences, 64 heads, D 128 up to 32768 positions fits at partitions of 512).
+ * All calls on one device share its array, and no part of it needs to start at zero: calls
+ * that overlap on one device (on different streams or host threads) race and give undefined
+ * results; calls queued on one stream are ordered. */
+pkv_status pkv_paged_attention_decode_static(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* work_items, int32_t num_work_items, int32_t max_context_len,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, float scale, pkv_dtype dtype,
+    int32_t partition_size, void* stream);
+
 /* Merge split-context partitions: for each (i, h) with n = ceil(L_i / partition_size)
  * partitions, M = max_p max_logits, w_p = exp_sums_p * exp(max_logits_p - M),
  * out = sum_p w_p tmp_out_p / sum_p w_p (a zero row when n = 0). The merge is an exact
@@ -392,7 +418,7 @@ pkv_status pkv_probe_tile_gather(const void* base, size_t base_bytes,
 const char* pkv_status_string(pkv_status s);
 int pkv_last_hip_error(void);              /* hipError_t behind the last PKV_ERR_HIP */
 const char* pkv_last_error_message(void);  /* thread-local text of the last failure */
-int pkv_abi_version(void);                 /* 3: read-bandwidth probes */
+int pkv_abi_version(void);                 /* 4: decode with the static workspace */
 
 #ifdef __cplusplus
 }

@@ -42,6 +42,8 @@ SIGNATURES = {
     "pkv_paged_attention_decode_shared": (_I, [_P, _P, _P, _P, _I, _P, _P, _I, _P, _I, _P, _P,
                                                _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P,
                                                _P, _P]),
+    "pkv_paged_attention_decode_static": (_I, [_P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I,
+                                               _I, _I, _I, _I, _F, _I, _I, _P]),
     "pkv_paged_attention_reduce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pkv_copy_blocks": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pkv_partition_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
@@ -136,7 +138,8 @@ class OutOfBlocks(PagedKVError):
 
 PKV_ERR_HIP = 3
 PKV_ERR_NO_BLOCKS = 4
-ABI_VERSION = 3  # the argument lists in SIGNATURES
+ABI_VERSION = 4  # the argument lists in SIGNATURES
+STATIC_WORKSPACE_BYTES = 80 << 20  # PKV_STATIC_WORKSPACE_BYTES
 
 
 def _check(status: int):
@@ -326,6 +329,41 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         _ptr(v_cache), _ptr(block_tables), MB, _ptr(context_lens), _ptr(work_items),
         0 if work_items is None else work_items.shape[0], int(max_context_len), B, H,
         Hkv, D, S, N, float(scale), _dt(q), int(partition_size), _ptr(ml), _ptr(es), _ptr(to),
+        _stream(q)))
+
+
+def paged_attention_decode_static(out, q, k_cache, v_cache, block_tables, context_lens,
+                                  max_context_len, scale, partition_size, work_items=None):
+    """pkv_paged_attention_decode_static: split-context decode and the merge into `out`, with
+    the partition workspace in the library's static device array (nothing is allocated)."""
+    _need(q, "q", ndim=3)
+    dt = q.dtype
+    B, H, D = q.shape
+    _need(out, "out", dt, 3, q.device)
+    if tuple(out.shape) != (B, H, D):
+        raise ValueError("out must be [B, H, D]")
+    _need(k_cache, "k_cache", dt, 4, q.device)
+    N, Hkv, S, Dk = k_cache.shape
+    if Dk != D:
+        raise ValueError("head_dim of q and k_cache differ")
+    _need(v_cache, "v_cache", dt, 4, q.device)
+    if tuple(v_cache.shape) != (N, *v_block_shape(Hkv, D, S)):
+        raise ValueError(f"v_cache must be {(N, *v_block_shape(Hkv, D, S))}")
+    _need(block_tables, "block_tables", torch.int32, 2, q.device)
+    _need(context_lens, "context_lens", torch.int32, 1, q.device)
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables and context_lens need one row per sequence")
+    if work_items is not None:
+        _need(work_items, "work_items", torch.int32, 1, q.device)
+    MB = block_tables.shape[1]
+    if validating():
+        _contract_check(_contract.check_decode, _host(block_tables), _host(context_lens),
+                        int(max_context_len), S, N, MB, int(partition_size), _host(work_items),
+                        False)
+    _check(load().pkv_paged_attention_decode_static(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), MB,
+        _ptr(context_lens), _ptr(work_items), 0 if work_items is None else work_items.shape[0],
+        int(max_context_len), B, H, Hkv, D, S, N, float(scale), _dt(q), int(partition_size),
         _stream(q)))
 
 

@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libpagedkv.so")
 BLOCK_SIZES = (16, 32, 64, 128, 256)
 PER_BLOCK_SIZE = ("decode_valu.hip", "decode_mfma.hip")
 SOURCES = ["api.cpp", "vmm.cpp", "block_manager.cpp", "cache_ops.hip", *PER_BLOCK_SIZE,
-           "reduce.hip", "prefill.hip", "probe.hip"]
+           "reduce.hip", "prefill.hip", "probe.hip", "static_workspace.hip"]
 # (source, object stem, defines): one unit of parallel compilation each
 UNITS = [(src, f"{os.path.splitext(src)[0]}_s{S}", [f"-DPKV_BLOCK_SIZE={S}"])
          for src in PER_BLOCK_SIZE for S in BLOCK_SIZES] + \

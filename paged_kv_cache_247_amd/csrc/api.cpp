@@ -440,6 +440,6 @@ int pkv_last_hip_error(void) { return t_last_hip; }
 
 const char* pkv_last_error_message(void) { return t_msg; }
 
-int pkv_abi_version(void) { return 3; }
+int pkv_abi_version(void) { return 4; }
 
 }  // extern "C"

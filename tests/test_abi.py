@@ -32,11 +32,11 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
-    assert len(names) == 39, names
+    assert len(names) == 40, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES), "binding prototypes out of step with the header"
-    assert lib.pkv_abi_version() == 3
+    assert lib.pkv_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -219,6 +219,25 @@ def prefill(lib, **kw):
 ])
 def test_prefill_validation(lib, kw, status):
     assert prefill(lib, **kw) == status
+
+
+def test_static_workspace_validation(lib):
+    """Decode with the library's static workspace: split-context only, and shapes whose
+    workspace exceeds the static array are refused before any HIP call."""
+    f = lib.pkv_paged_attention_decode_static
+
+    def call(B=2, H=8, maxlen=64, P=32, D=128, MB=4):
+        return f(A16, A16, A16, A16, A16, MB, A16, None, 0, maxlen, B, H, 2, D, 16, 4096, 0.125,
+                 2, P, None)
+    assert call(P=0) == INVALID
+    assert call(P=-16) == INVALID
+    assert call(H=0) == INVALID
+    # 32 sequences x 64 heads x 64 partitions x (128 + 2) floats fit in 80 MiB ...
+    assert lib.pkv_partition_workspace_bytes(32, 64, 128, 32768, 512) < _lib.STATIC_WORKSPACE_BYTES
+    # ... 64 sequences do not
+    assert call(B=64, H=64, maxlen=32768, P=512, MB=2048) == INVALID
+    assert b"static workspace" in lib.pkv_last_error_message()
+    assert call(B=1 << 20, H=1 << 10, maxlen=1 << 20, P=16, MB=1 << 16) == INVALID  # no overflow
 
 
 def test_probe_validation(lib):
