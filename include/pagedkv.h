@@ -248,7 +248,8 @@ pkv_status pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t
                            int32_t num_blocks, pkv_dtype dtype, void* stream);
 
 /* Bytes of the split-context workspace: 4 * B * H * NPmax * (D + 2); 0 when
- * partition_size <= 0. Carve it as max_logits | exp_sums | tmp_out in that order. */
+ * partition_size <= 0 (or any size is not positive), SIZE_MAX when the product does not fit in
+ * size_t. Carve it as max_logits | exp_sums | tmp_out in that order. */
 size_t pkv_partition_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                      int32_t max_context_len, int32_t partition_size);
 

@@ -47,14 +47,16 @@ pkv_status hip_status(hipError_t e, const char* what) {
 
 bool aligned(const void* p, uintptr_t a) { return p && ((uintptr_t)p % a) == 0; }
 
-bool valid_dtype(pkv_dtype d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16; }
+// Enum arguments are checked as the ints the caller passed (pkv::enum_arg) before they are
+// used as enums.
+bool valid_dtype(int d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16; }
 
-pkv::Dt to_dt(pkv_dtype d) { return static_cast<pkv::Dt>((int)d); }
+pkv::Dt to_dt(int d) { return static_cast<pkv::Dt>(d); }
 
 // Shape checks shared by every entry point.
 pkv_status check_tile(const char* fn, int32_t num_kv_heads, int32_t head_dim,
-                      int32_t block_size, pkv_dtype dtype) {
-  if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID_ARGUMENT, "%s: bad dtype %d", fn, (int)dtype);
+                      int32_t block_size, int dtype) {
+  if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID_ARGUMENT, "%s: bad dtype %d", fn, dtype);
   if (num_kv_heads <= 0) return fail(PKV_ERR_INVALID_ARGUMENT, "%s: num_kv_heads %d", fn, num_kv_heads);
   if (head_dim <= 0 || block_size <= 0)
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: head_dim %d block_size %d", fn, head_dim, block_size);
@@ -73,7 +75,7 @@ pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, 
                        const int32_t* work_items, int32_t num_work_items,
                        int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                       int32_t num_blocks, float scale, pkv_dtype dtype,
+                       int32_t num_blocks, float scale, int dtype,
                        int32_t partition_size, float* max_logits, float* exp_sums,
                        float* tmp_out, void* stream, const int32_t* groups = nullptr,
                        int32_t num_groups = 0) {
@@ -90,6 +92,9 @@ pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, 
   if (num_blocks <= 0 || max_blocks_per_seq <= 0)
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: num_blocks %d max_blocks_per_seq %d", fn,
                 num_blocks, max_blocks_per_seq);
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: max_blocks_per_seq %d x block_size %d positions "
+                "exceed int32", fn, max_blocks_per_seq, block_size);
   if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: max_context_len %d outside [0, %lld]", fn,
                 max_context_len, (long long)max_blocks_per_seq * block_size);
@@ -121,11 +126,12 @@ pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, 
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: new_key/new_value must both be NULL or both set "
                 "and 16-byte aligned", fn);
   bool mfma;
-  switch (opt->kernel) {
+  const int kernel = pkv::enum_arg(opt->kernel);
+  switch (kernel) {
     case PKV_KERNEL_AUTO: mfma = dtype != PKV_F32 && G >= 4; break;
     case PKV_KERNEL_VALU: mfma = false; break;
     case PKV_KERNEL_MFMA: mfma = true; break;
-    default: return fail(PKV_ERR_INVALID_ARGUMENT, "%s: bad kernel family %d", fn, (int)opt->kernel);
+    default: return fail(PKV_ERR_INVALID_ARGUMENT, "%s: bad kernel family %d", fn, kernel);
   }
   if (mfma && dtype == PKV_F32)
     return fail(PKV_ERR_UNSUPPORTED, "%s: the MFMA kernel takes fp16/bf16 only", fn);
@@ -214,7 +220,7 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cac
                                  int32_t block_size, int32_t num_blocks, pkv_dtype dtype,
                                  void* stream) {
   const char* fn = "pkv_reshape_and_cache";
-  pkv_status st = check_tile(fn, num_kv_heads, head_dim, block_size, dtype);
+  pkv_status st = check_tile(fn, num_kv_heads, head_dim, block_size, pkv::enum_arg(dtype));
   if (st != PKV_OK) return st;
   if (num_tokens < 0 || num_blocks <= 0)
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: num_tokens %d num_blocks %d", fn, num_tokens, num_blocks);
@@ -246,7 +252,7 @@ pkv_status pkv_paged_attention_decode(
   return decode_impl(nullptr, out, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
                      block_tables, max_blocks_per_seq, context_lens, work_items,
                      num_work_items, max_context_len, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                     num_blocks, scale, dtype, partition_size, max_logits, exp_sums, tmp_out,
+                     num_blocks, scale, pkv::enum_arg(dtype), partition_size, max_logits, exp_sums, tmp_out,
                      stream);
 }
 
@@ -260,7 +266,7 @@ pkv_status pkv_paged_attention_decode_ex(
   return decode_impl(options, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
                      context_lens, work_items, num_work_items, max_context_len, num_seqs,
                      num_heads,
-                     num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                     num_kv_heads, head_dim, block_size, num_blocks, scale, pkv::enum_arg(dtype),
                      partition_size, max_logits, exp_sums, tmp_out, stream);
 }
 
@@ -278,7 +284,7 @@ pkv_status pkv_paged_attention_decode_shared(
   return decode_impl(&mfma, nullptr, q, k_cache, v_cache,
                      block_tables, max_blocks_per_seq, context_lens, work_items, num_work_items,
                      max_context_len, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                     num_blocks, scale, dtype, partition_size, max_logits, exp_sums, tmp_out,
+                     num_blocks, scale, pkv::enum_arg(dtype), partition_size, max_logits, exp_sums, tmp_out,
                      stream, groups, num_groups);
 }
 
@@ -289,7 +295,8 @@ pkv_status pkv_paged_attention_reduce(void* out, const float* max_logits,
                                       int32_t partition_size, int32_t max_num_partitions,
                                       pkv_dtype dtype, void* stream) {
   const char* fn = "pkv_paged_attention_reduce";
-  if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID_ARGUMENT, "%s: bad dtype %d", fn, (int)dtype);
+  const int dt = pkv::enum_arg(dtype);
+  if (!valid_dtype(dt)) return fail(PKV_ERR_INVALID_ARGUMENT, "%s: bad dtype %d", fn, dt);
   if (num_seqs < 0 || num_heads <= 0 || partition_size <= 0 || max_num_partitions < 0)
     return fail(PKV_ERR_INVALID_ARGUMENT,
                 "%s: num_seqs %d num_heads %d partition_size %d max_num_partitions %d", fn,
@@ -314,7 +321,7 @@ pkv_status pkv_paged_attention_reduce(void* out, const float* max_logits,
   p.num_heads = num_heads;
   p.partition_size = partition_size;
   p.max_num_partitions = max_num_partitions;
-  return hip_status(pkv::launch_reduce(to_dt(dtype), head_dim, p, reinterpret_cast<hipStream_t>(stream)), fn);
+  return hip_status(pkv::launch_reduce(to_dt(dt), head_dim, p, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
 int32_t pkv_prefill_tile_tokens(int32_t num_heads, int32_t num_kv_heads) {
@@ -334,7 +341,7 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
                                        int32_t block_size, int32_t num_blocks, float scale,
                                        pkv_dtype dtype, void* stream) {
   const char* fn = "pkv_paged_attention_prefill";
-  pkv_status st = check_tile(fn, num_kv_heads, head_dim, block_size, dtype);
+  pkv_status st = check_tile(fn, num_kv_heads, head_dim, block_size, pkv::enum_arg(dtype));
   if (st != PKV_OK) return st;
   if (dtype == PKV_F32)
     return fail(PKV_ERR_UNSUPPORTED, "%s: fp32 inputs (the matrix-core kernel takes fp16/bf16)", fn);
@@ -387,7 +394,7 @@ pkv_status pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                            int32_t num_blocks, pkv_dtype dtype, void* stream) {
   const char* fn = "pkv_copy_blocks";
-  pkv_status st = check_tile(fn, num_kv_heads, head_dim, block_size, dtype);
+  pkv_status st = check_tile(fn, num_kv_heads, head_dim, block_size, pkv::enum_arg(dtype));
   if (st != PKV_OK) return st;
   if (num_layers < 0 || num_pairs < 0 || num_blocks <= 0)
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: num_layers %d num_pairs %d num_blocks %d", fn,
@@ -422,11 +429,13 @@ size_t pkv_partition_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_
       max_context_len <= 0)
     return 0;
   const size_t np = ((size_t)max_context_len + partition_size - 1) / partition_size;
-  return 4 * (size_t)num_seqs * num_heads * np * ((size_t)head_dim + 2);
+  const unsigned __int128 bytes =
+      (unsigned __int128)4 * (size_t)num_seqs * (size_t)num_heads * np * ((size_t)head_dim + 2);
+  return bytes > SIZE_MAX ? SIZE_MAX : (size_t)bytes;
 }
 
 const char* pkv_status_string(pkv_status s) {
-  switch (s) {
+  switch (pkv::enum_arg(s)) {
     case PKV_OK: return "ok";
     case PKV_ERR_INVALID_ARGUMENT: return "invalid argument";
     case PKV_ERR_UNSUPPORTED: return "unsupported shape";

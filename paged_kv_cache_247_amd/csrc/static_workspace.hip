@@ -51,6 +51,9 @@ extern "C" pkv_status pkv_paged_attention_decode_static(
     int32_t block_size, int32_t num_blocks, float scale, pkv_dtype dtype,
     int32_t partition_size, void* stream) {
   const char* fn = "pkv_paged_attention_decode_static";
+  const int dt = pkv::enum_arg(dtype);
+  if (dt != PKV_F32 && dt != PKV_F16 && dt != PKV_BF16)
+    return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "%s: bad dtype %d", fn, dt);
   if (partition_size <= 0)
     return pkv::fail(PKV_ERR_INVALID_ARGUMENT, "%s: partition_size %d (split-context only)", fn,
                      partition_size);

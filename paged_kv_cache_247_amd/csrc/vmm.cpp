@@ -31,7 +31,7 @@ namespace {
 
 using pkv::fail;
 
-size_t elt_size(pkv_dtype d) { return d == PKV_F32 ? 4 : 2; }
+size_t elt_size(int dtype) { return dtype == PKV_F32 ? 4 : 2; }
 
 hipMemAllocationProp device_prop(int device) {
   hipMemAllocationProp prop;
@@ -118,8 +118,9 @@ pkv_status pkv_vmm_pool_create(int32_t num_seqs, int32_t max_context_len, int32_
   const char* fn = "pkv_vmm_pool_create";
   if (!pool) return fail(PKV_ERR_INVALID_ARGUMENT, "%s: pool is NULL", fn);
   *pool = nullptr;
+  const int dt = pkv::enum_arg(dtype);
   if (num_seqs <= 0 || max_context_len <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-      block_size <= 0 || (dtype != PKV_F32 && dtype != PKV_F16 && dtype != PKV_BF16))
+      block_size <= 0 || (dt != PKV_F32 && dt != PKV_F16 && dt != PKV_BF16))
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: bad shape or dtype", fn);
   int device = 0;
   hipError_t e = hipGetDevice(&device);
@@ -135,7 +136,7 @@ pkv_status pkv_vmm_pool_create(int32_t num_seqs, int32_t max_context_len, int32_
   if (page % min_gran)
     return fail(PKV_ERR_INVALID_ARGUMENT, "%s: page_bytes %zu is not a multiple of %zu", fn,
                 page, min_gran);
-  const size_t block_bytes = (size_t)num_kv_heads * block_size * head_dim * elt_size(dtype);
+  const size_t block_bytes = (size_t)num_kv_heads * block_size * head_dim * elt_size(dt);
   // Blocks per sequence: enough for max_context_len, rounded up so that every region is a
   // whole number of pages (a multiple of page / gcd(page, block_bytes) blocks).
   const size_t unit = page / gcd(page, block_bytes);

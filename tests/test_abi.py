@@ -51,6 +51,8 @@ def test_workspace_bytes(lib):
     assert lib.pkv_partition_workspace_bytes(32, 64, 128, 30785, 512) == 4 * 32 * 64 * 61 * 130
     assert lib.pkv_partition_workspace_bytes(32, 64, 128, 30785, 0) == 0
     assert lib.pkv_partition_workspace_bytes(32, 64, 128, 0, 512) == 0
+    # a product that does not fit in size_t saturates instead of wrapping to a small size
+    assert lib.pkv_partition_workspace_bytes(2**31 - 1, 2**31 - 1, 128, 2**31 - 1, 1) == 2**64 - 1
 
 
 def decode(lib, **kw):
@@ -103,6 +105,8 @@ def decode(lib, **kw):
     (dict(bt=None, N=7), INVALID),  # table-free: the pool must hold B * MB blocks
     (dict(bt=None, kernel=1), UNSUPPORTED),  # table-free runs on the MFMA kernel only
     (dict(bt=None, kernel=2, B=0), OK),
+    (dict(MB=(1 << 31) // 16), INVALID),  # table span beyond int32 positions
+    (dict(dtype=-1), INVALID),
 ])
 def test_decode_validation(lib, kw, status):
     assert decode(lib, **kw) == status
