@@ -598,7 +598,30 @@ def prefill_main(args):
         pk.paged_attention_prefill(out, q, kc, vc, bt, lens, qs, maxq, cfg.scale,
                                    work_items=order)
 
+    # The chunk's own cache write: its new tokens' K/V rows (already in the pool, so rewriting
+    # them is idempotent) at the slots of positions L - Q .. L - 1, consecutive runs per block.
+    S = cfg.block_size
+    slots = np.concatenate([
+        wl.block_tables[i, np.arange(L - Q, L) // S].astype(np.int64) * S + np.arange(L - Q, L) % S
+        for i, (L, Q) in enumerate(zip(wl.context_lens.astype(np.int64),
+                                       wl.query_lens.astype(np.int64)))])
+    pos_rows = [(i, p) for i, (L, Q) in enumerate(zip(wl.context_lens, wl.query_lens))
+                for p in range(int(L - Q), int(L))]
+    knew = np.stack([wl.k_cache[wl.block_tables[i, p // S], :, p % S, :] for i, p in pos_rows])
+    VS = min(S, 32)
+    vv = wl.v_cache.reshape(wl.v_cache.shape[0], cfg.num_kv_heads, S // VS, cfg.head_dim, VS)
+    vnew = np.stack([vv[wl.block_tables[i, p // S], :, (p % S) // VS, :, p % VS]
+                     for i, p in pos_rows])
+    dkey, dval, dslots = dev(knew), dev(vnew), dev(slots)
+
     kernels = {"paged_attention_prefill": launch_stats(torch, prefill, args.launches, args.reps)}
+    kernels["reshape_and_cache"] = dict(
+        launch_stats(torch, lambda: pk.reshape_and_cache(dkey, dval, kc, vc, dslots),
+                     args.launches, args.reps),
+        bytes=2 * 2 * int(knew.nbytes), tokens=len(slots))
+    kernels["reshape_and_cache"]["GB_per_s"] = round(
+        kernels["reshape_and_cache"]["bytes"] / (kernels["reshape_and_cache"]["median_us"] * 1e-6)
+        / 1e9, 2)
     for _ in range(args.warmup):
         prefill()
     torch.cuda.synchronize()
@@ -635,6 +658,13 @@ def prefill_main(args):
                      "ms_per_launch": round(launch_ms, 5), "flops_per_launch": fl},
         "kernels": kernels,
     }
+    if args.copy_calibration_gib > 0:
+        n = int(args.copy_calibration_gib * (1 << 30)) // 4
+        a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = n * 4
     ok = True
     if cpu is not None:
         line["cpu_baseline"] = cpu

@@ -14,36 +14,69 @@
 namespace pkv {
 namespace {
 
-// One workgroup per new token. K rows are 16-byte vector stores into the [S][D] tile; V
-// elements go to column pos % VS of column group pos / VS, each group a [D][VS] tile
-// (VS = min(S, 32)).
+// One workgroup per new token. K: the token's rows are 16-byte vector stores into the [S][D]
+// tiles. V goes to column pos % VS of column group pos / VS, each group a [D][VS] tile
+// (VS = min(S, 32)): one element per (head, dim) row. When the token's aligned piece of kPiece
+// positions (32 bytes of 16-bit elements: a whole memory sector, one row of a block of 16) is
+// filled by kPiece consecutive tokens with consecutive slots -- the new tokens of a prompt --
+// the k-th of them stores whole pieces of the k-th sixteenth of the (head, dim) rows, gathering
+// each row's kPiece elements from all of them, so every token does the same work and every
+// row is written once in full. Otherwise (the newest token of each of many sequences, the ends
+// of a prompt) the token stores its own element of every row.
+constexpr int kCacheThreads = 128;
+constexpr int kPiece = 16;
+
 template <Dt DT, int D, int S>
-__global__ void __launch_bounds__(256) reshape_and_cache_kernel(const CacheWriteParams a) {
+__global__ void __launch_bounds__(kCacheThreads) reshape_and_cache_kernel(const CacheWriteParams a) {
   using T = typename Elt<DT>::T;
   constexpr int EB = Elt<DT>::bytes;
   constexpr int VEC = 16 / EB;
+  constexpr int VS = S < 32 ? S : 32;
+  static_assert(VS % kPiece == 0, "a piece of positions stays within one column group");
   const int t = blockIdx.x;
-  const int64_t slot = a.slot_mapping[t];
-  if (slot < 0 || slot >= (int64_t)a.num_blocks * S) return;
-  const int64_t blk = slot / S;
-  const int pos = (int)(slot % S);
   const int Hkv = a.num_kv_heads;
+  const int64_t sl = a.slot_mapping[t];
+  if (sl < 0 || sl >= (int64_t)a.num_blocks * S) return;
+  const int64_t blk = sl / S;
+  const int pos = (int)(sl % S);
 
   const char* key = reinterpret_cast<const char*>(a.key) + (size_t)t * Hkv * D * EB;
   char* kc = reinterpret_cast<char*>(a.k_cache);
-  for (int v = threadIdx.x; v < Hkv * D / VEC; v += blockDim.x) {
+  for (int v = threadIdx.x; v < Hkv * D / VEC; v += kCacheThreads) {
     const int h = (v * VEC) / D;
     const int d = (v * VEC) % D;
     const u32x4 x = *reinterpret_cast<const u32x4*>(key + ((size_t)h * D + d) * EB);
-    *reinterpret_cast<u32x4*>(kc + ((((size_t)blk * Hkv + h) * S + pos) * D + d) * EB) = x;
+    *reinterpret_cast<u32x4*>(kc + (((blk * Hkv + h) * S + pos) * D + d) * EB) = x;
   }
-  constexpr int VS = S < 32 ? S : 32;
-  const T* val = reinterpret_cast<const T*>(a.value) + (size_t)t * Hkv * D;
-  T* vc = reinterpret_cast<T*>(a.v_cache) + (size_t)(pos / VS) * VS * D + pos % VS;
-  for (int e = threadIdx.x; e < Hkv * D; e += blockDim.x) {
-    const int h = e / D;
-    const int d = e % D;
-    vc[((size_t)blk * Hkv + h) * S * D + (size_t)d * VS] = val[e];
+
+  // Is the piece filled by tokens t - k .. t - k + kPiece - 1 with consecutive slots?
+  const int k = pos % kPiece;
+  const int t0 = t - k;
+  bool full = t0 >= 0 && t0 + kPiece <= a.num_tokens;
+  int64_t w[kPiece];
+#pragma unroll
+  for (int q = 0; q < kPiece; ++q) w[q] = full ? a.slot_mapping[t0 + q] : -1;
+#pragma unroll
+  for (int q = 0; q < kPiece; ++q) full = full && w[q] == sl - k + q;
+  T* piece = reinterpret_cast<T*>(a.v_cache) + (size_t)blk * Hkv * S * D +
+             (size_t)(pos / VS) * VS * D + (pos - k) % VS;
+  if (full) {
+    const T* val = reinterpret_cast<const T*>(a.value) + (size_t)t0 * Hkv * D;
+    const int R = Hkv * D / kPiece;  // rows of this token's share
+    for (int x = threadIdx.x; x < R; x += kCacheThreads) {
+      const int e = k * R + x;
+      __attribute__((aligned(16))) T row[kPiece];
+#pragma unroll
+      for (int q = 0; q < kPiece; ++q) row[q] = val[(size_t)q * Hkv * D + e];
+      T* dst = piece + (size_t)(e / D) * S * D + (size_t)(e % D) * VS;
+#pragma unroll
+      for (int q = 0; q < kPiece * EB / 16; ++q)
+        reinterpret_cast<u32x4*>(dst)[q] = reinterpret_cast<const u32x4*>(row)[q];
+    }
+  } else {
+    const T* val = reinterpret_cast<const T*>(a.value) + (size_t)t * Hkv * D;
+    for (int e = threadIdx.x; e < Hkv * D; e += kCacheThreads)
+      piece[(size_t)(e / D) * S * D + (size_t)(e % D) * VS + k] = val[e];
   }
 }
 
@@ -70,12 +103,13 @@ __global__ void __launch_bounds__(kCopyThreads) copy_blocks_kernel(const CopyPar
 template <Dt DT, int D>
 hipError_t write_d(int block_size, const CacheWriteParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)p.num_tokens);
+  constexpr int TH = kCacheThreads;
   switch (block_size) {
-    case 16: reshape_and_cache_kernel<DT, D, 16><<<grid, 256, 0, stream>>>(p); break;
-    case 32: reshape_and_cache_kernel<DT, D, 32><<<grid, 256, 0, stream>>>(p); break;
-    case 64: reshape_and_cache_kernel<DT, D, 64><<<grid, 256, 0, stream>>>(p); break;
-    case 128: reshape_and_cache_kernel<DT, D, 128><<<grid, 256, 0, stream>>>(p); break;
-    case 256: reshape_and_cache_kernel<DT, D, 256><<<grid, 256, 0, stream>>>(p); break;
+    case 16: reshape_and_cache_kernel<DT, D, 16><<<grid, TH, 0, stream>>>(p); break;
+    case 32: reshape_and_cache_kernel<DT, D, 32><<<grid, TH, 0, stream>>>(p); break;
+    case 64: reshape_and_cache_kernel<DT, D, 64><<<grid, TH, 0, stream>>>(p); break;
+    case 128: reshape_and_cache_kernel<DT, D, 128><<<grid, TH, 0, stream>>>(p); break;
+    case 256: reshape_and_cache_kernel<DT, D, 256><<<grid, TH, 0, stream>>>(p); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();

@@ -61,6 +61,49 @@ def test_reshape_and_cache_skips_negative_and_out_of_range_slots():
     assert np.array_equal(bits(to_host(dev.v, "bf16")), bits(ev))
 
 
+def _prompt_slots(rng, N, S, lens, starts):
+    """Slots of prompt runs: sequence k writes positions starts[k] .. starts[k] + lens[k] - 1
+    through its own randomly placed blocks (distinct across sequences)."""
+    blocks = rng.permutation(N)
+    slots, used = [], 0
+    for n, p0 in zip(lens, starts):
+        nb = -(-(p0 + n) // S)
+        tab = blocks[used:used + nb]
+        used += nb
+        slots += [int(tab[p // S]) * S + p % S for p in range(p0, p0 + n)]
+    return np.array(slots, dtype=np.int64)
+
+
+@pytest.mark.parametrize("S,dtype", [(16, "bf16"), (32, "bf16"), (64, "f16"), (256, "bf16"),
+                                     (16, "f32"), (128, "f32")])
+def test_reshape_and_cache_prompt_runs_bit_exact(S, dtype):
+    """Prompt-shaped writes: runs of consecutive positions (aligned and unaligned starts, runs
+    across block boundaries, a partial last group of tokens), some slots of a run skipped
+    (negative or past the pool), then single scattered tokens; the whole pool bit for bit."""
+    cfg = W.SMALL["c3"].replace(block_size=S, dtype=dtype, num_blocks=max(200, 4096 // S * 4))
+    wl = W.generate(cfg)
+    rng = np.random.default_rng(S)
+    lens = [70, 8, 16, 1, 33, 7, 2 * S + 3]
+    starts = [0, 8, 5, 0, S - 3, 1, 0]
+    slots = _prompt_slots(rng, cfg.num_blocks, S, lens, starts)
+    slots[20] = -1
+    slots[45] = cfg.num_blocks * S + 7  # past the pool: skipped
+    T = len(slots)
+    Hkv, D = cfg.num_kv_heads, cfg.head_dim
+    st = W.storage_dtype(dtype)
+    width = np.uint32 if dtype == "f32" else np.uint16
+    key = rng.integers(0, 1 << 15, size=(T, Hkv, D)).astype(width).view(st)
+    value = rng.integers(0, 1 << 15, size=(T, Hkv, D)).astype(width).view(st)
+    kd, vd = to_dev(wl.k_cache, dtype), to_dev(wl.v_cache, dtype)
+    pk.reshape_and_cache(to_dev(key, dtype), to_dev(value, dtype), kd, vd, to_dev(slots))
+    torch.cuda.synchronize()
+    keep = slots.copy()
+    keep[45] = -1
+    ek, ev = oracle.write_cache(wl.k_cache, wl.v_cache, key, value, keep, S)
+    assert np.array_equal(bits(to_host(kd, dtype)), bits(ek))
+    assert np.array_equal(bits(to_host(vd, dtype)), bits(ev))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_copy_blocks_bit_exact_all_layers(dtype):
     cfg = _cfg("c4", dtype=dtype)
