@@ -102,9 +102,13 @@ def parse():
                     help="repetitions of back-to-back launch timing per kernel")
     ap.add_argument("--launches", type=int, default=100,
                     help="back-to-back launches per repetition")
-    ap.add_argument("--shared-prefix", default="auto", choices=["auto", "on", "off"],
-                    help="decode blocks that sequences share once per group of sequences "
-                         "(auto: when the batch shares a prefix and runs single pass)")
+    ap.add_argument("--shared-prefix", default="auto", choices=["auto", "whole", "on", "off"],
+                    help="decode blocks that sequences share once per group of sequences: "
+                         "whole = one pass per group over the shared and its members' own "
+                         "positions; on = the groups' shared partition beside the other "
+                         "split-context units, then the merge; auto = whole when every "
+                         "sequence can join a group, else on, when the batch shares a prefix "
+                         "and runs single pass; off = plain decode")
     ap.add_argument("--block-size", type=int, default=None,
                     help="run the workload in blocks of this many positions (16..256); the "
                          "pool keeps at least its capacity")
@@ -256,7 +260,7 @@ def counter_traffic(kernel_sources, workload, shared=False):
         h.update(open(os.path.join(root, "paged_kv_cache_247_amd", "csrc", src), "rb").read())
     if vals.get("source_sha256") != h.hexdigest():
         return None
-    if int(vals.get("shared_prefix", "0")) != int(bool(shared)):
+    if vals.get("shared_prefix", "0") != str(shared if isinstance(shared, str) else int(bool(shared))):
         return None
     return int(float(vals["traffic_bytes_per_launch"]))
 
@@ -307,7 +311,7 @@ def build_step(torch, pk, wl, kernel, P, cached, shared_prefix="auto", fused=Tru
         return torch.from_numpy(a).cuda()
 
     s = SimpleNamespace(cfg=cfg, wl=wl, kernel=kernel, P=P, cached=cached, fused=fused,
-                        layout=layout, plan=None, pool=None)
+                        layout=layout, plan=None, whole=None, pool=None)
     s.q, s.key, s.value = dev(wl.q), dev(wl.key), dev(wl.value)
     s.kc, s.vc = dev(wl.k_cache), dev(wl.v_cache)
     s.slots = dev(wl.slot_mapping, False)
@@ -337,13 +341,24 @@ def build_step(torch, pk, wl, kernel, P, cached, shared_prefix="auto", fused=Tru
     s.family = kernel_family(kernel, cfg, table_free)
     # Blocks shared by several sequences (a common prefix): plan groups that read each shared
     # tile once for all their members (host scheduler input, like the work list).
-    if shared_prefix == "on" or (shared_prefix == "auto" and cfg.prefix_len and not P):
-        from paged_kv_cache_247_amd import sharing
+    from paged_kv_cache_247_amd import sharing
+    if shared_prefix == "whole" or (shared_prefix == "auto" and cfg.prefix_len and not P):
+        s.whole = sharing.plan_whole(wl.block_tables, wl.context_lens, cfg.block_size,
+                                     cfg.group, newest_outside=fused)
+        if s.whole is None and shared_prefix == "whole":
+            raise ValueError("--shared-prefix whole: no blocks are shared, or a sequence is too "
+                             "short to join a group")
+    if s.whole is None and (shared_prefix == "on" or
+                            (shared_prefix == "auto" and cfg.prefix_len and not P)):
         s.plan = sharing.plan(wl.block_tables, wl.context_lens, cfg.block_size,
                               wl.max_context_len, cfg.group, newest_outside=fused)
         if s.plan is None and shared_prefix == "on":
             raise ValueError("--shared-prefix on: no blocks are shared")
-    if s.plan is not None:
+    if s.whole is not None:
+        s.P, s.kernel, s.cached, s.family = 0, "mfma", True, "mfma"
+        s.groups = dev(s.whole.groups, False)
+        s.order = None
+    elif s.plan is not None:
         s.P, s.kernel, s.cached, s.family = s.plan.partition_size, "mfma", True, "mfma"
         s.groups = dev(s.plan.groups, False)
         s.order = dev(s.plan.work_items, False)
@@ -361,6 +376,11 @@ def build_step(torch, pk, wl, kernel, P, cached, shared_prefix="auto", fused=Tru
 
     def decode():
         # With fused=True the decode launch also writes each sequence's newest K/V to its slot.
+        if s.whole is not None:  # one pass per group, shared and own positions
+            pk.paged_attention_decode_grouped(s.out, s.q, kpool, vpool, s.bt, s.lens, s.groups,
+                                              s.whole.shared_len, cfg.scale, new_key=nk,
+                                              new_value=nv)
+            return
         if s.plan is not None:  # the groups and every other unit in one launch
             pk.paged_attention_decode_shared(s.q, kpool, vpool, s.bt, s.lens, s.groups, maxlen,
                                              cfg.scale, P, s.ws, work_items=s.order,
@@ -402,6 +422,14 @@ def build_step(torch, pk, wl, kernel, P, cached, shared_prefix="auto", fused=Tru
     return s
 
 
+def kernel_name(s):
+    if s.whole is not None:
+        return "paged_attention_decode_grouped (mfma: whole groups over a shared prefix)"
+    if s.plan is not None:
+        return "paged_attention_decode_shared (mfma: groups and other units)"
+    return f"paged_attention_decode ({s.family})"
+
+
 def roofline_bytes(wl):
     """Bytes the decode launch must read: the KV bytes, or with shared blocks the distinct
     tiles (the shared prefix is served from cache after its first read), without the
@@ -433,8 +461,7 @@ def config_entry(torch, pk, name, P_over, reps, launches):
     entry = {
         "workload": f"{name}: {cfg.description}", "seed": cfg.seed,
         "context_tokens": wl.total_tokens, "kv_bytes": kvb,
-        "kernel": ("paged_attention_decode_shared (mfma)" if s.plan is not None
-                   else f"paged_attention_decode ({s.family})"),
+        "kernel": kernel_name(s),
         "partition_size": s.P, "cached_kv": s.cached,
         "step_us": stp["median_us"],
         "GB_per_s": round(kvb / (stp["median_us"] * 1e-6) / 1e9, 2),
@@ -804,10 +831,24 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
+    in_step_ms = None
     if alone:
         dec_ms = span[0].elapsed_time(span[1]) / args.steps
     else:
-        dec_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+        # The step has other kernels too: an event pair around each decode launch also times
+        # the gaps the events themselves open (a few us per launch), so the launch duration is
+        # taken the way it is for a step of the decode alone -- the same launch repeated
+        # `steps` times back to back under one event pair (its inputs are unchanged by a
+        # repeat) -- and the per-launch event figure is reported beside it.
+        in_step_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            s.decode()
+        e1.record()
+        torch.cuda.synchronize()
+        dec_ms = e0.elapsed_time(e1) / args.steps
     print(f"[bench] {args.steps} steps, {ms_step:.4f} ms/step, decode {dec_ms:.4f} ms/launch",
           file=sys.stderr, flush=True)
     check = None
@@ -823,7 +864,8 @@ def main():
     # paged layout).
     traffic = None if shard or args.layout != "paged" or \
         cfg.block_size != W.CONFIGS[name].block_size \
-        else counter_traffic(KERNEL_SOURCES[s.family], name, s.plan is not None)
+        else counter_traffic(KERNEL_SOURCES[s.family], name,
+                             "whole" if s.whole is not None else s.plan is not None)
     value = kvb / (ms_step * 1e-3) / 1e9
     rb = roofline_bytes(wl)
     # With shared prefix blocks the logical bytes count the prefix once per sequence, but it is
@@ -850,9 +892,13 @@ def main():
                    "context_tokens": wl.total_tokens, "max_context_len": maxlen,
                    "kernel": kernel, "partition_size": P, "cached_kv": cached,
                    "layout": args.layout,
-                   "shared_prefix": None if s.plan is None else {
-                       "groups": len(s.plan.groups), "partition_size": P,
-                       "members": int((s.plan.groups >= 0).sum())},
+                   "shared_prefix": (
+                       {"mode": "whole groups", "groups": len(s.whole.groups),
+                        "shared_len": s.whole.shared_len,
+                        "members": int((s.whole.groups >= 0).sum())} if s.whole is not None
+                       else None if s.plan is None else
+                       {"mode": "groups beside split-context units", "groups": len(s.plan.groups),
+                        "partition_size": P, "members": int((s.plan.groups >= 0).sum())}),
                    "fused_cache_write": fused, "kv_bytes": kvb,
                    "unique_kv_bytes": wl.unique_kv_bytes(), "shard": shard},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
@@ -861,10 +907,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": ("paged_attention_decode_shared (mfma: groups and other units)"
-                                if s.plan is not None
-                                else f"paged_attention_decode ({s.family})"),
+                     "kernel": kernel_name(s),
                      "ms_per_launch": round(dec_ms, 5), "bytes_per_launch": rb,
+                     "ms_per_launch_between_events_in_step": None if in_step_ms is None
+                     else round(in_step_ms, 5),
                      "logical_GB_per_s": round(kvb / (dec_ms * 1e-3) / 1e9, 2)},
         "kernels": kernels,
         "parity": check,

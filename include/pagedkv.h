@@ -196,6 +196,34 @@ pkv_status pkv_paged_attention_decode_shared(
     int32_t num_blocks, float scale, pkv_dtype dtype, int32_t partition_size,
     float* max_logits, float* exp_sums, float* tmp_out, void* stream);
 
+/* Decode of groups of sequences that share their first shared_len positions, each group in
+ * one pass that writes its members' outputs. Requests that share a prompt prefix share its KV
+ * blocks (Hacker News discussion of PagedAttention, replies on prefix sharing); the matrix-core
+ * product's 16 columns hold the G query heads of each of up to 16 / G members
+ * (grouped-query attention, vAttention section 3.1), so a shared tile is read once per group
+ * and feeds every member, and then each member's own positions (shared_len .. L_i - 1) are read
+ * through its own table row and feed only its columns. The result is the operation at the top
+ * of this file for every member, as pkv_paged_attention_decode in single-pass mode computes it
+ * (same tolerance, different order of the fp32 additions).
+ * out, q: device [B, H, D]; k_cache, v_cache, block_tables, context_lens: as for
+ * pkv_paged_attention_decode. groups: device int32 [num_groups][4], 16-byte aligned; row u
+ * lists the member sequences of group u (-1 for none; entries past 16 / G must be -1; the
+ * first entry must be a member). shared_len: a multiple of block_size, at most
+ * max_blocks_per_seq * block_size. new_key/new_value: NULL, or device [B, Hkv, D] rows of each
+ * sequence's newest position (L_i - 1), written to its slot and attended to as in
+ * pkv_paged_attention_decode_ex. Workgroups run in group order, so list the groups with the
+ * most positions first. Only members' rows of out are written. fp16/bf16.
+ * Caller contract (not checked; PKV_VALIDATE=1 in the Python binding checks it): a sequence is
+ * in at most one group; every member's table agrees with its group's first member's over
+ * entries 0 .. shared_len / S - 1; every member has L_i >= shared_len (L_i > shared_len with
+ * new rows). */
+pkv_status pkv_paged_attention_decode_grouped(
+    void* out, const void* q, void* k_cache, void* v_cache, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* groups,
+    int32_t num_groups, int32_t shared_len, const void* new_key, const void* new_value,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, float scale, pkv_dtype dtype, void* stream);
+
 /* Bytes of the library-owned partition workspace of pkv_paged_attention_decode_static (each
  * device the library runs on holds its own copy until the process ends). */
 #define PKV_STATIC_WORKSPACE_BYTES ((size_t)80 << 20)
@@ -419,7 +447,7 @@ pkv_status pkv_probe_tile_gather(const void* base, size_t base_bytes,
 const char* pkv_status_string(pkv_status s);
 int pkv_last_hip_error(void);              /* hipError_t behind the last PKV_ERR_HIP */
 const char* pkv_last_error_message(void);  /* thread-local text of the last failure */
-int pkv_abi_version(void);                 /* 4: decode with the static workspace */
+int pkv_abi_version(void);                 /* 5: whole-group decode over shared prefixes */
 
 #ifdef __cplusplus
 }

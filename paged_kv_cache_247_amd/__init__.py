@@ -6,7 +6,8 @@ ctypes binding. The seeded workload generators live in `workload`.
 from ._lib import (KERNELS, BlockManager, DeviceRegion, OutOfBlocks, PagedKVError, VmmPool,
                    auto_partition_size, copy_blocks, load, swap_blocks,
                    num_partitions, paged_attention, paged_attention_decode,
-                   paged_attention_decode_shared, paged_attention_decode_static,
+                   paged_attention_decode_grouped, paged_attention_decode_shared,
+                   paged_attention_decode_static,
                    paged_attention_shared,
                    paged_attention_prefill, paged_attention_reduce, partition_workspace,
                    prefill_tile_tokens, probe_stream_read, probe_tile_gather,
@@ -15,7 +16,8 @@ from ._lib import (KERNELS, BlockManager, DeviceRegion, OutOfBlocks, PagedKVErro
 __all__ = ["KERNELS", "BlockManager", "DeviceRegion", "OutOfBlocks", "PagedKVError", "VmmPool",
            "auto_partition_size", "copy_blocks", "load", "swap_blocks",
            "num_partitions", "paged_attention", "paged_attention_decode",
-           "paged_attention_decode_shared", "paged_attention_decode_static",
+           "paged_attention_decode_grouped", "paged_attention_decode_shared",
+           "paged_attention_decode_static",
            "paged_attention_shared",
            "paged_attention_prefill", "paged_attention_reduce", "partition_workspace",
            "prefill_tile_tokens", "probe_stream_read", "probe_tile_gather",

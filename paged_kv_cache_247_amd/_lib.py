@@ -44,6 +44,8 @@ SIGNATURES = {
                                                _P, _P]),
     "pkv_paged_attention_decode_static": (_I, [_P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I,
                                                _I, _I, _I, _I, _F, _I, _I, _P]),
+    "pkv_paged_attention_decode_grouped": (_I, [_P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _P, _P,
+                                                _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "pkv_paged_attention_reduce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pkv_copy_blocks": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pkv_partition_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
@@ -138,7 +140,7 @@ class OutOfBlocks(PagedKVError):
 
 PKV_ERR_HIP = 3
 PKV_ERR_NO_BLOCKS = 4
-ABI_VERSION = 4  # the argument lists in SIGNATURES
+ABI_VERSION = 5  # the argument lists in SIGNATURES
 STATIC_WORKSPACE_BYTES = 80 << 20  # PKV_STATIC_WORKSPACE_BYTES
 
 
@@ -330,6 +332,48 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         0 if work_items is None else work_items.shape[0], int(max_context_len), B, H,
         Hkv, D, S, N, float(scale), _dt(q), int(partition_size), _ptr(ml), _ptr(es), _ptr(to),
         _stream(q)))
+
+
+def paged_attention_decode_grouped(out, q, k_cache, v_cache, block_tables, context_lens, groups,
+                                   shared_len, scale, new_key=None, new_value=None):
+    """pkv_paged_attention_decode_grouped: every member of each group (groups: device int32
+    [num_groups, 4], -1 pads) decoded in one pass per group -- the first shared_len positions,
+    which the members' tables share, read once for all of them -- into `out` [B, H, D]; with
+    new_key/new_value [B, Hkv, D] also each member's newest-position cache write."""
+    _need(q, "q", ndim=3)
+    dt = q.dtype
+    B, H, D = q.shape
+    _need(out, "out", dt, 3, q.device)
+    if tuple(out.shape) != (B, H, D):
+        raise ValueError("out must be [B, H, D]")
+    _need(k_cache, "k_cache", dt, 4, q.device)
+    N, Hkv, S, Dk = k_cache.shape
+    if Dk != D:
+        raise ValueError("head_dim of q and k_cache differ")
+    _need(v_cache, "v_cache", dt, 4, q.device)
+    if tuple(v_cache.shape) != (N, *v_block_shape(Hkv, D, S)):
+        raise ValueError(f"v_cache must be {(N, *v_block_shape(Hkv, D, S))}")
+    _need(block_tables, "block_tables", torch.int32, 2, q.device)
+    _need(context_lens, "context_lens", torch.int32, 1, q.device)
+    _need(groups, "groups", torch.int32, 2, q.device)
+    if groups.shape[1] != 4 or block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("groups must be [num_groups, 4]; tables and lengths one row per sequence")
+    if (new_key is None) != (new_value is None):
+        raise ValueError("new_key and new_value go together")
+    if new_key is not None:
+        for t, nm in ((new_key, "new_key"), (new_value, "new_value")):
+            _need(t, nm, dt, 3, q.device)
+            if tuple(t.shape) != (B, Hkv, D):
+                raise ValueError(f"{nm} must be {(B, Hkv, D)}")
+    MB = block_tables.shape[1]
+    if validating():
+        _contract_check(_contract.check_whole_groups, _host(groups), _host(block_tables),
+                        _host(context_lens), int(shared_len), S, N, H // Hkv,
+                        fused_write=new_key is not None)
+    _check(load().pkv_paged_attention_decode_grouped(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), MB,
+        _ptr(context_lens), _ptr(groups), groups.shape[0], int(shared_len), _ptr(new_key),
+        _ptr(new_value), B, H, Hkv, D, S, N, float(scale), _dt(q), _stream(q)))
 
 
 def paged_attention_decode_static(out, q, k_cache, v_cache, block_tables, context_lens,

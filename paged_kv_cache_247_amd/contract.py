@@ -162,6 +162,25 @@ def check_groups(groups, block_tables, context_lens, partition_size: int, block_
             _fail(f"work item {int(both[0])} is partition 0 of a grouped sequence")
 
 
+def check_whole_groups(groups, block_tables, context_lens, shared_len: int, block_size: int,
+                       num_blocks: int, group: int, fused_write: bool = False):
+    """Groups for the whole-group decode: as check_groups over the shared positions, and every
+    table entry a member uses (its first ceil(L / S)) names a pool block."""
+    check_groups(groups, block_tables, context_lens, shared_len, block_size, num_blocks, group,
+                 fused_write=fused_write)
+    gm = np.asarray(groups).astype(np.int64).reshape(-1, 4)
+    L = np.asarray(context_lens).astype(np.int64)
+    tables = np.asarray(block_tables).astype(np.int64)
+    S = int(block_size)
+    for m in gm[gm >= 0].tolist():
+        nb = -(-int(L[m]) // S)
+        if nb > tables.shape[1]:
+            _fail(f"sequence {m} has {int(L[m])} positions, its table row holds {tables.shape[1]} blocks")
+        ids = tables[m, :nb]
+        if len(ids) and (ids.min() < 0 or ids.max() >= num_blocks):
+            _fail(f"sequence {m}: a used table entry is not a pool block")
+
+
 def check_prefill(block_tables, context_lens, query_start, max_query_len: int, block_size: int,
                   num_blocks: int, num_tokens: int):
     L = np.asarray(context_lens).astype(np.int64)

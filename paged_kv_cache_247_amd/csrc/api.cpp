@@ -288,6 +288,71 @@ pkv_status pkv_paged_attention_decode_shared(
                      stream, groups, num_groups);
 }
 
+pkv_status pkv_paged_attention_decode_grouped(
+    void* out, const void* q, void* k_cache, void* v_cache, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* groups,
+    int32_t num_groups, int32_t shared_len, const void* new_key, const void* new_value,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, float scale, pkv_dtype dtype, void* stream) {
+  const char* fn = "pkv_paged_attention_decode_grouped";
+  const int dt = pkv::enum_arg(dtype);
+  pkv_status st = check_tile(fn, num_kv_heads, head_dim, block_size, dt);
+  if (st != PKV_OK) return st;
+  if (dt == PKV_F32) return fail(PKV_ERR_UNSUPPORTED, "%s: the matrix-core kernel takes fp16/bf16 only", fn);
+  if (num_seqs < 0 || num_groups < 0)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: num_seqs %d num_groups %d", fn, num_seqs, num_groups);
+  if (num_heads <= 0 || num_heads % num_kv_heads)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: num_heads %d not a positive multiple of num_kv_heads %d",
+                fn, num_heads, num_kv_heads);
+  const int G = num_heads / num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(PKV_ERR_UNSUPPORTED, "%s: query group %d (supported: 1, 2, 4, 8, 16)", fn, G);
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: num_blocks %d max_blocks_per_seq %d", fn,
+                num_blocks, max_blocks_per_seq);
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: max_blocks_per_seq %d x block_size %d positions "
+                "exceed int32", fn, max_blocks_per_seq, block_size);
+  if (shared_len < 0 || shared_len % block_size || shared_len > max_blocks_per_seq * block_size)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: shared_len %d is not a multiple of %d in [0, %d]",
+                fn, shared_len, block_size, max_blocks_per_seq * block_size);
+  if (!isfinite(scale)) return fail(PKV_ERR_INVALID_ARGUMENT, "%s: scale is not finite", fn);
+  if ((new_key == nullptr) != (new_value == nullptr) ||
+      (new_key && (!aligned(new_key, 16) || !aligned(new_value, 16))))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: new_key/new_value must both be NULL or both set "
+                "and 16-byte aligned", fn);
+  if ((int64_t)num_groups * num_kv_heads > INT32_MAX)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: grid of %lld workgroups", fn,
+                (long long)num_groups * num_kv_heads);
+  if (num_groups == 0 || num_seqs == 0) return PKV_OK;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(groups, 16))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: a tensor pointer is null or misaligned", fn);
+  pkv::DecodeParams p = {};
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.work_items = nullptr;
+  p.group_members = groups;
+  p.new_key = new_key;
+  p.new_value = new_value;
+  p.max_logits = p.exp_sums = p.tmp_out = nullptr;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.range_tokens = shared_len;
+  p.num_ranges = 1;
+  p.num_units = num_groups;
+  p.scale_log2e = scale * pkv::kLog2e;
+  return hip_status(pkv::launch_decode_mfma(to_dt(dt), head_dim, block_size, false, false, p,
+                                            reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
 pkv_status pkv_paged_attention_reduce(void* out, const float* max_logits,
                                       const float* exp_sums, const float* tmp_out,
                                       const int32_t* context_lens, int32_t num_seqs,
@@ -449,6 +514,6 @@ int pkv_last_hip_error(void) { return t_last_hip; }
 
 const char* pkv_last_error_message(void) { return t_msg; }
 
-int pkv_abi_version(void) { return 4; }
+int pkv_abi_version(void) { return 5; }
 
 }  // extern "C"

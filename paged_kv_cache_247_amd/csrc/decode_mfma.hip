@@ -77,17 +77,34 @@ template <int D, int NW>
 struct DecodeLds {
   __attribute__((aligned(16))) char stage[NW * 2 * 32 * D * 2];
   float new_logit[16];
-  float new_v[D];
+  float new_v[4 * D];  // the newest V row of each member of a group (of the sequence: row 0)
 };
+
+// x_k of four values, for a k that may differ between lanes: the values are taken by value so
+// that they stay in registers (selecting among the fields of one object can be turned into an
+// indexed load, which puts the object in scratch memory).
+__device__ __forceinline__ int pick4(int k, int x0, int x1, int x2, int x3) {
+  int r = x3;
+  r = k == 2 ? x2 : r;
+  r = k == 1 ? x1 : r;
+  r = k == 0 ? x0 : r;
+  return r;
+}
 
 // One workgroup's unit: w is its index in the launch's numbering (below).
 // GRP: a unit is a group of sequences whose block tables agree over the first range (a shared
 // prefix); column c of the products is head c % G of member c / G, so each shared tile is read
 // once for every member, and the range's partial state is written for each member.
+// WG (GRP without PARTIAL): a unit is a whole group -- its members agree over the first
+// range_tokens positions, which are read once for all members (every column), and then each
+// member's own positions past them through its own table row (that member's columns only); the
+// unit writes each member's output.
 template <Dt DT, int D, int S, int NW, bool PARTIAL, bool NTL, bool TBL, bool GRP>
 __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
                                             DecodeLds<D, NW>& lds) {
-  static_assert(!GRP || (PARTIAL && TBL), "groups write partials through block tables");
+  static_assert(!GRP || TBL, "groups read through block tables");
+  constexpr bool WG = GRP && !PARTIAL;
+  static_assert(!WG || !NTL, "whole groups keep the shared tiles in L2 (cached loads)");
   static_assert(DT == Dt::BF16 || DT == Dt::F16, "16-bit inputs only");
   constexpr int EB = 2;
   constexpr int CT = 32;        // positions per chunk
@@ -168,17 +185,93 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
   // The first batch is loaded now, in parallel with the context length; any entry of the row
   // may be read and ids are clamped into the pool before use.
   constexpr int CPB = 64 / BPC;
+
+  // WG: members (up to 16 / G, -1 for none), their lengths and ends of their own positions
+  // (L - 1 with a fused write), and how many chunks each has past the shared P positions.
+  // Chunk v of the unit's list is, while both kinds last, shared chunk v / 2 for even v and
+  // member chunk v / 2 for odd v -- shared chunks come from L2, members' chunks from HBM, and
+  // mixing them keeps both busy -- then the rest of whichever kind is left; member chunks are
+  // member 0's, then member 1's, and so on.
+  // (Four named values per quantity rather than arrays: indexed by a lane's member, an array
+  // would live in scratch memory.)
+  struct Four {
+    int v0, v1, v2, v3;
+    __device__ __forceinline__ int operator[](int k) const { return pick4(k, v0, v1, v2, v3); }
+  };
+  Four wm = {-1, -1, -1, -1}, wL = {0, 0, 0, 0}, wE = {0, 0, 0, 0}, wcum = {0, 0, 0, 0};
+  int wP = 0, wNS = 0, wNM = 0;
+  if constexpr (WG) {
+    auto member = [&](int k) {
+      const int m = k * G < 16 ? a.group_members[4 * unit + k] : -1;
+      return m >= 0 && m < a.num_seqs ? m : -1;
+    };
+    wm = {member(0), member(1), member(2), member(3)};
+    auto len = [&](int m) { return m >= 0 ? min(max(a.context_lens[m], 0), MB * S) : 0; };
+    wL = {len(wm.v0), len(wm.v1), len(wm.v2), len(wm.v3)};
+    wP = min(max(a.range_tokens, 0), MB * S);
+    wNS = wm.v0 >= 0 ? (wP + CT - 1) / CT : 0;
+    const int nf = a.new_key != nullptr ? 1 : 0;
+    wE = {max(wL.v0 - nf, 0), max(wL.v1 - nf, 0), max(wL.v2 - nf, 0), max(wL.v3 - nf, 0)};
+    auto own = [&](int e) { return e > wP ? (e - wP + CT - 1) / CT : 0; };
+    wcum.v0 = own(wE.v0);
+    wcum.v1 = wcum.v0 + own(wE.v1);
+    wcum.v2 = wcum.v1 + own(wE.v2);
+    wcum.v3 = wcum.v2 + own(wE.v3);
+    wNM = wcum.v3;
+  }
+  struct ChunkInfo {
+    int row;  // sequence whose table row holds the chunk's blocks
+    int cs;   // the chunk's first position
+    int ce;   // end of the positions of its range
+    int k;    // member whose columns it feeds, -1 for all (shared)
+  };
+  auto chunk_info = [&](int v) {
+    const int mn = min(wNS, wNM);
+    int sh = -1, mi = -1;
+    if (v < 2 * mn) {
+      if (v & 1) mi = v >> 1;
+      else sh = v >> 1;
+    } else if (wNS > wNM) {
+      sh = v - mn;
+    } else {
+      mi = v - mn;
+    }
+    ChunkInfo ci;
+    if (sh >= 0) {
+      ci.row = wm.v0;
+      ci.cs = sh * CT;
+      ci.ce = wP;
+      ci.k = -1;
+    } else {
+      const int k = (mi >= wcum.v0) + (mi >= wcum.v1) + (mi >= wcum.v2);
+      const int base = k == 0 ? 0 : wcum[k - 1];
+      ci.row = wm[k];
+      ci.cs = wP + (mi - base) * CT;
+      ci.ce = wE[k];
+      ci.k = k;
+    }
+    ci.row = max(ci.row, 0);
+    return ci;
+  };
+
   auto load_id_batch = [&](int kb) {
     const int n = wave + NW * (kb * CPB + lane / BPC);
-    const int blk = start / S + (BPC == 2 ? n * BPC + lane % BPC : n / CPK);
-    return blk < MB ? bt[blk] : 0;
+    if constexpr (WG) {
+      if (n >= wNS + wNM) return 0;
+      const ChunkInfo ci = chunk_info(n);
+      const int blk = ci.cs / S + (BPC == 2 ? lane % BPC : 0);
+      return blk < MB ? a.block_tables[(size_t)ci.row * MB + blk] : 0;
+    } else {
+      const int blk = start / S + (BPC == 2 ? n * BPC + lane % BPC : n / CPK);
+      return blk < MB ? bt[blk] : 0;
+    }
   };
   int id_batch = 0;
   if constexpr (TBL) id_batch = load_id_batch(0);
 
-  int L = a.context_lens[i];
+  int L = WG ? wL.v0 : a.context_lens[i];
   L = min(max(L, 0), MB * S);
-  if (start >= L) {
+  if (!WG && start >= L) {
     if (!PARTIAL && part == 0) {
       T* o = reinterpret_cast<T*>(a.out) + ((size_t)i * H + (size_t)g * G) * D;
       for (int e = threadIdx.x; e < G * D; e += NW * 64) o[e] = from_f32<DT>(0.0f);
@@ -186,10 +279,10 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
     return;
   }
   // With a fused write, position L-1 comes from new_key/new_value (this is then the sequence's
-  // last range) and the cache is read only up to L-2.
-  const bool fused = a.new_key != nullptr && start + a.range_tokens >= L;
+  // last range) and the cache is read only up to L-2. (WG: each member's position L - 1.)
+  const bool fused = a.new_key != nullptr && (WG || start + a.range_tokens >= L);
   const int end = min(start + a.range_tokens, L) - (fused ? 1 : 0);
-  const int nch = max(end - start + CT - 1, 0) / CT;
+  const int nch = WG ? wNS + wNM : max(end - start + CT - 1, 0) / CT;
   const int blk_end = (end + S - 1) / S;  // first logical block past the cached range
 
   // q columns: lane (r, c) holds head c (zero beyond the group) at d = 32 kk + 8r .. +8; in
@@ -234,6 +327,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
   struct Ids {
     int b0, b1;
     int ro;  // first row of the chunk within block b0 (nonzero only for blocks over 32)
+    int cs, ce, k;  // WG: the chunk's first position, its range's end, its member (-1: shared)
     // This lane's V^T pieces of the chunk, formed with the ids a step early; pieces 4 KiB and
     // more past vt are addressed from vt4 (= vt + 4 KiB, the reach of an immediate offset).
     const char* vt;
@@ -244,9 +338,22 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
   // positions are masked). Called for m = 0, 1, 2, ... in order.
   auto fetch_ids = [&](int m) {
     const int n = wave + NW * m;
-    const int b0 = start / S + (BPC == 2 ? n * BPC : n / CPK);
     Ids ids;
-    ids.ro = (n % CPK) * CT;
+    int b0, bend;  // the chunk's first logical block; the first block past its range
+    if constexpr (WG) {
+      const ChunkInfo ci = chunk_info(n);
+      b0 = ci.cs / S;
+      ids.ro = CPK > 1 ? ci.cs % S : 0;
+      bend = (ci.ce + S - 1) / S;
+      ids.cs = ci.cs;
+      ids.ce = ci.ce;
+      ids.k = ci.k;
+    } else {
+      b0 = start / S + (BPC == 2 ? n * BPC : n / CPK);
+      ids.ro = (n % CPK) * CT;
+      bend = blk_end;
+      ids.cs = ids.ce = ids.k = 0;
+    }
     if constexpr (TBL) {
       if (m > 0 && m % CPB == 0) {
         id_batch = load_id_batch(m / CPB);
@@ -256,12 +363,12 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
       }
       const int sel = (m % CPB) * BPC;
       ids.b0 = clamp_id(__builtin_amdgcn_readlane(id_batch, sel));
-      ids.b1 = (BPC == 2 && b0 + 1 < blk_end)
+      ids.b1 = (BPC == 2 && b0 + 1 < bend)
                    ? clamp_id(__builtin_amdgcn_readlane(id_batch, sel + 1))
                    : ids.b0;
     } else {
       ids.b0 = clamp_id(contig0 + b0);
-      ids.b1 = (BPC == 2 && b0 + 1 < blk_end) ? clamp_id(contig0 + b0 + 1) : ids.b0;
+      ids.b1 = (BPC == 2 && b0 + 1 < bend) ? clamp_id(contig0 + b0 + 1) : ids.b0;
     }
     ids.vt = vpool + (size_t)(v_blk ? ids.b1 : ids.b0) * id_stride + (size_t)ids.ro * D * EB +
              v_off;
@@ -271,6 +378,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
 
   struct Regs {
     u32x4 v[NT];
+    int cs, ce, k;  // WG: the chunk these registers hold (see Ids)
   };
   auto rot = [](int t) { return t + 4 * (t >> 4); };
 
@@ -287,7 +395,8 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
         const_cast<char*>(kpool + (size_t)id * id_stride + (size_t)ro * RB), 0,
         (int)tile_bytes - ro * RB, kBufferFlags);
   };
-  auto load = [&](const Ids& ids, Regs& R, int slot) {
+  auto load_as = [&](const Ids& ids, Regs& R, int slot, auto nt) {
+    constexpr bool NTC = decltype(nt)::value;
     char* dst = smem + (wave * 2 + slot) * SLOT;
     const __amdgpu_buffer_rsrc_t r0 = tile_rsrc(ids.b0, ids.ro);
     const __amdgpu_buffer_rsrc_t r1 = BPC == 2 ? tile_rsrc(ids.b1, 0) : r0;
@@ -296,16 +405,32 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
       const int t = x * (1024 / RB) + lane / NPC;
       const int jt = (lane % NPC - rot(t)) & (NPC - 1);
       const bool second = BPC == 2 && x * (1024 / RB) >= S;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          second ? r1 : r0, (__attribute__((address_space(3))) void*)(dst + x * 1024), 16,
-          (t % S) * RB + jt * 16, 0, 0, NTL ? 2 : 0);
+      // WG: a member's own K streams from HBM with the non-temporal policy, so that it does
+      // not push the shared tiles out of L2 (its V loads stay ordinary: a choice of load
+      // instruction per chunk would cost the register waits their precision).
+      if (WG && ids.k >= 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            second ? r1 : r0, (__attribute__((address_space(3))) void*)(dst + x * 1024), 16,
+            (t % S) * RB + jt * 16, 0, 0, 2);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            second ? r1 : r0, (__attribute__((address_space(3))) void*)(dst + x * 1024), 16,
+            (t % S) * RB + jt * 16, 0, 0, NTC ? 2 : 0);
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       constexpr int kStep = 16 * VS * EB;
       const int off = nt * kStep;
-      R.v[nt] = load_kv<NTL, u32x4>(off < 4096 ? ids.vt + off : ids.vt4 + (off - 4096));
+      R.v[nt] = load_kv<NTC, u32x4>(off < 4096 ? ids.vt + off : ids.vt4 + (off - 4096));
     }
+  };
+  auto load = [&](const Ids& ids, Regs& R, int slot) {
+    if constexpr (WG) {
+      R.cs = ids.cs;
+      R.ce = ids.ce;
+      R.k = ids.k;
+    }
+    load_as(ids, R, slot, std::integral_constant<bool, NTL>());
   };
   // Operand pieces of chunk K from the wave's slot. The reads are issued as inline LDS
   // instructions that the compiler does not see as LDS reads, so it adds no waits of its own
@@ -338,7 +463,12 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
   // Chunk n from the registers R and LDS slot. Only a wave's last chunk can reach past the end
   // of the range (chunks are dealt round robin), so only that one (last = true) masks.
   auto compute = [&](int n, Regs& R, int slot, auto last) {
-    constexpr bool MASK = decltype(last)::value;
+    // WG: chunks of any range can be partial, so every chunk masks; a member's chunk feeds
+    // only that member's columns (the others see no position in it).
+    constexpr bool MASK = WG || decltype(last)::value;
+    const int cbase = WG ? R.cs : start + n * CT;
+    const int cend = WG ? R.ce : end;
+    const bool active = !WG || R.k < 0 || c / G == R.k;
     u32x4 kr[2][KK];
     read_k(slot, kr);
     f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -347,29 +477,32 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
       s0 = M::mac(__builtin_bit_cast(V8, kr[0][kk]), qb[kk], s0);
       s1 = M::mac(__builtin_bit_cast(V8, kr[1][kk]), qb[kk], s1);
     }
-    const int pos0 = start + n * CT + 8 * r;  // position of this lane's first logit
+    const int pos0 = cbase + 8 * r;  // position of this lane's first logit
     float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      sv[j] = (!MASK || pos0 + j < end) ? sv[j] * a.scale_log2e : -INFINITY;
+      sv[j] = (!MASK || (pos0 + j < cend && active)) ? sv[j] * a.scale_log2e : -INFINITY;
       mx = fmaxf(mx, sv[j]);
     }
     mx = across16(mx, OpMax());
     mx = across32(mx, OpMax());
     const float mnew = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    // WG: a column that has seen no position yet keeps m = -inf; offsetting by 0 instead keeps
+    // its weights and rescale at 0 rather than NaN.
+    const float mref = WG && mnew == -INFINITY ? 0.0f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(m - mref);
     m = mnew;
     V8 pb;
     float psum = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      pb[j] = M::narrow(__builtin_amdgcn_exp2f(sv[j] - mnew));
+      pb[j] = M::narrow(__builtin_amdgcn_exp2f(sv[j] - mref));
       psum += (float)pb[j];  // the sum matches the weights the product uses
     }
     l = fmaf(l, alpha, psum);
     // Positions past the end may hold anything (even NaN): zero them, 0 * NaN is NaN.
-    const int nv = end - pos0;
+    const int nv = cend - pos0;
     if (MASK && nv < 8) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -388,23 +521,56 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
   // Position L-1 joins the merge below as one more partial state (m = its logit, l = 1,
   // acc = its V row). Its rows are loaded before the first chunk (vector loads return in
   // order, so waiting for them below does not wait for the chunk).
-  const char* kn = reinterpret_cast<const char*>(a.new_key) + ((size_t)i * Hkv + g) * D * EB;
+  // WG: every member's newest position; the K row pieces of member k go to lanes
+  // k * PPR .. k * PPR + PPR - 1, and lane (r, c)'s logit pieces are those of its column's
+  // member.
+  constexpr int NMEM = WG ? 4 : 1;   // newest rows per unit
+  constexpr int PPR = D * EB / 16;   // sixteen-byte pieces per K row
+  auto new_row = [&](int seq) {      // this kv head's newest K row of sequence seq, in bytes
+    return reinterpret_cast<const char*>(a.new_key) + ((size_t)seq * Hkv + g) * D * EB;
+  };
+  const char* kn = new_row(i);
   const T* vn = reinterpret_cast<const T*>(a.new_value) + ((size_t)i * Hkv + g) * D;
   u32x4 kpiece[KK];
   u32x4 krow = {0u, 0u, 0u, 0u};
-  T vrow[D / 64];
-  int slot_blk = 0;
+  T vrow[NMEM][D / 64];
+  int slot_blk[NMEM];
+#pragma unroll
+  for (int k = 0; k < NMEM; ++k) slot_blk[k] = 0;
   if (fused) {
     if (wave == NW - 1) {
+      if constexpr (WG) {
+        const int qs = column_seq(c);
+        const char* kp = new_row(max(qs, 0));
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        kpiece[kk] = *reinterpret_cast<const u32x4*>(kn + (32 * kk + 8 * r) * EB);
+        for (int kk = 0; kk < KK; ++kk)
+          kpiece[kk] = qs >= 0 ? *reinterpret_cast<const u32x4*>(kp + (32 * kk + 8 * r) * EB)
+                               : u32x4{0u, 0u, 0u, 0u};
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          kpiece[kk] = *reinterpret_cast<const u32x4*>(kn + (32 * kk + 8 * r) * EB);
+      }
     }
     if (wave == 0) {
-      slot_blk = TBL ? bt[(L - 1) / S] : contig0 + (L - 1) / S;
-      if (lane < D * EB / 16) krow = reinterpret_cast<const u32x4*>(kn)[lane];
+      if constexpr (WG) {
 #pragma unroll
-      for (int e = 0; e < D / 64; ++e) vrow[e] = vn[lane + 64 * e];
+        for (int k = 0; k < NMEM; ++k) {
+          const bool has = wm[k] >= 0 && wL[k] > 0;
+          slot_blk[k] = has ? a.block_tables[(size_t)wm[k] * MB + (wL[k] - 1) / S] : 0;
+          const T* vk = reinterpret_cast<const T*>(a.new_value) + ((size_t)max(wm[k], 0) * Hkv + g) * D;
+#pragma unroll
+          for (int e = 0; e < D / 64; ++e) vrow[k][e] = has ? vk[lane + 64 * e] : T(0);
+        }
+        const int km = lane / PPR;
+        const int kmem = km < 4 ? wm[km] : -1;
+        if (kmem >= 0) krow = reinterpret_cast<const u32x4*>(new_row(kmem))[lane % PPR];
+      } else {
+        slot_blk[0] = TBL ? bt[(L - 1) / S] : contig0 + (L - 1) / S;
+        if (lane < PPR) krow = reinterpret_cast<const u32x4*>(kn)[lane];
+#pragma unroll
+        for (int e = 0; e < D / 64; ++e) vrow[0][e] = vn[lane + 64 * e];
+      }
     }
   }
 
@@ -422,15 +588,17 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
       }
       part_dot = across16(part_dot, OpAdd());
       part_dot = across32(part_dot, OpAdd());
-      if (r == 0 && c < G) sh_new[c] = part_dot * a.scale_log2e;
+      if (r == 0 && c < ncol) sh_new[c] = part_dot * a.scale_log2e;
     }
     if (wave == 0) {
 #pragma unroll
-      for (int e = 0; e < D / 64; ++e) {
-        const int d = lane + 64 * e;
-        if constexpr (DT == Dt::BF16) sh_vnew[d] = bits_f((uint32_t)vrow[e] << 16);
-        else sh_vnew[d] = (float)vrow[e];
-      }
+      for (int k = 0; k < NMEM; ++k)
+#pragma unroll
+        for (int e = 0; e < D / 64; ++e) {
+          const int d = lane + 64 * e;
+          if constexpr (DT == Dt::BF16) sh_vnew[k * D + d] = bits_f((uint32_t)vrow[k][e] << 16);
+          else sh_vnew[k * D + d] = (float)vrow[k][e];
+        }
     }
   };
 
@@ -480,14 +648,23 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
   // The new rows go to the slot the table maps position L-1 to. The stores come after every
   // block-table read so the table can stay in the scalar cache (a store that might alias it
   // would force those reads through the vector memory path).
+  // WG: each member's rows (V read back from LDS, where it is stored exactly).
   if (fused && wave == 0) {
-    const int p = L - 1;
-    const size_t tile = ((size_t)clamp_id(slot_blk) * Hkv + g) * S * D;
-    T* kc = reinterpret_cast<T*>(a.k_cache) + tile + (size_t)(p % S) * D;
-    T* vc = reinterpret_cast<T*>(a.v_cache) + tile + (size_t)((p % S) / VS) * VS * D + p % VS;
-    if (lane < D * EB / 16) reinterpret_cast<u32x4*>(kc)[lane] = krow;
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) vc[(size_t)(lane + 64 * e) * VS] = vrow[e];
+    for (int k = 0; k < NMEM; ++k) {
+      const int Lk = WG ? wL[k] : L;
+      if (WG && (wm[k] < 0 || Lk <= 0)) continue;
+      const int p = Lk - 1;
+      const size_t tile = ((size_t)clamp_id(slot_blk[k]) * Hkv + g) * S * D;
+      T* kc = reinterpret_cast<T*>(a.k_cache) + tile + (size_t)(p % S) * D;
+      T* vc = reinterpret_cast<T*>(a.v_cache) + tile + (size_t)((p % S) / VS) * VS * D + p % VS;
+      if (WG ? lane / PPR == k : lane < PPR)
+        reinterpret_cast<u32x4*>(kc)[WG ? lane % PPR : lane] = krow;
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e)
+        vc[(size_t)(lane + 64 * e) * VS] =
+            WG ? from_f32<DT>(sh_vnew[k * D + lane + 64 * e]) : vrow[0][e];
+    }
   }
 
   l = across16(l, OpAdd());
@@ -514,6 +691,11 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
     float Mx = fused ? sh_new[h] : -INFINITY;
 #pragma unroll
     for (int v = 0; v < NW; ++v) Mx = fmaxf(Mx, sh_m[v][h]);
+    if (WG && Mx == -INFINITY) {  // a member with no position at all: a zero row
+      reinterpret_cast<T*>(a.out)[((size_t)seq * H + (size_t)g * G + h % G) * D + d] =
+          from_f32<DT>(0.0f);
+      continue;
+    }
     float num = 0.0f, den = 0.0f;
 #pragma unroll
     for (int v = 0; v < NW; ++v) {
@@ -523,7 +705,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
     }
     if (fused) {
       const float f = __builtin_amdgcn_exp2f(sh_new[h] - Mx);
-      num = fmaf(f, sh_vnew[d], num);
+      num = fmaf(f, sh_vnew[(WG ? h / G : 0) * D + d], num);
       den += f;
     }
     const float o = num / den;
@@ -607,9 +789,20 @@ hipError_t launch_combined(const DecodeParams& grp, const DecodeParams& rest,
   return hipGetLastError();
 }
 
+// Whole groups sharing a prefix: final outputs, one workgroup per (group, kv head), head g on
+// XCD g % 8 so a shared tile stays in one L2; each chunk picks its own cache policy.
+template <Dt DT, int D, int S>
+hipError_t launch_whole(const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)p.num_units * (unsigned)p.num_kv_heads);
+  decode_mfma_kernel<DT, D, S, kMfmaWaves, false, false, true, true>
+      <<<grid, dim3(kMfmaWaves * 64), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
 template <Dt DT, int D, int S>
 hipError_t launch_s(bool partial, bool nt, const DecodeParams& p, hipStream_t stream) {
-  if (p.group_members) return partial ? launch_grouped<DT, D, S>(p, stream) : hipErrorNotSupported;
+  if (p.group_members)
+    return partial ? launch_grouped<DT, D, S>(p, stream) : launch_whole<DT, D, S>(p, stream);
   if (partial) return nt ? launch_p<DT, D, S, true, true>(p, stream) : launch_p<DT, D, S, true, false>(p, stream);
   return nt ? launch_p<DT, D, S, false, true>(p, stream) : launch_p<DT, D, S, false, false>(p, stream);
 }

@@ -116,3 +116,51 @@ def plan(block_tables: np.ndarray, context_lens: np.ndarray, block_size: int,
     order = np.argsort(-np.asarray(sizes, dtype=np.int64), kind="stable")
     items = np.asarray(units, dtype=np.int32)[order] if units else np.zeros(0, np.int32)
     return SharedPlan(P, NP, groups, items)
+
+
+@dataclasses.dataclass
+class WholePlan:
+    shared_len: int           # positions every member of a group shares (a multiple of S)
+    groups: np.ndarray        # int32 [num_groups, 4], -1 pads, most positions first
+
+
+def plan_whole(block_tables: np.ndarray, context_lens: np.ndarray, block_size: int,
+               group: int, newest_outside: bool = True,
+               prefix_blocks: int | None = None) -> WholePlan | None:
+    """Groups for pkv_paged_attention_decode_grouped: every sequence in exactly one group of up
+    to group_width(group) sequences whose tables agree over the first prefix_blocks entries
+    (default: the length that saves the most tile reads, see best_prefix_blocks); a sequence
+    sharing with none is a group of its own. Within a class of sequences that agree, members are
+    dealt to the class's groups longest own part first onto the group with the fewest own
+    positions, so the groups' work is even; groups are listed with the most positions first.
+    None when some sequence is too short for the shared length (it must reach past it, by one
+    more position when the step writes the newest token) or nothing is shared."""
+    S = int(block_size)
+    L = np.asarray(context_lens).astype(np.int64)
+    tables = np.asarray(block_tables)
+    width = group_width(group)
+    nb = (best_prefix_blocks(tables, L, S, width, newest_outside) if prefix_blocks is None
+          else int(prefix_blocks))
+    if nb <= 0 or not len(L):
+        return None
+    P = nb * S
+    need = P + (1 if newest_outside else 0)
+    if (L < need).any():
+        return None
+    classes: dict[bytes, list[int]] = {}
+    for i in range(len(L)):
+        classes.setdefault(tables[i, :nb].tobytes(), []).append(i)
+    groups, loads = [], []
+    for members in classes.values():
+        ng = -(-len(members) // width)
+        rows = [[] for _ in range(ng)]
+        load = [0] * ng
+        for i in sorted(members, key=lambda m: -int(L[m])):
+            k = min((j for j in range(ng) if len(rows[j]) < width), key=lambda j: load[j])
+            rows[k].append(i)
+            load[k] += int(L[i]) - P
+        for row, ld in zip(rows, load):
+            groups.append(row + [-1] * (4 - len(row)))
+            loads.append(P + ld)
+    order = np.argsort(-np.asarray(loads, dtype=np.int64), kind="stable")
+    return WholePlan(P, np.asarray(groups, dtype=np.int32).reshape(-1, 4)[order])

@@ -32,11 +32,11 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
-    assert len(names) == 40, names
+    assert len(names) == 41, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES), "binding prototypes out of step with the header"
-    assert lib.pkv_abi_version() == 4
+    assert lib.pkv_abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -172,6 +172,38 @@ def shared(lib, **kw):
 ])
 def test_decode_shared_validation(lib, kw, status):
     assert shared(lib, **kw) == status
+
+
+def grouped(lib, **kw):
+    a = dict(out=A16, q=A16, k=A16, v=A16, bt=A16, MB=4, lens=A16, groups=A16, ng=2, P=32,
+             nk=None, nv=None, B=8, H=8, Hkv=2, D=128, S=16, N=32, scale=0.125, dtype=2)
+    a.update(kw)
+    return lib.pkv_paged_attention_decode_grouped(
+        a["out"], a["q"], a["k"], a["v"], a["bt"], a["MB"], a["lens"], a["groups"], a["ng"],
+        a["P"], a["nk"], a["nv"], a["B"], a["H"], a["Hkv"], a["D"], a["S"], a["N"], a["scale"],
+        a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=0), UNSUPPORTED),            # the matrix-core kernel: fp16/bf16
+    (dict(dtype=5), INVALID),
+    (dict(P=24), INVALID),                   # not a multiple of the block size
+    (dict(P=80), INVALID),                   # beyond max_blocks_per_seq * block_size
+    (dict(P=-16), INVALID),
+    (dict(groups=A16 + 4), INVALID),
+    (dict(groups=None), INVALID),
+    (dict(ng=-1), INVALID),
+    (dict(nk=A16), INVALID),                 # new rows come in pairs
+    (dict(H=64, Hkv=2), UNSUPPORTED),        # group 32
+    (dict(D=96), UNSUPPORTED),
+    (dict(scale=float("nan")), INVALID),
+    (dict(MB=(1 << 31) // 16), INVALID),
+    (dict(ng=0), OK),                        # nothing to do, nothing enqueued
+    (dict(B=0), OK),
+    (dict(P=0, ng=0), OK),
+])
+def test_decode_grouped_validation(lib, kw, status):
+    assert grouped(lib, **kw) == status
 
 
 def test_vmm_pool_validation(lib):

@@ -168,3 +168,102 @@ def test_one_launch_equals_two_launches(size, over, listed):
     assert torch.equal(da.k.view(torch.int16), db.k.view(torch.int16))
     assert torch.equal(da.v.view(torch.int16), db.v.view(torch.int16))
     assert not torch.isnan(wb[0]).all(), "the launch wrote partials"
+
+
+# ------------------------------------------------------------------ whole groups, one pass
+
+def whole_step(wl, groups, shared_len, fused=True):
+    """copy_blocks (the workload's copy-on-write) -> [reshape_and_cache] -> whole-group decode."""
+    c = wl.cfg
+    d = upload(wl)
+    if len(wl.block_mapping):
+        pk.copy_blocks([d.k], [d.v], d.mapping)
+    if not fused:
+        pk.reshape_and_cache(d.key, d.value, d.k, d.v, d.slots)
+    out = torch.full((c.num_seqs, c.num_heads, c.head_dim), float("nan"),
+                     dtype=TORCH_DT[c.dtype], device="cuda")
+    pk.paged_attention_decode_grouped(out, d.q, d.k, d.v, d.bt, d.lens,
+                                      to_dev(np.asarray(groups, dtype=np.int32)), shared_len,
+                                      c.scale, new_key=d.key if fused else None,
+                                      new_value=d.value if fused else None)
+    torch.cuda.synchronize()
+    return out, d
+
+
+def _check_whole(wl, groups, shared_len, fused=True):
+    c = wl.cfg
+    out, d = whole_step(wl, groups, shared_len, fused)
+    kc, vc = oracle_pools(wl)
+    got = out_f64(out)
+    members = sorted(int(m) for m in np.asarray(groups).ravel() if m >= 0)
+    err = oracle.max_abs_err(got[members], oracle_out(wl, members, pools=(kc, vc)))
+    print(f"[gpu] whole groups: {len(groups)} groups, shared {shared_len}, fused {fused}, "
+          f"max abs err {err:.3g}", file=sys.stderr, flush=True)
+    assert err <= TOL[c.dtype], f"max abs err {err}"
+    others = np.setdiff1d(np.arange(c.num_seqs), members)
+    assert np.isnan(got[others]).all(), "rows of sequences in no group stay untouched"
+    assert np.array_equal(bits(to_host(d.k, c.dtype)), bits(kc))
+    assert np.array_equal(bits(to_host(d.v, c.dtype)), bits(vc))
+
+
+WHOLE = [({}, True), ({}, False), ({"num_heads": 16}, True), ({"num_heads": 4}, True),
+         ({"num_heads": 32}, True), ({"dtype": "f16", "head_dim": 64}, True),
+         ({"head_dim": 64}, False),
+         ({"block_size": 32, "prefix_len": 64, "num_blocks": 24}, True),
+         ({"block_size": 64, "prefix_len": 192, "num_blocks": 16}, True),
+         ({"block_size": 128, "prefix_len": 256, "num_blocks": 16}, True),
+         ({"block_size": 256, "prefix_len": 512, "num_blocks": 16}, True)]
+
+
+@pytest.mark.parametrize("over,fused", WHOLE,
+                         ids=[f"{'-'.join(f'{k}{v}' for k, v in c[0].items()) or 'base'}-"
+                              f"{'fused' if c[1] else 'unfused'}" for c in WHOLE])
+def test_whole_groups_match_oracle(over, fused):
+    """Every sequence of the prefix workload in groups sharing the prefix (one pass per
+    group): outputs against the oracle, and the copy-on-write plus newest-token writes bit for
+    bit."""
+    wl = W.generate(W.SMALL["c4"].replace(**over))
+    c = wl.cfg
+    nb = c.prefix_len // c.block_size - 1  # the last prefix block is copied for some sequences
+    plan = sharing.plan_whole(wl.block_tables, wl.context_lens, c.block_size, c.group,
+                              newest_outside=fused, prefix_blocks=nb)
+    assert plan is not None
+    _check_whole(wl, plan.groups, plan.shared_len, fused)
+
+
+@pytest.mark.parametrize("name,width", [("c3", 4), ("c3", 3), ("c5", 2), ("c2", 4)])
+def test_whole_groups_without_shared_positions(name, width):
+    """shared_len = 0: any grouping is valid, and every chunk is one member's own -- the
+    column masking and the interleaving of members' chunks on their own."""
+    wl = W.generate(W.SMALL[name])
+    c = wl.cfg
+    if c.dtype == "f32":
+        pytest.skip("fp32 has no matrix-core path")
+    w = min(width, sharing.group_width(c.group))
+    order = np.random.default_rng(5).permutation(c.num_seqs).tolist()
+    groups = [order[k:k + w] + [-1] * (4 - len(order[k:k + w])) for k in range(0, c.num_seqs, w)]
+    _check_whole(wl, groups, 0, fused=True)
+    _check_whole(wl, groups[: max(1, len(groups) - 1)], 0, fused=False)
+
+
+def test_whole_groups_members_with_no_own_positions():
+    """Members whose only position past the shared part is the newest one, sequences whose
+    copied last prefix block keeps them out of the sharing class (groups of their own)."""
+    cfg = W.SMALL["c4"]
+    P = cfg.prefix_len
+    lens = np.array([P + 1, P + 30, P + 1, P + 1, P + 2, P + 1, P + 40, P + 1], dtype=np.int32)
+    wl = W.generate(cfg, lens=lens)
+    plan = sharing.plan_whole(wl.block_tables, wl.context_lens, cfg.block_size, cfg.group,
+                              prefix_blocks=P // cfg.block_size)
+    assert plan is not None and plan.shared_len == P
+    _check_whole(wl, plan.groups, plan.shared_len, fused=True)
+
+
+def test_whole_groups_full_size():
+    """The prefix-shared batch: 64 balanced groups of four, every sequence against the
+    oracle."""
+    wl = W.generate(W.CONFIGS["c4"])
+    c = wl.cfg
+    plan = sharing.plan_whole(wl.block_tables, wl.context_lens, c.block_size, c.group)
+    assert plan.shared_len == 1008 and len(plan.groups) == 64
+    _check_whole(wl, plan.groups, plan.shared_len, fused=True)

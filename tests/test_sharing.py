@@ -97,3 +97,70 @@ def test_group_contract_with_the_work_list():
     with pytest.raises(C.ContractError):             # but the newest position would be in it
         C.check_groups(g, wl.block_tables, L, P, S, N, 4, work_items=plan.work_items,
                        num_partitions=NP, fused_write=True)
+
+
+@pytest.mark.parametrize("heads,width", [(8, 4), (16, 2), (4, 4), (32, 1)])
+def test_whole_plan_covers_every_sequence_once(heads, width):
+    cfg = W.SMALL["c4"].replace(num_heads=heads)
+    wl = W.generate(cfg)
+    S = cfg.block_size
+    plan = sharing.plan_whole(wl.block_tables, wl.context_lens, S, cfg.group)
+    if width == 1:  # one sequence per group: grouping would save no read
+        assert plan is None
+        plan = sharing.plan_whole(wl.block_tables, wl.context_lens, S, cfg.group,
+                                  prefix_blocks=cfg.prefix_len // S - 1)
+    assert plan is not None and plan.shared_len == (cfg.prefix_len // S - 1) * S
+    g = plan.groups
+    assert g.shape[1] == 4 and ((g >= 0).sum(axis=1) <= width).all() and (g[:, 0] >= 0).all()
+    members = g[g >= 0]
+    assert sorted(members.tolist()) == list(range(cfg.num_seqs))
+    C.check_whole_groups(g, wl.block_tables, wl.context_lens, plan.shared_len, S,
+                         cfg.num_blocks, cfg.group, fused_write=True)
+    load = [plan.shared_len + sum(int(wl.context_lens[m]) - plan.shared_len for m in row if m >= 0)
+            for row in g]
+    assert load == sorted(load, reverse=True)
+
+
+def test_whole_plan_balances_the_groups():
+    """The prefix-shared batch: 256 sequences in 64 groups of four whose own positions (past
+    the shared 1008) differ by little; every group holds four members."""
+    cfg = W.CONFIGS["c4"]
+    wl = W.generate(cfg, poison="zero")
+    plan = sharing.plan_whole(wl.block_tables, wl.context_lens, cfg.block_size, cfg.group)
+    assert plan.shared_len == 1008 and plan.groups.shape == (64, 4) and (plan.groups >= 0).all()
+    own = [sum(int(wl.context_lens[m]) - plan.shared_len for m in row) for row in plan.groups]
+    assert max(own) - min(own) <= 0.05 * np.mean(own)
+
+
+def test_whole_plan_needs_every_sequence_past_the_shared_part():
+    wl = W.generate(W.SMALL["c4"])
+    L = wl.context_lens.copy()
+    plan = sharing.plan_whole(wl.block_tables, L, 16, 4)
+    L[2] = plan.shared_len  # the newest position would fall in the shared part
+    assert sharing.plan_whole(wl.block_tables, L, 16, 4, prefix_blocks=plan.shared_len // 16) is None
+    assert sharing.plan_whole(wl.block_tables, L, 16, 4, newest_outside=False,
+                              prefix_blocks=plan.shared_len // 16) is not None
+    assert sharing.plan_whole(W.generate(W.SMALL["c3"]).block_tables,
+                              W.generate(W.SMALL["c3"]).context_lens, 16, 4) is None
+
+
+def test_whole_group_contract_violations():
+    wl = W.generate(W.SMALL["c4"])
+    c = wl.cfg
+    plan = sharing.plan_whole(wl.block_tables, wl.context_lens, c.block_size, c.group)
+    args = (wl.block_tables, wl.context_lens, plan.shared_len, c.block_size, c.num_blocks, c.group)
+    C.check_whole_groups(plan.groups, *args, fused_write=True)
+    bad = plan.groups.copy()
+    bad[0, 1] = bad[1, 0]  # a sequence in two groups
+    with pytest.raises(C.ContractError):
+        C.check_whole_groups(bad, *args)
+    tables = wl.block_tables.copy()
+    m = int(plan.groups[0, 1])
+    tables[m, 0] = (tables[m, 0] + 1) % c.num_blocks  # a member disagrees over the shared part
+    with pytest.raises(C.ContractError):
+        C.check_whole_groups(plan.groups, tables, *args[1:])
+    tables = wl.block_tables.copy()
+    nb = -(-int(wl.context_lens[m]) // c.block_size)
+    tables[m, nb - 1] = c.num_blocks  # a member's own block outside the pool
+    with pytest.raises(C.ContractError):
+        C.check_whole_groups(plan.groups, tables, *args[1:])
