@@ -380,7 +380,18 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
     u32x4 v[NT];
     int cs, ce, k;  // WG: the chunk these registers hold (see Ids)
   };
-  auto rot = [](int t) { return t + 4 * (t >> 4); };
+  // Placement of a K row's pieces. A wave's 16-byte LDS read is served in four passes of 16
+  // lanes over the 256 bytes of bank space (gfx950: lanes 0-7 with 24-31, 8-15 with 16-23,
+  // and the same in the upper half, as the bank-conflict counter shows for test patterns), so
+  // a conflict-free read needs each pass's 16 pieces in 16 different 16-byte bank slots. With
+  // 256-byte rows (head_dim 128) the slot is the rotated piece index: rows 0-3 and 8-11 (and
+  // 4-7, 12-15) must take the eight even rotations and rows 16-19 and 24-27 the same, which
+  // 2 (t mod 4) + 8 (t / 8 mod 2) does (lane (r, c) adds r, odd for half of each pass).
+  // With 128-byte rows (head_dim 64) two rows share the bank space and t + 4 (t / 16) is
+  // conflict-free as it is.
+  auto rot = [](int t) {
+    return NPC == 16 ? 2 * (t & 3) + 8 * ((t >> 3) & 1) : t + 4 * (t >> 4);
+  };
 
   // Chunk loads: K with KLD coalesced 1 KiB buffer loads straight into the wave's LDS slot
   // (lane l of load x fills row t = x * (1024 / RB) + l / NPC, rotated piece l % NPC), V^T

@@ -1,7 +1,9 @@
 // Paged decode attention on the vector ALUs (fp32, and fp16/bf16 when the query group is too
-// small for a dense product). One workgroup of NW waves owns one (sequence, kv head, range)
-// unit; each wave walks a contiguous run of the range's blocks with an online softmax, and the
-// waves merge their (max, sum, accumulator) states through LDS at the end.
+// small for a dense product). One workgroup of NW waves owns one (sequence, range) unit for
+// HPW adjacent kv heads (two when the kv head count is even, so the two tiles of a block it
+// reads at once are one contiguous run); each of a head's NW / HPW waves walks every
+// (NW / HPW)-th step of the range with an online softmax, and a head's waves merge their
+// (max, sum, accumulator) states through LDS at the end.
 //
 // The operation is attention over non-contiguous KV-cache blocks (vAttention, section 3.1
 // "Requires re-writing the attention kernel"): each block is found through the sequence's
@@ -27,9 +29,11 @@
 namespace pkv {
 namespace {
 
-template <Dt DT, int D, int S, int G, int NW, bool PARTIAL, bool NTL>
+template <Dt DT, int D, int S, int G, int NW, int HPW, bool PARTIAL, bool NTL>
 __global__ void __launch_bounds__(NW * 64)
 decode_valu_kernel(const DecodeParams a) {
+  constexpr int WPH = NW / HPW;  // waves per kv head
+  static_assert(WPH * HPW == NW, "waves must split evenly over the workgroup's kv heads");
   constexpr int EB = Elt<DT>::bytes;
   constexpr int VEC = 16 / EB;   // elements per 16-byte piece
   constexpr int LPR = D / VEC;   // lanes per K row
@@ -45,51 +49,57 @@ decode_valu_kernel(const DecodeParams a) {
   __shared__ float sh_m[NW][G];
   __shared__ float sh_l[NW][G];
   __shared__ float sh_acc[NW][G][D];
-  __shared__ float sh_new[G];
-  __shared__ float sh_vnew[D];
+  __shared__ float sh_new[HPW][G];
+  __shared__ float sh_vnew[HPW][D];
 
   const int Hkv = a.num_kv_heads;
   const int H = a.num_heads;
   const int MB = a.max_blocks_per_seq;
-  // Workgroups go to the XCDs round robin (w % 8). Unshared KV (non-temporal loads): every kv
-  // head of a unit on one XCD (groups of 8 Hkv workgroups hold 8 units, head g of the group's
-  // unit j at 8 g + j), so an XCD streams whole blocks of its sequences. Cached loads (shared
-  // prefix blocks): head g of every unit on XCD g % 8, so a shared tile stays in one L2.
+  // A workgroup takes kv heads HPW gg .. HPW gg + HPW - 1 (head group gg; waves 0 .. WPH-1
+  // the first head). Workgroups go to the XCDs round robin (w % 8). Unshared KV (non-temporal
+  // loads): every head group of a unit on one XCD (groups of 8 HG workgroups hold 8 units,
+  // head group gg of the group's unit j at 8 gg + j), so an XCD streams whole blocks of its
+  // sequences. Cached loads (shared prefix blocks): head group gg of every unit on XCD gg % 8,
+  // so a shared tile stays in one L2.
   const int w = blockIdx.x;
+  const int HG = Hkv / HPW;  // kv-head groups per unit
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int hw = wave / WPH;  // this wave's head within the workgroup
+  const int wv = wave % WPH;  // this wave's index among its head's waves
   int g, slot;
   if constexpr (NTL) {
     constexpr int XC = 8;
-    g = (w % (XC * Hkv)) / XC;
-    slot = (w / (XC * Hkv)) * XC + w % XC;
+    g = (w % (XC * HG)) / XC;
+    slot = (w / (XC * HG)) * XC + w % XC;
     if (slot >= a.num_units) return;  // the grid is padded to whole groups of 8 units
   } else {
-    g = w % Hkv;
-    slot = w / Hkv;
+    g = w % HG;
+    slot = w / HG;
   }
+  g = g * HPW + hw;
   int unit = a.work_items ? a.work_items[slot] : slot;
   unit = min(max(unit, 0), a.num_seqs * a.num_ranges - 1);
   const int part = unit % a.num_ranges;
   const int i = unit / a.num_ranges;
-  const int lane = lane_id();
-  const int wave = wave_id();
   const int r = lane / LPR;
   const int c = lane % LPR;
   const int32_t* bt = a.block_tables + (size_t)i * MB;
   auto table = [&](int j) { return bt[j]; };
   const int start = part * a.range_tokens;
 
-  // Waves take steps start/CS + wave, + NW, ... (step b covers positions b*CS .. b*CS+CS-1 of
-  // logical block b / SPB); the first one's id is fetched before the context length arrives
-  // (any entry of the row may be read; ids are clamped before use).
-  const int b_first = start / CS + wave;
+  // A head's waves take steps start/CS + wv, + WPH, ... (step b covers positions b*CS ..
+  // b*CS+CS-1 of logical block b / SPB); the first one's id is fetched before the context
+  // length arrives (any entry of the row may be read; ids are clamped before use).
+  const int b_first = start / CS + wv;
   const int first_id = b_first / SPB < MB ? table(b_first / SPB) : 0;
 
   int L = a.context_lens[i];
   L = min(max(L, 0), MB * S);
   if (start >= L) {
     if (!PARTIAL && part == 0) {
-      T* o = reinterpret_cast<T*>(a.out) + ((size_t)i * H + (size_t)g * G) * D;
-      for (int e = threadIdx.x; e < G * D; e += NW * 64) o[e] = from_f32<DT>(0.0f);
+      T* o = reinterpret_cast<T*>(a.out) + ((size_t)i * H + (size_t)(g - hw) * G) * D;
+      for (int e = threadIdx.x; e < HPW * G * D; e += NW * 64) o[e] = from_f32<DT>(0.0f);
     }
     return;
   }
@@ -212,8 +222,8 @@ decode_valu_kernel(const DecodeParams a) {
   T vrow[D / 64];
   int slot_blk = 0;
   if (fused) {
-    if (wave == NW - 1) kpiece = *reinterpret_cast<const u32x4*>(kn + (size_t)c * 16);
-    if (wave == 0) {
+    if (wv == WPH - 1) kpiece = *reinterpret_cast<const u32x4*>(kn + (size_t)c * 16);
+    if (wv == 0) {
       slot_blk = table((L - 1) / S);
       if (lane < D * EB / 16) krow = reinterpret_cast<const u32x4*>(kn)[lane];
 #pragma unroll
@@ -222,9 +232,9 @@ decode_valu_kernel(const DecodeParams a) {
   }
 
   // Consumes the new rows loaded above (after this wave's first loads are in flight): the
-  // last wave's logits and wave 0's LDS copy of the V row.
+  // head's last wave's logits and its first wave's LDS copy of the V row.
   auto use_new_rows = [&]() {
-    if (wave == NW - 1) {
+    if (wv == WPH - 1) {
       const uint32_t kw4[4] = {kpiece.x, kpiece.y, kpiece.z, kpiece.w};
       float kf[VEC];
       unpack_words<DT, 4>(kw4, kf);
@@ -234,16 +244,16 @@ decode_valu_kernel(const DecodeParams a) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) t = fmaf(qf[h][e], kf[e], t);
         t = group_reduce<LPR>(t, OpAdd());
-        if (lane == 0) sh_new[h] = t * a.scale_log2e;
+        if (lane == 0) sh_new[hw][h] = t * a.scale_log2e;
       }
     }
-    if (wave == 0) {
+    if (wv == 0) {
 #pragma unroll
       for (int e = 0; e < D / 64; ++e) {
         const int d = lane + 64 * e;
-        if constexpr (DT == Dt::F32) sh_vnew[d] = vrow[e];
-        else if constexpr (DT == Dt::BF16) sh_vnew[d] = bits_f((uint32_t)vrow[e] << 16);
-        else sh_vnew[d] = (float)vrow[e];
+        if constexpr (DT == Dt::F32) sh_vnew[hw][d] = vrow[e];
+        else if constexpr (DT == Dt::BF16) sh_vnew[hw][d] = bits_f((uint32_t)vrow[e] << 16);
+        else sh_vnew[hw][d] = (float)vrow[e];
       }
     }
   };
@@ -252,24 +262,24 @@ decode_valu_kernel(const DecodeParams a) {
   if (b < blk_hi) {
     Regs A, B;
     load(clamp_id(first_id), b, A);
-    int id = b + NW < blk_hi ? clamp_id(table((b + NW) / SPB)) : 0;
+    int id = b + WPH < blk_hi ? clamp_id(table((b + WPH) / SPB)) : 0;
     if (fused) use_new_rows();
-    // Two register sets: step b + NW loads while step b computes; its id was fetched one
+    // Two register sets: step b + WPH loads while step b computes; its id was fetched one
     // step earlier still.
     while (true) {
-      if (b + NW < blk_hi) {
-        load(id, b + NW, B);
-        if (b + 2 * NW < blk_hi) id = clamp_id(table((b + 2 * NW) / SPB));
+      if (b + WPH < blk_hi) {
+        load(id, b + WPH, B);
+        if (b + 2 * WPH < blk_hi) id = clamp_id(table((b + 2 * WPH) / SPB));
       }
       compute(b, A);
-      b += NW;
+      b += WPH;
       if (b >= blk_hi) break;
-      if (b + NW < blk_hi) {
-        load(id, b + NW, A);
-        if (b + 2 * NW < blk_hi) id = clamp_id(table((b + 2 * NW) / SPB));
+      if (b + WPH < blk_hi) {
+        load(id, b + WPH, A);
+        if (b + 2 * WPH < blk_hi) id = clamp_id(table((b + 2 * WPH) / SPB));
       }
       compute(b, B);
-      b += NW;
+      b += WPH;
       if (b >= blk_hi) break;
     }
   } else if (fused) {
@@ -279,7 +289,7 @@ decode_valu_kernel(const DecodeParams a) {
   // The new rows go to the slot the table maps position L-1 to. The stores come after every
   // block-table read so the table can stay in the scalar cache (a store that might alias it
   // would force those reads through the vector memory path).
-  if (fused && wave == 0) {
+  if (fused && wv == 0) {
     const int p = L - 1;
     const size_t tile = ((size_t)clamp_id(slot_blk) * Hkv + g) * S * D;
     T* kc = reinterpret_cast<T*>(a.k_cache) + tile + (size_t)(p % S) * D;
@@ -311,27 +321,29 @@ decode_valu_kernel(const DecodeParams a) {
   }
   __syncthreads();
 
-  // Merge the waves: M = max m_w, weights 2^(m_w - M) (a wave without blocks has m = -inf).
-  for (int e = threadIdx.x; e < G * D; e += NW * 64) {
-    const int h = e / D;
+  // Merge each head's waves: M = max m_w, weights 2^(m_w - M) (a wave without blocks has
+  // m = -inf).
+  for (int e = threadIdx.x; e < HPW * G * D; e += NW * 64) {
+    const int hh = e / (G * D);
+    const int h = (e / D) % G;
     const int d = e % D;
-    float M = fused ? sh_new[h] : -INFINITY;
+    float M = fused ? sh_new[hh][h] : -INFINITY;
 #pragma unroll
-    for (int v = 0; v < NW; ++v) M = fmaxf(M, sh_m[v][h]);
+    for (int v = 0; v < WPH; ++v) M = fmaxf(M, sh_m[hh * WPH + v][h]);
     float num = 0.0f, den = 0.0f;
 #pragma unroll
-    for (int v = 0; v < NW; ++v) {
-      const float f = __builtin_amdgcn_exp2f(sh_m[v][h] - M);
-      num = fmaf(f, sh_acc[v][h][d], num);
-      den = fmaf(f, sh_l[v][h], den);
+    for (int v = 0; v < WPH; ++v) {
+      const float f = __builtin_amdgcn_exp2f(sh_m[hh * WPH + v][h] - M);
+      num = fmaf(f, sh_acc[hh * WPH + v][h][d], num);
+      den = fmaf(f, sh_l[hh * WPH + v][h], den);
     }
     if (fused) {
-      const float f = __builtin_amdgcn_exp2f(sh_new[h] - M);
-      num = fmaf(f, sh_vnew[d], num);
+      const float f = __builtin_amdgcn_exp2f(sh_new[hh][h] - M);
+      num = fmaf(f, sh_vnew[hh][d], num);
       den += f;
     }
     const float o = num / den;
-    const size_t row = (size_t)i * H + (size_t)g * G + h;
+    const size_t row = (size_t)i * H + (size_t)(g - hw + hh) * G + h;
     if constexpr (PARTIAL) {
       const size_t rec = row * a.num_ranges + part;
       a.tmp_out[rec * D + d] = o;
@@ -347,19 +359,27 @@ decode_valu_kernel(const DecodeParams a) {
 
 constexpr int kValuWaves = 4;
 
-template <Dt DT, int D, int S, int G>
-hipError_t launch_g(bool partial, bool nt, const DecodeParams& p, hipStream_t stream) {
+template <Dt DT, int D, int S, int G, int HPW>
+hipError_t launch_h(bool partial, bool nt, const DecodeParams& p, hipStream_t stream) {
+  constexpr int NW = kValuWaves;
   const unsigned units = nt ? (p.num_units + 7) / 8 * 8 : p.num_units;
-  const dim3 grid(units * (unsigned)p.num_kv_heads);
-  const dim3 block(kValuWaves * 64);
+  const dim3 grid(units * (unsigned)(p.num_kv_heads / HPW));
+  const dim3 block(NW * 64);
   if (partial) {
-    if (nt) decode_valu_kernel<DT, D, S, G, kValuWaves, true, true><<<grid, block, 0, stream>>>(p);
-    else decode_valu_kernel<DT, D, S, G, kValuWaves, true, false><<<grid, block, 0, stream>>>(p);
+    if (nt) decode_valu_kernel<DT, D, S, G, NW, HPW, true, true><<<grid, block, 0, stream>>>(p);
+    else decode_valu_kernel<DT, D, S, G, NW, HPW, true, false><<<grid, block, 0, stream>>>(p);
   } else {
-    if (nt) decode_valu_kernel<DT, D, S, G, kValuWaves, false, true><<<grid, block, 0, stream>>>(p);
-    else decode_valu_kernel<DT, D, S, G, kValuWaves, false, false><<<grid, block, 0, stream>>>(p);
+    if (nt) decode_valu_kernel<DT, D, S, G, NW, HPW, false, true><<<grid, block, 0, stream>>>(p);
+    else decode_valu_kernel<DT, D, S, G, NW, HPW, false, false><<<grid, block, 0, stream>>>(p);
   }
   return hipGetLastError();
+}
+
+template <Dt DT, int D, int S, int G>
+hipError_t launch_g(bool partial, bool nt, const DecodeParams& p, hipStream_t stream) {
+  if (p.num_kv_heads % 2 == 0)
+    return launch_h<DT, D, S, G, 2>(partial, nt, p, stream);
+  return launch_h<DT, D, S, G, 1>(partial, nt, p, stream);
 }
 
 template <Dt DT, int D, int S>

@@ -13,7 +13,8 @@
 // 128 rows (token x head of the group, token-major), 32 per wave as two 16-column tiles of
 // v_mfma_f32_16x16x32_{bf16,f16}. Unlike decode, the query side is large, so every 32-position
 // KV chunk is staged in LDS once per workgroup (buffer loads straight into LDS, spread over the
-// waves, a ring of four stages, one barrier per two chunks) and read by all four waves: for
+// waves, a ring of four stages loaded three chunks ahead, one barrier per chunk) and read by
+// all four waves: for
 // each column tile the logits S^T = K Q^T (rows positions, columns query rows; K rows permuted
 // as in decode so that a lane's accumulator holds eight consecutive positions of its own row),
 // the causal mask (only on chunks that reach a row's limit) and online softmax of the lane's
@@ -191,7 +192,18 @@ prefill_kernel(const PrefillParams a) {
     return __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(pool + (size_t)id * id_stride + ro), 0, TILE - ro, kBufferFlags);
   };
-  auto rot = [](int t) { return t + 4 * (t >> 4); };
+  // Placement of a K row's pieces. A wave's 16-byte LDS read is served in four passes of 16
+  // lanes over the 256 bytes of bank space (gfx950: lanes 0-7 with 24-31, 8-15 with 16-23,
+  // and the same in the upper half, as the bank-conflict counter shows for test patterns), so
+  // a conflict-free read needs each pass's 16 pieces in 16 different 16-byte bank slots. With
+  // 256-byte rows (head_dim 128) the slot is the rotated piece index: rows 0-3 and 8-11 (and
+  // 4-7, 12-15) must take the eight even rotations and rows 16-19 and 24-27 the same, which
+  // 2 (t mod 4) + 8 (t / 8 mod 2) does (lane (r, c) adds r, odd for half of each pass).
+  // With 128-byte rows (head_dim 64) two rows share the bank space and t + 4 (t / 16) is
+  // conflict-free as it is.
+  auto rot = [](int t) {
+    return NPC == 16 ? 2 * (t & 3) + 8 * ((t >> 3) & 1) : t + 4 * (t >> 4);
+  };
 
   // This wave's share of chunk n's loads into stage st: LPW consecutive 1 KiB pieces, all of
   // K or all of V^T and all of one block (so one block id and one descriptor per chunk).
@@ -228,6 +240,8 @@ prefill_kernel(const PrefillParams a) {
   };
 
   // Operand reads from a stage (explicit LDS reads; the caller's barrier made the stage whole).
+  // K is read first and waited for here; the V^T reads stay in flight behind the logits and
+  // the softmax until wait_v (LDS reads complete in order).
   const int k_tau = 8 * (c >> 2) + (c & 3);
   auto read_stage = [&](int st, u32x4 (&kr)[2][KK], u32x4 (&vr)[NT]) {
     const char* ks = smem + st * STAGE;
@@ -250,11 +264,15 @@ prefill_kernel(const PrefillParams a) {
     for (int nt = 0; nt < NT; ++nt)
       asm volatile("ds_read_b128 %0, %1 offset:%2"
                    : "=v"(vr[nt]) : "v"(vaddr), "i"(16 * nt * CS * EB) : "memory");
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    static_assert(NT <= 15, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%0)" :: "i"(NT) : "memory");
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(kr[gi][kk]));
+  };
+  auto wait_v = [&](u32x4 (&vr)[NT]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+v"(vr[nt]));
   };
@@ -291,16 +309,6 @@ prefill_kernel(const PrefillParams a) {
     u32x4 vr[NT];
     read_stage(st, kr, vr);
     const int pos0 = n * CT + 8 * r;  // this lane's first position of the chunk
-    // Positions at or past L may hold anything (even NaN): zero their V, 0 * NaN is NaN.
-    const int nv = L - pos0;
-    if (masked && n * CT + CT > L && nv < 8) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t keep = (2 * q + 1 < nv) ? 0xffffffffu : (2 * q < nv) ? 0x0000ffffu : 0u;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) vr[nt][q] &= keep;
-      }
-    }
     // Logits of both column tiles first, then one test for both: the part after it is one
     // straight run (exp, P, the PV products) that the compiler can interleave across the tiles.
     float sv[2][8];
@@ -345,6 +353,17 @@ prefill_kernel(const PrefillParams a) {
         for (int nt = 0; nt < NT; ++nt) acc[j][nt] *= alpha;
       }
     }
+    wait_v(vr);
+    // Positions at or past L may hold anything (even NaN): zero their V, 0 * NaN is NaN.
+    const int nv = L - pos0;
+    if (masked && n * CT + CT > L && nv < 8) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t keep = (2 * q + 1 < nv) ? 0xffffffffu : (2 * q < nv) ? 0x0000ffffu : 0u;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) vr[nt][q] &= keep;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       V8 pb;
@@ -358,20 +377,23 @@ prefill_kernel(const PrefillParams a) {
     }
   };
 
-  // A ring of four stages, chunk n in stage n % 4, consumed two chunks per barrier. Before
-  // the barrier of step n (chunks n and n + 1) this wave waits for its own loads of them;
-  // after it, every wave's loads of them are in and every wave is done with chunks n - 2 and
-  // n - 1, whose stages then take chunks n + 2 and n + 3 (used one step later).
-  static_assert(kStages == 4, "two chunks per step, two steps of stages");
-  for (int k = 0; k < 2 && k < nch; ++k) issue(k, k);
-  for (int n = 0; n < nch; n += 2) {
-    wait_vm_le<0>();
-    stage_barrier();
-    for (int k = n + 2; k < n + 4 && k < nch; ++k) issue(k, k % kStages);
+  // A ring of four stages, chunk n in stage n % 4, loaded three chunks ahead. Before the
+  // barrier of step n this wave waits for its own loads of chunk n; after it, every wave's
+  // loads of chunk n are in and every wave is done with chunk n - 1, whose stage then takes
+  // chunk n + 3.
+  static_assert(kStages == 4, "one chunk per step, three chunks ahead");
+  for (int k = 0; k < 3 && k < nch; ++k) issue(k, k);
 #pragma unroll 1
-    for (int k = n; k < n + 2 && k < nch; ++k)
-      if (wave_live && k * CT <= wave_last_limit)
-        compute(k, k % kStages, k * CT + CT - 1 > wave_first_limit);
+  for (int n = 0; n < nch; ++n) {
+    // This wave's loads of chunk n are done when at most those of the chunks after it that
+    // were issued (up to two) are still in flight.
+    if (n + 2 < nch) wait_vm_le<2 * LPW>();
+    else if (n + 1 < nch) wait_vm_le<LPW>();
+    else wait_vm_le<0>();
+    stage_barrier();
+    if (n + 3 < nch) issue(n + 3, (n + 3) % kStages);
+    if (wave_live && n * CT <= wave_last_limit)
+      compute(n, n % kStages, n * CT + CT - 1 > wave_first_limit);
   }
 
   // Lane (r, c) holds O^T[16 nt + 4 r + e][row c] of each column tile, and the row's whole
