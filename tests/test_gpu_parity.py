@@ -423,3 +423,30 @@ def test_auto_partition_size_matches_oracle():
     torch.cuda.synchronize()
     assert oracle.max_abs_err(out_f64(out), oracle_out(wl)) <= TOL[dt]
     assert pk.auto_partition_size(4096, 8, 16) == 0
+
+
+VALU_HEADS = [(3, 1, "f32"), (6, 1, "bf16"), (3, 2, "bf16"), (5, 2, "f16"), (6, 2, "f32")]
+
+
+@pytest.mark.parametrize("Hkv,G,dtype", VALU_HEADS,
+                         ids=[f"Hkv{h}-G{g}-{d}" for h, g, d in VALU_HEADS])
+@pytest.mark.parametrize("cached", [False, True], ids=["nt", "cached"])
+def test_valu_kernel_heads_per_workgroup(Hkv, G, dtype, cached):
+    """The vector-ALU kernel takes two adjacent kv heads per workgroup when the kv head count
+    is even and one otherwise, in either workgroup numbering (non-temporal loads: every head of
+    a unit on one XCD; cached: a head group per XCD): single pass and partitions, with the
+    fused newest-token write, against the oracle, and the pools bit-identical to its cache
+    write."""
+    wl = W.generate(W.SMALL["c2"].replace(num_kv_heads=Hkv, num_heads=G * Hkv, dtype=dtype))
+    kc, vc = oracle_pools(wl)
+    ref = oracle_out(wl, pools=(kc, vc))
+    for P in (0, 64):
+        dev = upload(wl)
+        out = run_step(dev, wl, kernel="valu", partition_size=P, fused=True, cached_kv=cached,
+                       order=wl.work_items(P))
+        err = oracle.max_abs_err(out_f64(out), ref)
+        print(f"[gpu] valu Hkv={Hkv} G={G} {dtype} P={P} cached={cached}: max abs err {err:.3g}",
+              file=sys.stderr, flush=True)
+        assert err <= TOL[dtype], f"P={P}: {err}"
+        assert np.array_equal(bits(to_host(dev.k, dtype)), bits(kc))
+        assert np.array_equal(bits(to_host(dev.v, dtype)), bits(vc))
