@@ -275,6 +275,23 @@ pkv_status pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                            int32_t num_blocks, pkv_dtype dtype, void* stream);
 
+/* Conversion of a V pool between token rows and the column-group layout this library reads
+ * (see Layouts above): for every block b < num_blocks, kv head h, position t < S, dim d,
+ *   v_cache[b, h, (t / VS) * D + d, t % VS] = v_rows[b, h, t, d]      (from_rows)
+ *   v_rows[b, h, t, d] = v_cache[b, h, (t / VS) * D + d, t % VS]      (to_rows)
+ * Bit copies. For callers whose V pool is laid out like K ([N, Hkv, S, D] token rows, the
+ * blocks of the Qualiteg post's item 1-2): convert once, then decode, prefill and the cache
+ * writes run on the column-group pool; to_rows exports it back.
+ * v_rows, v_cache: device pools of num_blocks blocks, 16-byte aligned. The two may be the same
+ * buffer (converted in place, group by group) or disjoint; any other overlap is rejected.
+ * num_blocks may be 0. */
+pkv_status pkv_v_cache_from_rows(const void* v_rows, void* v_cache, int32_t num_blocks,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 pkv_dtype dtype, void* stream);
+pkv_status pkv_v_cache_to_rows(const void* v_cache, void* v_rows, int32_t num_blocks,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               pkv_dtype dtype, void* stream);
+
 /* Bytes of the split-context workspace: 4 * B * H * NPmax * (D + 2); 0 when
  * partition_size <= 0 (or any size is not positive), SIZE_MAX when the product does not fit in
  * size_t. Carve it as max_logits | exp_sums | tmp_out in that order. */
@@ -447,7 +464,7 @@ pkv_status pkv_probe_tile_gather(const void* base, size_t base_bytes,
 const char* pkv_status_string(pkv_status s);
 int pkv_last_hip_error(void);              /* hipError_t behind the last PKV_ERR_HIP */
 const char* pkv_last_error_message(void);  /* thread-local text of the last failure */
-int pkv_abi_version(void);                 /* 5: whole-group decode over shared prefixes */
+int pkv_abi_version(void);                 /* 6: V pool layout conversion */
 
 #ifdef __cplusplus
 }

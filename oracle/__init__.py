@@ -4,8 +4,9 @@ TEST INFRASTRUCTURE: imported only by tests/, the smoke entry point and the benc
 CPU-baseline leg. The HIP library and its binding never import it.
 """
 from .paged_attention import (copy_blocks, decode, decode_partials, gather, max_abs_err,
-                              num_partitions, prefill, reduce_partials, to_f64, v_group,
-                              write_cache)
+                              num_partitions, prefill, reduce_partials, to_f64, v_from_rows,
+                              v_group, v_to_rows, write_cache)
 
 __all__ = ["copy_blocks", "decode", "decode_partials", "gather", "max_abs_err",
-           "num_partitions", "prefill", "reduce_partials", "to_f64", "v_group", "write_cache"]
+           "num_partitions", "prefill", "reduce_partials", "to_f64", "v_from_rows", "v_group",
+           "v_to_rows", "write_cache"]

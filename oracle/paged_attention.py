@@ -56,7 +56,7 @@ import math
 import numpy as np
 
 __all__ = ["V_GROUP", "v_group", "to_f64", "write_cache", "copy_blocks", "gather", "decode", "decode_partials",
-           "reduce_partials", "num_partitions", "prefill"]
+           "reduce_partials", "num_partitions", "prefill", "v_from_rows", "v_to_rows"]
 
 
 V_GROUP = 32  # most block positions in one column group of the V layout
@@ -75,6 +75,30 @@ def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype in ("f32", "f16", "f64"):
         return np.asarray(a).astype(np.float64)
     raise ValueError(dtype)
+
+
+def v_from_rows(v_rows, block_size):
+    """The column-group V pool holding the same elements as a pool of token rows
+    [N, Hkv, S, D] (the layout statement above, position by position)."""
+    N, Hkv, S, D = v_rows.shape
+    assert S == block_size
+    VS = v_group(S)
+    v = np.zeros((N, Hkv, S // VS * D, VS), dtype=v_rows.dtype)
+    for t in range(S):
+        v[:, :, (t // VS) * D:(t // VS + 1) * D, t % VS] = v_rows[:, :, t, :]
+    return v
+
+
+def v_to_rows(v_cache, block_size):
+    """Token rows [N, Hkv, S, D] of a column-group V pool (the inverse of v_from_rows)."""
+    N, Hkv, R, VS = v_cache.shape
+    S = block_size
+    assert VS == v_group(S) and R % (S // VS) == 0
+    D = R // (S // VS)
+    rows = np.zeros((N, Hkv, S, D), dtype=v_cache.dtype)
+    for t in range(S):
+        rows[:, :, t, :] = v_cache[:, :, (t // VS) * D:(t // VS + 1) * D, t % VS]
+    return rows
 
 
 def write_cache(k_cache, v_cache, key, value, slot_mapping, block_size):

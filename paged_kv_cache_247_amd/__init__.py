@@ -11,7 +11,7 @@ from ._lib import (KERNELS, BlockManager, DeviceRegion, OutOfBlocks, PagedKVErro
                    paged_attention_shared,
                    paged_attention_prefill, paged_attention_reduce, partition_workspace,
                    prefill_tile_tokens, probe_stream_read, probe_tile_gather,
-                   reshape_and_cache, v_block_shape)
+                   reshape_and_cache, v_block_shape, v_cache_from_rows, v_cache_to_rows)
 
 __all__ = ["KERNELS", "BlockManager", "DeviceRegion", "OutOfBlocks", "PagedKVError", "VmmPool",
            "auto_partition_size", "copy_blocks", "load", "swap_blocks",
@@ -21,4 +21,4 @@ __all__ = ["KERNELS", "BlockManager", "DeviceRegion", "OutOfBlocks", "PagedKVErr
            "paged_attention_shared",
            "paged_attention_prefill", "paged_attention_reduce", "partition_workspace",
            "prefill_tile_tokens", "probe_stream_read", "probe_tile_gather",
-           "reshape_and_cache", "v_block_shape"]
+           "reshape_and_cache", "v_block_shape", "v_cache_from_rows", "v_cache_to_rows"]

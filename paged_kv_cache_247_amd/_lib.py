@@ -48,6 +48,8 @@ SIGNATURES = {
                                                 _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "pkv_paged_attention_reduce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pkv_copy_blocks": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "pkv_v_cache_from_rows": (_I, [_P, _P, _I, _I, _I, _I, _I, _P]),
+    "pkv_v_cache_to_rows": (_I, [_P, _P, _I, _I, _I, _I, _I, _P]),
     "pkv_partition_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "pkv_status_string": (ctypes.c_char_p, [_I]),
     "pkv_last_hip_error": (ctypes.c_int, []),
@@ -140,7 +142,7 @@ class OutOfBlocks(PagedKVError):
 
 PKV_ERR_HIP = 3
 PKV_ERR_NO_BLOCKS = 4
-ABI_VERSION = 5  # the argument lists in SIGNATURES
+ABI_VERSION = 6  # the argument lists in SIGNATURES
 STATIC_WORKSPACE_BYTES = 80 << 20  # PKV_STATIC_WORKSPACE_BYTES
 
 
@@ -550,6 +552,28 @@ def copy_blocks(k_caches, v_caches, block_mapping):
     varr = (ctypes.c_void_p * nl)(*[v.data_ptr() for v in v_caches])
     _check(load().pkv_copy_blocks(karr, varr, nl, _ptr(block_mapping), block_mapping.shape[0],
                                   Hkv, D, S, N, _dt(k0), _stream(k0)))
+
+
+def _v_layout(name, src, dst, rows_src):
+    rows, cols = (src, dst) if rows_src else (dst, src)
+    _need(rows, "v_rows", ndim=4)
+    N, Hkv, S, D = rows.shape
+    _need(cols, "v_cache", rows.dtype, 4, rows.device)
+    if tuple(cols.shape) != (N, *v_block_shape(Hkv, D, S)):
+        raise ValueError(f"v_cache must be {(N, *v_block_shape(Hkv, D, S))} for v_rows "
+                         f"{tuple(rows.shape)}, got {tuple(cols.shape)}")
+    _check(getattr(load(), name)(_ptr(src), _ptr(dst), N, Hkv, D, S, _dt(rows), _stream(rows)))
+
+
+def v_cache_from_rows(v_rows, v_cache):
+    """pkv_v_cache_from_rows: fill the column-group V pool [N, Hkv, (S/VS) D, VS] from a pool of
+    token rows [N, Hkv, S, D]. v_cache may view the same memory as v_rows (in place)."""
+    _v_layout("pkv_v_cache_from_rows", v_rows, v_cache, True)
+
+
+def v_cache_to_rows(v_cache, v_rows):
+    """pkv_v_cache_to_rows: the inverse of v_cache_from_rows (in place allowed as well)."""
+    _v_layout("pkv_v_cache_to_rows", v_cache, v_rows, False)
 
 
 AUTO_PARTITION_TOKENS = 2048

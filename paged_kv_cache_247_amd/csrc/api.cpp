@@ -210,6 +210,30 @@ pkv_status decode_impl(const pkv_decode_options* opt, void* out, const void* q, 
   return hip_status(e, fn);
 }
 
+pkv_status v_layout(const char* fn, bool to_columns, const void* src, void* dst,
+                    int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int dtype, void* stream) {
+  pkv_status st = check_tile(fn, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PKV_OK) return st;
+  if (num_blocks < 0) return fail(PKV_ERR_INVALID_ARGUMENT, "%s: num_blocks %d", fn, num_blocks);
+  if (num_blocks == 0) return PKV_OK;
+  if (!aligned(src, 16) || !aligned(dst, 16))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: a pointer is null or misaligned", fn);
+  static const int eb[3] = {4, 2, 2};
+  const int64_t bytes = (int64_t)num_blocks * num_kv_heads * block_size * head_dim * eb[dtype];
+  const uintptr_t s = (uintptr_t)src, d = (uintptr_t)dst;
+  if (s != d && s < d + bytes && d < s + bytes)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "%s: source and destination overlap but differ", fn);
+  pkv::VLayoutParams p;
+  p.src = src;
+  p.dst = dst;
+  p.group = block_size < 32 ? block_size : 32;
+  p.num_groups = (int64_t)num_blocks * num_kv_heads * (block_size / p.group);
+  p.head_dim = head_dim;
+  return hip_status(pkv::launch_v_layout(to_dt(dtype), to_columns, p,
+                                         reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -488,6 +512,20 @@ pkv_status pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t
   return PKV_OK;
 }
 
+pkv_status pkv_v_cache_from_rows(const void* v_rows, void* v_cache, int32_t num_blocks,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 pkv_dtype dtype, void* stream) {
+  return v_layout("pkv_v_cache_from_rows", true, v_rows, v_cache, num_blocks, num_kv_heads,
+                  head_dim, block_size, pkv::enum_arg(dtype), stream);
+}
+
+pkv_status pkv_v_cache_to_rows(const void* v_cache, void* v_rows, int32_t num_blocks,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               pkv_dtype dtype, void* stream) {
+  return v_layout("pkv_v_cache_to_rows", false, v_cache, v_rows, num_blocks, num_kv_heads,
+                  head_dim, block_size, pkv::enum_arg(dtype), stream);
+}
+
 size_t pkv_partition_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                      int32_t max_context_len, int32_t partition_size) {
   if (partition_size <= 0 || num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 ||
@@ -514,6 +552,6 @@ int pkv_last_hip_error(void) { return t_last_hip; }
 
 const char* pkv_last_error_message(void) { return t_msg; }
 
-int pkv_abi_version(void) { return 5; }
+int pkv_abi_version(void) { return 6; }
 
 }  // extern "C"

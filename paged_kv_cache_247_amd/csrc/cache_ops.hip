@@ -100,6 +100,66 @@ __global__ void __launch_bounds__(kCopyThreads) copy_blocks_kernel(const CopyPar
   if (e < a.tile_bytes / 16) d[e] = s[e];
 }
 
+// Conversion of a V pool between token rows [N, Hkv, S, D] and column groups. In both layouts
+// column group c of a (block, kv head) tile holds positions c*VS .. c*VS + VS - 1 in the same
+// VS*D elements, as [VS][D] rows or as a [D][VS] tile; so each workgroup transposes whole
+// groups through LDS, reading and writing 16-byte vectors in HBM order. The LDS rows of
+// positions are padded by one dword, so that the strided reads and writes along a head-dim
+// index spread over the banks.
+constexpr int kLayoutThreads = 256;
+constexpr int kLayoutGrid = 4096;  // workgroups; each loops over groups
+constexpr int kLayoutRowDwords = 128 + 1;  // f32 rows of D = 128, padded
+
+template <typename U, bool TO_COLUMNS>
+__global__ void __launch_bounds__(kLayoutThreads) v_layout_kernel(const VLayoutParams a) {
+  constexpr int VEC = 16 / (int)sizeof(U);  // elements per 16-byte vector
+  constexpr int UW = 4 / (int)sizeof(U);    // elements per dword
+  __shared__ uint32_t lds[32 * kLayoutRowDwords];
+  U* const lu = reinterpret_cast<U*>(lds);
+  const int D = a.head_dim;
+  const int VS = a.group;
+  const int RW = D / UW;                // dwords of one position row
+  const int LW = RW + 1;                // dwords of its padded LDS row
+  const int nvec = VS * D / VEC;        // 16-byte vectors of a group
+  for (int64_t grp = blockIdx.x; grp < a.num_groups; grp += gridDim.x) {
+    const size_t off = (size_t)grp * VS * D * sizeof(U);
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.src) + off);
+    u32x4* dst = reinterpret_cast<u32x4*>(static_cast<char*>(a.dst) + off);
+    if constexpr (TO_COLUMNS) {
+      for (int v = threadIdx.x; v < nvec; v += kLayoutThreads) {
+        const u32x4 x = src[v];
+        const int t = (4 * v) / RW;  // RW is a multiple of 4: a vector stays in its row
+        uint32_t* r = lds + t * LW + (4 * v) % RW;
+        r[0] = x[0]; r[1] = x[1]; r[2] = x[2]; r[3] = x[3];
+      }
+      __syncthreads();
+      for (int v = threadIdx.x; v < nvec; v += kLayoutThreads) {
+        const int d = (v * VEC) / VS;  // VS is a multiple of VEC: a vector stays in its row
+        const int t0 = (v * VEC) % VS;
+        __attribute__((aligned(16))) U col[VEC];
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) col[j] = lu[(t0 + j) * LW * UW + d];
+        dst[v] = *reinterpret_cast<const u32x4*>(col);
+      }
+    } else {
+      for (int v = threadIdx.x; v < nvec; v += kLayoutThreads) {
+        const int d = (v * VEC) / VS;
+        const int t0 = (v * VEC) % VS;
+        __attribute__((aligned(16))) U col[VEC];
+        *reinterpret_cast<u32x4*>(col) = src[v];
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) lu[(t0 + j) * LW * UW + d] = col[j];
+      }
+      __syncthreads();
+      for (int v = threadIdx.x; v < nvec; v += kLayoutThreads) {
+        const uint32_t* r = lds + ((4 * v) / RW) * LW + (4 * v) % RW;
+        dst[v] = u32x4{r[0], r[1], r[2], r[3]};
+      }
+    }
+    __syncthreads();  // the next group reuses the LDS rows
+  }
+}
+
 template <Dt DT, int D>
 hipError_t write_d(int block_size, const CacheWriteParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)p.num_tokens);
@@ -142,6 +202,19 @@ hipError_t launch_copy_blocks(int num_layers, const CopyParams& p, hipStream_t s
   if ((int64_t)p.num_pairs * q.pieces > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(p.num_pairs * q.pieces), (unsigned)num_layers, 2);
   copy_blocks_kernel<<<grid, kCopyThreads, 0, stream>>>(q);
+  return hipGetLastError();
+}
+
+hipError_t launch_v_layout(Dt dt, bool to_columns, const VLayoutParams& p, hipStream_t stream) {
+  if (p.head_dim > 128 || p.group > 32 || p.num_groups <= 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(p.num_groups < kLayoutGrid ? p.num_groups : kLayoutGrid));
+  if (dt == Dt::F32) {
+    if (to_columns) v_layout_kernel<uint32_t, true><<<grid, kLayoutThreads, 0, stream>>>(p);
+    else v_layout_kernel<uint32_t, false><<<grid, kLayoutThreads, 0, stream>>>(p);
+  } else {
+    if (to_columns) v_layout_kernel<uint16_t, true><<<grid, kLayoutThreads, 0, stream>>>(p);
+    else v_layout_kernel<uint16_t, false><<<grid, kLayoutThreads, 0, stream>>>(p);
+  }
   return hipGetLastError();
 }
 

@@ -73,6 +73,15 @@ struct CacheWriteParams {
   int32_t num_blocks;
 };
 
+// Conversion of a V pool between token rows [N, Hkv, S, D] and the column-group layout.
+struct VLayoutParams {
+  const void* src;
+  void* dst;
+  int64_t num_groups;  // N * Hkv * S / VS column groups
+  int32_t head_dim;
+  int32_t group;       // VS = min(S, 32) positions per column group
+};
+
 // Each returns hipSuccess or the launch error; hipErrorNotSupported if no instantiation
 // matches (the C ABI validates shapes before calling, so that is a library bug).
 // nt: non-temporal K/V loads (else cached loads, for shared prefixes).
@@ -147,5 +156,6 @@ hipError_t launch_reduce(Dt dt, int head_dim, const ReduceParams& p, hipStream_t
 hipError_t launch_reshape_and_cache(Dt dt, int head_dim, int block_size,
                                     const CacheWriteParams& p, hipStream_t stream);
 hipError_t launch_copy_blocks(int num_layers, const CopyParams& p, hipStream_t stream);
+hipError_t launch_v_layout(Dt dt, bool to_columns, const VLayoutParams& p, hipStream_t stream);
 
 }  // namespace pkv

@@ -147,6 +147,17 @@ hipError_t launch_copy_blocks(int num_layers, const CopyParams& p, hipStream_t) 
   return hipSuccess;
 }
 
+hipError_t launch_v_layout(Dt dt, bool, const VLayoutParams& p, hipStream_t) {
+  ++g_launches;
+  CHECK(valid_dt(dt) && (p.head_dim == 64 || p.head_dim == 128), "v layout: dtype/head_dim");
+  CHECK(p.group == 16 || p.group == 32, "v layout: group %d", p.group);
+  CHECK(p.num_groups > 0 && p.src && p.dst, "v layout: sizes");
+  const int64_t bytes = p.num_groups * p.group * p.head_dim * (dt == Dt::F32 ? 4 : 2);
+  const uintptr_t s = (uintptr_t)p.src, d = (uintptr_t)p.dst;
+  CHECK(s == d || s + bytes <= d || d + bytes <= s, "v layout: overlapping pools");
+  return hipSuccess;
+}
+
 hipError_t launch_prefill(Dt dt, int head_dim, int block_size, const PrefillParams& p,
                           hipStream_t) {
   ++g_launches;
@@ -215,7 +226,7 @@ int main() {
   int ok = 0, refused = 0;
   for (int it = 0; it < 60000; ++it) {
     const int before = g_launches;
-    const int which = rng() % 7;
+    const int which = rng() % 8;
     pkv_status st;
     const char* fn = "";
     const int32_t B = pick_int({1, 2, 4, 9, 128}), H = pick_int({4, 8, 32, 64}),
@@ -278,6 +289,15 @@ int main() {
       after(fn, st, before, layers / 32 + 1);
       (st == PKV_OK ? ok : refused)++;
       continue;
+    } else if (which == 6) {
+      fn = "v_layout";
+      void* src = pick_ptr();
+      const int r = (int)(rng() % 4);  // the same pool, a near one (overlapping) or a far one
+      void* dst = r == 0 ? src : (void*)((uintptr_t)src + (r == 1 ? 4096 : ((uintptr_t)1 << 40)));
+      if (rng() % 2)
+        st = pkv_v_cache_from_rows(src, dst, pick_int({-1, 0, 1, 32768}), Hkv, D, S, dt, nullptr);
+      else
+        st = pkv_v_cache_to_rows(src, dst, pick_int({-1, 0, 1, 32768}), Hkv, D, S, dt, nullptr);
     } else {
       fn = "prefill";
       st = pkv_paged_attention_prefill(pick_ptr(), pick_ptr(), pick_ptr(), pick_ptr(),

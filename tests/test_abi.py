@@ -32,11 +32,11 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
-    assert len(names) == 41, names
+    assert len(names) == 43, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES), "binding prototypes out of step with the header"
-    assert lib.pkv_abi_version() == 5
+    assert lib.pkv_abi_version() == 6
 
 
 def test_status_strings(lib):
@@ -123,6 +123,22 @@ def test_reshape_and_cache_validation(lib):
     assert f(A16, A16, A16, A16, A16 + 4, 4, 2, 128, 16, 8, 2, None) == INVALID
     assert f(A16, A16, A16, A16, A16, 4, 2, 128, 16, 0, 2, None) == INVALID
 
+
+
+@pytest.mark.parametrize("name", ["pkv_v_cache_from_rows", "pkv_v_cache_to_rows"])
+def test_v_layout_validation(lib, name):
+    f = getattr(lib, name)
+    tile = 2 * 16 * 128 * 2  # bytes of one bf16 block of 2 kv heads, S 16, D 128
+    assert f(A16, A16 + 4 * tile, 0, 2, 128, 16, 2, None) == OK  # nothing to convert
+    assert f(A16, A16 + 4 * tile, -1, 2, 128, 16, 2, None) == INVALID
+    assert f(A16, A16 + 4 * tile, 4, 2, 96, 16, 2, None) == UNSUPPORTED
+    assert f(A16, A16 + 4 * tile, 4, 2, 128, 24, 2, None) == UNSUPPORTED
+    assert f(A16, A16 + 4 * tile, 4, 0, 128, 16, 2, None) == INVALID
+    assert f(A16, A16 + 4 * tile, 4, 2, 128, 16, 7, None) == INVALID
+    assert f(None, A16, 4, 2, 128, 16, 2, None) == INVALID
+    assert f(A16, A16 + 8, 4, 2, 128, 16, 2, None) == INVALID  # misaligned
+    assert f(A16, A16 + 3 * tile, 4, 2, 128, 16, 2, None) == INVALID  # partial overlap
+    assert f(A16 + 3 * tile, A16, 4, 2, 128, 16, 2, None) == INVALID
 
 def test_reduce_and_copy_validation(lib):
     r = lib.pkv_paged_attention_reduce

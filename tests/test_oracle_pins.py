@@ -345,6 +345,69 @@ def test_gather_follows_layout_statement():
     assert np.array_equal(K, expect) and np.array_equal(V, expect)
 
 
+
+def check_v_layout(S, N=3, Hkv=2, D=5, seed=0):
+    """The V conversion against gather (pinned above): a V pool converted from the very rows
+    that form the K pool gathers to the same rows as K, for every position; writing every
+    position with write_cache gives the same pool; the two conversions undo each other."""
+    rows = np.random.default_rng(seed).standard_normal((N, Hkv, S, D))
+    vc = oracle.v_from_rows(rows, S)
+    ok = vc.shape == (N, Hkv, S // oracle.v_group(S) * D, oracle.v_group(S))
+    table = np.array([2, 0, 1], dtype=np.int32)[:N]
+    for g in range(Hkv):
+        K, V = oracle.gather(rows, vc, table, N * S, g, S, "f64")
+        ok = ok and np.array_equal(K, V)
+    slots = np.arange(N * S)
+    key = rows.transpose(0, 2, 1, 3).reshape(N * S, Hkv, D)
+    _, vw = oracle.write_cache(np.zeros_like(rows), np.zeros_like(vc), key, key, slots, S)
+    ok = ok and np.array_equal(vw, vc)
+    ok = ok and np.array_equal(oracle.v_to_rows(vc, S), rows)
+    back = np.random.default_rng(seed + 1).standard_normal(vc.shape)
+    return bool(ok and np.array_equal(oracle.v_from_rows(oracle.v_to_rows(back, S), S), back))
+
+
+@pytest.mark.parametrize("S", [4, 16, 32, 64, 128])
+def test_v_layout_conversion(S):
+    assert check_v_layout(S)
+
+
+def test_v_layout_two_groups_by_hand():
+    """S = 64, D = 1, position t holding t: the two column groups are the rows 0..31 and
+    32..63 (the layout statement of the C header, VS = 32)."""
+    rows = np.arange(64, dtype=np.float64).reshape(1, 1, 64, 1)
+    expect = np.arange(64, dtype=np.float64).reshape(1, 1, 2, 32)
+    assert np.array_equal(oracle.v_from_rows(rows, 64), expect)
+    assert np.array_equal(oracle.v_to_rows(expect, 64), rows)
+
+
+def _bad_v_groups_swapped(v_rows, block_size):
+    v = _orig_v_from_rows(v_rows, block_size)
+    N, Hkv, R, VS = v.shape
+    G = block_size // VS
+    return v.reshape(N, Hkv, G, R // G, VS)[:, :, ::-1].reshape(v.shape)
+
+
+def _bad_v_transposed_group(v_rows, block_size):
+    N, Hkv, S, D = v_rows.shape
+    VS = oracle.v_group(S)
+    v = np.zeros((N, Hkv, S // VS * D, VS), dtype=v_rows.dtype)
+    for t in range(S):
+        flat = (t // VS) * D * VS + (t % VS) * D  # position-major inside the group
+        for d in range(D):
+            e = flat + d
+            v[:, :, e // VS, e % VS] = v_rows[:, :, t, d]
+    return v
+
+
+_orig_v_from_rows = pa.v_from_rows
+
+
+@pytest.mark.parametrize("mutant", [_bad_v_groups_swapped, _bad_v_transposed_group])
+def test_planted_v_layout_mistake_fails_a_pin(monkeypatch, mutant):
+    monkeypatch.setattr(pa, "v_from_rows", mutant)
+    monkeypatch.setattr(oracle, "v_from_rows", mutant)
+    assert not all(check_v_layout(S) for S in (16, 64, 128))
+
 def test_copy_blocks_oracle():
     rng = np.random.default_rng(0)
     ks = [rng.standard_normal((6, 2, 4, 3)) for _ in range(2)]
