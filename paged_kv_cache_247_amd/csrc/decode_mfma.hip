@@ -158,16 +158,97 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
   int unit = a.work_items ? a.work_items[slot] : slot;
   unit = min(max(unit, 0), (GRP ? a.num_units : a.num_seqs * a.num_ranges) - 1);
   const int part = GRP ? 0 : unit % a.num_ranges;
-  // GRP: the first member's table row and length stand for the group's (they agree over the
-  // range by the caller's contract).
-  const int i = GRP ? min(max(a.group_members[4 * unit], 0), a.num_seqs - 1)
-                    : unit / a.num_ranges;
+  // GRP: the group's row of four members in one 16-byte load (rows are 16-byte aligned), so
+  // that the loads which depend on it all issue together instead of one after another. The
+  // first member's table row and length stand for the group's (they agree over the range by the
+  // caller's contract).
+  u32x4 grow = {0u, 0u, 0u, 0u};
+  if constexpr (GRP) grow = *reinterpret_cast<const u32x4*>(a.group_members + 4 * unit);
+  const int i = GRP ? min(max((int)grow[0], 0), a.num_seqs - 1) : unit / a.num_ranges;
+  auto wm_of = [&](int k) {  // GRP: member k of the group, -1 for none
+    const int m = pick4(k, (int)grow[0], (int)grow[1], (int)grow[2], (int)grow[3]);
+    return k * G < 16 && m >= 0 && m < a.num_seqs ? m : -1;
+  };
   // Columns in use: the G heads, or G heads of each of up to 16 / G group members.
   const int ncol = GRP ? 16 : G;
   const int lane = lane_id();
   const int wave = wave_id();
   const int r = lane >> 4;
   const int c = lane & 15;
+  // q columns: lane (r, c) holds head c at d = 32 kk + 8r .. +8; in GRP mode head c % G of
+  // member c / G. Columns past the group's heads (or of a missing member) load some valid q row
+  // instead of zeros: the columns are independent and their results are never written, and
+  // unconditional loads let the compiler count them in its waits instead of waiting for all.
+  // These loads and the new rows below depend only on the unit, so they go out before the
+  // lengths and block ids the first chunk waits for.
+  auto column_seq = [&](int col) {
+    if constexpr (GRP) {
+      const int s = col / G;
+      const int m = s < 4 ? (int)pick4(s, grow[0], grow[1], grow[2], grow[3]) : -1;
+      return m < a.num_seqs ? m : -1;
+    } else {
+      return col < G ? i : -1;
+    }
+  };
+  V8 qb[KK];
+  {
+    const int qs = column_seq(c);
+    const char* qp = reinterpret_cast<const char*>(a.q) +
+                     (((size_t)(GRP ? max(qs, 0) : i) * H + (size_t)g * G + c % G) * D + 8 * r) *
+                         EB;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qb[kk] = __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(qp + kk * 64));
+  }
+
+  // Position L-1 joins the merge below as one more partial state (m = its logit, l = 1,
+  // acc = its V row). Its rows are loaded before the first chunk (vector loads return in
+  // order, so waiting for them below does not wait for the chunk).
+  // WG: every member's newest position; the K row pieces of member k go to lanes
+  // k * PPR .. k * PPR + PPR - 1, and lane (r, c)'s logit pieces are those of its column's
+  // member.
+  constexpr int NMEM = WG ? 4 : 1;   // newest rows per unit
+  constexpr int PPR = D * EB / 16;   // sixteen-byte pieces per K row
+  auto new_row = [&](int seq) {      // this kv head's newest K row of sequence seq, in bytes
+    return reinterpret_cast<const char*>(a.new_key) + ((size_t)seq * Hkv + g) * D * EB;
+  };
+  const char* kn = new_row(i);
+  const T* vn = reinterpret_cast<const T*>(a.new_value) + ((size_t)i * Hkv + g) * D;
+  // Set only in the waves that use them (no default value: a merge of a loaded value with a
+  // default makes the compiler copy, and so wait for, the load right where it is issued).
+  u32x4 kpiece[KK];
+  u32x4 krow;
+  T vrow[NMEM][D / 64];
+  // Block of the newest position: one per lane (lane k: member k's), so that the load stays a
+  // vector load that nothing waits for until the stores at the end (a uniform one would be
+  // moved to a scalar register, with a wait, as soon as it is issued).
+  int slot_blk;
+  // The rows depend on the unit only (in split mode on the range too: there they are loaded
+  // once the length is known). Every load is unconditional: lanes past a row's pieces and
+  // missing members read rows that exist (the stores skip them; use_new_rows zeroes a missing
+  // member's V).
+  auto load_new_rows = [&]() {
+    if (wave == NW - 1) {
+      const char* kp = WG ? new_row(max(column_seq(c), 0)) : kn;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        kpiece[kk] = *reinterpret_cast<const u32x4*>(kp + (32 * kk + 8 * r) * EB);
+    }
+    if (wave == 0) {
+#pragma unroll
+      for (int k = 0; k < NMEM; ++k) {
+        const T* vk = WG ? reinterpret_cast<const T*>(a.new_value) +
+                               ((size_t)max(wm_of(k), 0) * Hkv + g) * D
+                         : vn;
+#pragma unroll
+        for (int e = 0; e < D / 64; ++e) vrow[k][e] = vk[lane + 64 * e];
+      }
+      const int km = min(lane / PPR, NMEM - 1);
+      krow = reinterpret_cast<const u32x4*>(WG ? new_row(max(wm_of(km), 0)) : kn)[lane % PPR];
+    }
+  };
+  if ((WG || !PARTIAL) && a.new_key != nullptr) load_new_rows();
+
   // Physical block of logical block j: the sequence's table entry (TBL), or without tables the
   // contiguous reservation of MB blocks per sequence (block i * MB + j).
   const int32_t* bt = a.block_tables + (size_t)i * MB;
@@ -201,13 +282,15 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
   Four wm = {-1, -1, -1, -1}, wL = {0, 0, 0, 0}, wE = {0, 0, 0, 0}, wcum = {0, 0, 0, 0};
   int wP = 0, wNS = 0, wNM = 0;
   if constexpr (WG) {
-    auto member = [&](int k) {
-      const int m = k * G < 16 ? a.group_members[4 * unit + k] : -1;
-      return m >= 0 && m < a.num_seqs ? m : -1;
-    };
-    wm = {member(0), member(1), member(2), member(3)};
-    auto len = [&](int m) { return m >= 0 ? min(max(a.context_lens[m], 0), MB * S) : 0; };
-    wL = {len(wm.v0), len(wm.v1), len(wm.v2), len(wm.v3)};
+    wm = {wm_of(0), wm_of(1), wm_of(2), wm_of(3)};
+    // The four lengths load unconditionally (a missing member reads sequence 0's) and are
+    // masked after, so they too are one round trip (the empty asm keeps the compiler from
+    // moving each load back under its member's condition, one wait after another).
+    int x0 = a.context_lens[max(wm.v0, 0)], x1 = a.context_lens[max(wm.v1, 0)];
+    int x2 = a.context_lens[max(wm.v2, 0)], x3 = a.context_lens[max(wm.v3, 0)];
+    asm volatile("" : "+s"(x0), "+s"(x1), "+s"(x2), "+s"(x3));
+    auto len = [&](int m, int x) { return m >= 0 ? min(max(x, 0), MB * S) : 0; };
+    wL = {len(wm.v0, x0), len(wm.v1, x1), len(wm.v2, x2), len(wm.v3, x3)};
     wP = min(max(a.range_tokens, 0), MB * S);
     wNS = wm.v0 >= 0 ? (wP + CT - 1) / CT : 0;
     const int nf = a.new_key != nullptr ? 1 : 0;
@@ -266,6 +349,10 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
       return blk < MB ? bt[blk] : 0;
     }
   };
+  if (WG && a.new_key != nullptr && wave == 0) {
+    const int ks = min(lane, NMEM - 1);
+    slot_blk = a.block_tables[(size_t)max(wm[ks], 0) * MB + (max(wL[ks], 1) - 1) / S];
+  }
   int id_batch = 0;
   if constexpr (TBL) id_batch = load_id_batch(0);
 
@@ -284,31 +371,6 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
   const int end = min(start + a.range_tokens, L) - (fused ? 1 : 0);
   const int nch = WG ? wNS + wNM : max(end - start + CT - 1, 0) / CT;
   const int blk_end = (end + S - 1) / S;  // first logical block past the cached range
-
-  // q columns: lane (r, c) holds head c (zero beyond the group) at d = 32 kk + 8r .. +8; in
-  // GRP mode head c % G of member c / G (zero where the group has no such member).
-  auto column_seq = [&](int col) {
-    if constexpr (GRP) {
-      const int s = col / G;
-      const int m = s < 4 ? a.group_members[4 * unit + s] : -1;
-      return m < a.num_seqs ? m : -1;
-    } else {
-      return col < G ? i : -1;
-    }
-  };
-  V8 qb[KK];
-  {
-    const int qs = column_seq(c);
-    const char* qp = reinterpret_cast<const char*>(a.q) +
-                     (((size_t)max(qs, 0) * H + (size_t)g * G + (GRP ? c % G : c)) * D +
-                      8 * r) * EB;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (qs >= 0) v = *reinterpret_cast<const u32x4*>(qp + kk * 64);
-      qb[kk] = __builtin_bit_cast(V8, v);
-    }
-  }
 
   const size_t tile_bytes = (size_t)S * D * EB;
   const size_t id_stride = (size_t)Hkv * tile_bytes;
@@ -406,8 +468,9 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
         const_cast<char*>(kpool + (size_t)id * id_stride + (size_t)ro * RB), 0,
         (int)tile_bytes - ro * RB, kBufferFlags);
   };
-  auto load_as = [&](const Ids& ids, Regs& R, int slot, auto nt) {
-    constexpr bool NTC = decltype(nt)::value;
+  auto load_as = [&](const Ids& ids, Regs& R, int slot, auto nt, auto knt) {
+    constexpr bool NTC = decltype(nt)::value;   // every load non-temporal
+    constexpr bool KNT = decltype(knt)::value;  // the K loads non-temporal
     char* dst = smem + (wave * 2 + slot) * SLOT;
     const __amdgpu_buffer_rsrc_t r0 = tile_rsrc(ids.b0, ids.ro);
     const __amdgpu_buffer_rsrc_t r1 = BPC == 2 ? tile_rsrc(ids.b1, 0) : r0;
@@ -416,17 +479,9 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
       const int t = x * (1024 / RB) + lane / NPC;
       const int jt = (lane % NPC - rot(t)) & (NPC - 1);
       const bool second = BPC == 2 && x * (1024 / RB) >= S;
-      // WG: a member's own K streams from HBM with the non-temporal policy, so that it does
-      // not push the shared tiles out of L2 (its V loads stay ordinary: a choice of load
-      // instruction per chunk would cost the register waits their precision).
-      if (WG && ids.k >= 0)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            second ? r1 : r0, (__attribute__((address_space(3))) void*)(dst + x * 1024), 16,
-            (t % S) * RB + jt * 16, 0, 0, 2);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            second ? r1 : r0, (__attribute__((address_space(3))) void*)(dst + x * 1024), 16,
-            (t % S) * RB + jt * 16, 0, 0, NTC ? 2 : 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          second ? r1 : r0, (__attribute__((address_space(3))) void*)(dst + x * 1024), 16,
+          (t % S) * RB + jt * 16, 0, 0, (NTC || KNT) ? 2 : 0);
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -435,13 +490,13 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
       R.v[nt] = load_kv<NTC, u32x4>(off < 4096 ? ids.vt + off : ids.vt4 + (off - 4096));
     }
   };
-  auto load = [&](const Ids& ids, Regs& R, int slot) {
+  auto load = [&](const Ids& ids, Regs& R, int slot, auto knt) {
     if constexpr (WG) {
       R.cs = ids.cs;
       R.ce = ids.ce;
       R.k = ids.k;
     }
-    load_as(ids, R, slot, std::integral_constant<bool, NTL>());
+    load_as(ids, R, slot, std::integral_constant<bool, NTL>(), knt);
   };
   // Operand pieces of chunk K from the wave's slot. The reads are issued as inline LDS
   // instructions that the compiler does not see as LDS reads, so it adds no waits of its own
@@ -535,60 +590,22 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
   // WG: every member's newest position; the K row pieces of member k go to lanes
   // k * PPR .. k * PPR + PPR - 1, and lane (r, c)'s logit pieces are those of its column's
   // member.
-  constexpr int NMEM = WG ? 4 : 1;   // newest rows per unit
-  constexpr int PPR = D * EB / 16;   // sixteen-byte pieces per K row
-  auto new_row = [&](int seq) {      // this kv head's newest K row of sequence seq, in bytes
-    return reinterpret_cast<const char*>(a.new_key) + ((size_t)seq * Hkv + g) * D * EB;
-  };
-  const char* kn = new_row(i);
-  const T* vn = reinterpret_cast<const T*>(a.new_value) + ((size_t)i * Hkv + g) * D;
-  u32x4 kpiece[KK];
-  u32x4 krow = {0u, 0u, 0u, 0u};
-  T vrow[NMEM][D / 64];
-  int slot_blk[NMEM];
-#pragma unroll
-  for (int k = 0; k < NMEM; ++k) slot_blk[k] = 0;
-  if (fused) {
-    if (wave == NW - 1) {
-      if constexpr (WG) {
-        const int qs = column_seq(c);
-        const char* kp = new_row(max(qs, 0));
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          kpiece[kk] = qs >= 0 ? *reinterpret_cast<const u32x4*>(kp + (32 * kk + 8 * r) * EB)
-                               : u32x4{0u, 0u, 0u, 0u};
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          kpiece[kk] = *reinterpret_cast<const u32x4*>(kn + (32 * kk + 8 * r) * EB);
-      }
-    }
-    if (wave == 0) {
-      if constexpr (WG) {
-#pragma unroll
-        for (int k = 0; k < NMEM; ++k) {
-          const bool has = wm[k] >= 0 && wL[k] > 0;
-          slot_blk[k] = has ? a.block_tables[(size_t)wm[k] * MB + (wL[k] - 1) / S] : 0;
-          const T* vk = reinterpret_cast<const T*>(a.new_value) + ((size_t)max(wm[k], 0) * Hkv + g) * D;
-#pragma unroll
-          for (int e = 0; e < D / 64; ++e) vrow[k][e] = has ? vk[lane + 64 * e] : T(0);
-        }
-        const int km = lane / PPR;
-        const int kmem = km < 4 ? wm[km] : -1;
-        if (kmem >= 0) krow = reinterpret_cast<const u32x4*>(new_row(kmem))[lane % PPR];
-      } else {
-        slot_blk[0] = TBL ? bt[(L - 1) / S] : contig0 + (L - 1) / S;
-        if (lane < PPR) krow = reinterpret_cast<const u32x4*>(kn)[lane];
-#pragma unroll
-        for (int e = 0; e < D / 64; ++e) vrow[0][e] = vn[lane + 64 * e];
-      }
-    }
+  if (!WG && fused) {
+    if (PARTIAL) load_new_rows();
+    // Lane 0's entry is the one used; the others read neighbours in the row, which keeps this
+    // a vector load.
+    if (wave == 0)
+      slot_blk = TBL ? bt[min((L - 1) / S + lane, MB - 1)] : contig0 + (L - 1) / S;
   }
 
   // Consumes the new rows loaded above (after this wave's first loads are in flight): the
   // last wave's logits and wave 0's LDS copy of the V row.
   auto use_new_rows = [&]() {
+    // The empty asm statements order this after the first chunk's loads (which the compiler
+    // would otherwise let it precede, waiting there for the new rows before issuing them).
     if (wave == NW - 1) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(kpiece[kk]) : : "memory");
       // Logit of head c: fp32 dot over the d pieces this lane holds of q, summed over rows.
       float part_dot = 0.0f;
 #pragma unroll
@@ -605,20 +622,36 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
 #pragma unroll
       for (int k = 0; k < NMEM; ++k)
 #pragma unroll
+        for (int e = 0; e < D / 64; ++e) asm volatile("" : "+v"(vrow[k][e]) : : "memory");
+#pragma unroll
+      for (int k = 0; k < NMEM; ++k) {
+        const bool has = !WG || (wm[k] >= 0 && wL[k] > 0);
+#pragma unroll
         for (int e = 0; e < D / 64; ++e) {
           const int d = lane + 64 * e;
-          if constexpr (DT == Dt::BF16) sh_vnew[k * D + d] = bits_f((uint32_t)vrow[k][e] << 16);
-          else sh_vnew[k * D + d] = (float)vrow[k][e];
+          float x;
+          if constexpr (DT == Dt::BF16) x = bits_f((uint32_t)vrow[k][e] << 16);
+          else x = (float)vrow[k][e];
+          sh_vnew[k * D + d] = has ? x : 0.0f;
         }
+      }
     }
   };
 
+  // WG: the members' own K streams from HBM with the non-temporal policy, so that it does not
+  // push the shared tiles out of L2 (V loads stay ordinary). The policy is an immediate of the
+  // load instruction, and a choice per chunk (a branch around the loads) makes the compiler
+  // lose count of the loads in flight, so that it waits for the next chunk's K before
+  // computing the current one. So the policy is the wave's, for its whole loop (two copies of
+  // the loop): while both kinds of chunks last, the odd waves take the own chunks and the even
+  // ones the shared chunks (the order of the list above), and of the chunks left after that,
+  // of one kind, the odd waves load theirs non-temporal.
   int n = wave;
-  if (n < nch) {
+  auto chunk_loop = [&](auto knt) {
     Regs A, B;
     Ids ids = fetch_ids(0);
     int m_next = 1;  // local index of the chunk whose ids are fetched next
-    load(ids, A, 0);
+    load(ids, A, 0, knt);
     if (n + NW < nch) ids = fetch_ids(m_next++);
     if (fused) use_new_rows();
     // Two stages: chunk n + NW loads while chunk n computes; its block ids were fetched one
@@ -636,7 +669,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
         compute(n, A, 0, last);
         break;
       }
-      load(ids, B, 1);
+      load(ids, B, 1, knt);
       if (n + 2 * NW < nch) ids = fetch_ids(m_next++);
       wait_vm_le<KLD + NT>();
       compute(n, A, 0, mid);
@@ -646,36 +679,22 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
         compute(n, B, 1, last);
         break;
       }
-      load(ids, A, 0);
+      load(ids, A, 0, knt);
       if (n + 2 * NW < nch) ids = fetch_ids(m_next++);
       wait_vm_le<KLD + NT>();
       compute(n, B, 1, mid);
       n += NW;
     }
+  };
+  if (n < nch) {
+    if constexpr (WG) {
+      if (wave & 1) chunk_loop(std::true_type());
+      else chunk_loop(std::false_type());
+    } else {
+      chunk_loop(std::false_type());
+    }
   } else if (fused) {
     use_new_rows();
-  }
-
-  // The new rows go to the slot the table maps position L-1 to. The stores come after every
-  // block-table read so the table can stay in the scalar cache (a store that might alias it
-  // would force those reads through the vector memory path).
-  // WG: each member's rows (V read back from LDS, where it is stored exactly).
-  if (fused && wave == 0) {
-#pragma unroll
-    for (int k = 0; k < NMEM; ++k) {
-      const int Lk = WG ? wL[k] : L;
-      if (WG && (wm[k] < 0 || Lk <= 0)) continue;
-      const int p = Lk - 1;
-      const size_t tile = ((size_t)clamp_id(slot_blk[k]) * Hkv + g) * S * D;
-      T* kc = reinterpret_cast<T*>(a.k_cache) + tile + (size_t)(p % S) * D;
-      T* vc = reinterpret_cast<T*>(a.v_cache) + tile + (size_t)((p % S) / VS) * VS * D + p % VS;
-      if (WG ? lane / PPR == k : lane < PPR)
-        reinterpret_cast<u32x4*>(kc)[WG ? lane % PPR : lane] = krow;
-#pragma unroll
-      for (int e = 0; e < D / 64; ++e)
-        vc[(size_t)(lane + 64 * e) * VS] =
-            WG ? from_f32<DT>(sh_vnew[k * D + lane + 64 * e]) : vrow[0][e];
-    }
   }
 
   l = across16(l, OpAdd());
@@ -730,6 +749,31 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
       }
     } else {
       reinterpret_cast<T*>(a.out)[row * D + d] = from_f32<DT>(o);
+    }
+  }
+
+  // The new rows go to the slot the table maps position L-1 to. The stores come last: after
+  // every block-table read, so the table can stay in the scalar cache (a store that might alias
+  // it would force those reads through the vector memory path), and after the merge, whose LDS
+  // reads wait for every vector memory operation in flight (the direct-to-LDS loads count as
+  // LDS writes), stores included.
+  // WG: each member's rows (V read back from LDS, where it is stored exactly).
+  if (fused && wave == 0) {
+#pragma unroll
+    for (int k = 0; k < NMEM; ++k) {
+      const int Lk = WG ? wL[k] : L;
+      if (WG && (wm[k] < 0 || Lk <= 0)) continue;
+      const int p = Lk - 1;
+      const size_t tile =
+          ((size_t)clamp_id(__builtin_amdgcn_readlane(slot_blk, k)) * Hkv + g) * S * D;
+      T* kc = reinterpret_cast<T*>(a.k_cache) + tile + (size_t)(p % S) * D;
+      T* vc = reinterpret_cast<T*>(a.v_cache) + tile + (size_t)((p % S) / VS) * VS * D + p % VS;
+      if (WG ? lane / PPR == k : lane < PPR)
+        reinterpret_cast<u32x4*>(kc)[WG ? lane % PPR : lane] = krow;
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e)
+        vc[(size_t)(lane + 64 * e) * VS] =
+            WG ? from_f32<DT>(sh_vnew[k * D + lane + 64 * e]) : vrow[0][e];
     }
   }
 }
