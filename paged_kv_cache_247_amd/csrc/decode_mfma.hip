@@ -218,15 +218,16 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
   // default makes the compiler copy, and so wait for, the load right where it is issued).
   u32x4 kpiece[KK];
   u32x4 krow;
-  T vrow[NMEM][D / 64];
+  T vrow[D / 64];  // the sequence's V row (not WG)
+  u32x4 vrow4;     // WG: sixteen-byte piece lane % PPR of member lane / PPR's V row
   // Block of the newest position: one per lane (lane k: member k's), so that the load stays a
   // vector load that nothing waits for until the stores at the end (a uniform one would be
   // moved to a scalar register, with a wait, as soon as it is issued).
   int slot_blk;
   // The rows depend on the unit only (in split mode on the range too: there they are loaded
   // once the length is known). Every load is unconditional: lanes past a row's pieces and
-  // missing members read rows that exist (the stores skip them; use_new_rows zeroes a missing
-  // member's V).
+  // missing members read rows that exist (the stores skip them; publish_new_rows zeroes a
+  // missing member's V).
   auto load_new_rows = [&]() {
     if (wave == NW - 1) {
       const char* kp = WG ? new_row(max(column_seq(c), 0)) : kn;
@@ -235,15 +236,16 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
         kpiece[kk] = *reinterpret_cast<const u32x4*>(kp + (32 * kk + 8 * r) * EB);
     }
     if (wave == 0) {
-#pragma unroll
-      for (int k = 0; k < NMEM; ++k) {
-        const T* vk = WG ? reinterpret_cast<const T*>(a.new_value) +
-                               ((size_t)max(wm_of(k), 0) * Hkv + g) * D
-                         : vn;
-#pragma unroll
-        for (int e = 0; e < D / 64; ++e) vrow[k][e] = vk[lane + 64 * e];
-      }
+      // WG: the members' V rows in one load, laid out like their K rows below.
       const int km = min(lane / PPR, NMEM - 1);
+      if constexpr (WG) {
+        const int m = max(wm_of(km), 0);
+        vrow4 = reinterpret_cast<const u32x4*>(
+            reinterpret_cast<const char*>(a.new_value) + ((size_t)m * Hkv + g) * D * EB)[lane % PPR];
+      } else {
+#pragma unroll
+        for (int e = 0; e < D / 64; ++e) vrow[e] = vn[lane + 64 * e];
+      }
       krow = reinterpret_cast<const u32x4*>(WG ? new_row(max(wm_of(km), 0)) : kn)[lane % PPR];
     }
   };
@@ -598,12 +600,15 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
       slot_blk = TBL ? bt[min((L - 1) / S + lane, MB - 1)] : contig0 + (L - 1) / S;
   }
 
-  // Consumes the new rows loaded above (after this wave's first loads are in flight): the
-  // last wave's logits and wave 0's LDS copy of the V row.
-  auto use_new_rows = [&]() {
-    // The empty asm statements order this after the first chunk's loads (which the compiler
-    // would otherwise let it precede, waiting there for the new rows before issuing them).
+  // The new position's logits (the last wave: a register per lane, computed once the first
+  // chunk's loads are out) and, after the chunk loop, the LDS copies the merge reads: the
+  // logits and the V rows. LDS writes while direct-to-LDS loads are in flight would make the
+  // compiler wait for those loads (they count as LDS writes), so none are made before the loop.
+  float nlogit = 0.0f;
+  auto new_logit = [&]() {
     if (wave == NW - 1) {
+      // The empty asm statements keep this after the first chunk's loads (the compiler would
+      // otherwise let it precede them, waiting there for the new rows).
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(kpiece[kk]) : : "memory");
       // Logit of head c: fp32 dot over the d pieces this lane holds of q, summed over rows.
@@ -615,24 +620,26 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
         for (int j = 0; j < 8; ++j) part_dot = fmaf((float)qb[kk][j], (float)kv[j], part_dot);
       }
       part_dot = across16(part_dot, OpAdd());
-      part_dot = across32(part_dot, OpAdd());
-      if (r == 0 && c < ncol) sh_new[c] = part_dot * a.scale_log2e;
+      nlogit = across32(part_dot, OpAdd()) * a.scale_log2e;
     }
+  };
+  auto publish_new_rows = [&]() {
+    if (wave == NW - 1 && r == 0 && c < ncol) sh_new[c] = nlogit;
     if (wave == 0) {
+      if constexpr (WG) {
+        const int k = lane / PPR;  // lanes past the four members' pieces hold copies
+        const bool has = wm[min(k, NMEM - 1)] >= 0 && wL[min(k, NMEM - 1)] > 0;
+        const V8 x = __builtin_bit_cast(V8, vrow4);
+        if (k < NMEM) {
 #pragma unroll
-      for (int k = 0; k < NMEM; ++k)
-#pragma unroll
-        for (int e = 0; e < D / 64; ++e) asm volatile("" : "+v"(vrow[k][e]) : : "memory");
-#pragma unroll
-      for (int k = 0; k < NMEM; ++k) {
-        const bool has = !WG || (wm[k] >= 0 && wL[k] > 0);
+          for (int j = 0; j < 8; ++j) sh_vnew[k * D + (lane % PPR) * 8 + j] = has ? (float)x[j] : 0.0f;
+        }
+      } else {
 #pragma unroll
         for (int e = 0; e < D / 64; ++e) {
           const int d = lane + 64 * e;
-          float x;
-          if constexpr (DT == Dt::BF16) x = bits_f((uint32_t)vrow[k][e] << 16);
-          else x = (float)vrow[k][e];
-          sh_vnew[k * D + d] = has ? x : 0.0f;
+          if constexpr (DT == Dt::BF16) sh_vnew[d] = bits_f((uint32_t)vrow[e] << 16);
+          else sh_vnew[d] = (float)vrow[e];
         }
       }
     }
@@ -653,7 +660,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
     int m_next = 1;  // local index of the chunk whose ids are fetched next
     load(ids, A, 0, knt);
     if (n + NW < nch) ids = fetch_ids(m_next++);
-    if (fused) use_new_rows();
+    if (fused) new_logit();
     // Two stages: chunk n + NW loads while chunk n computes; its block ids were fetched one
     // step earlier still. The LDS half of a chunk is not tracked by the compiler, so each
     // step waits explicitly: vector memory operations complete in order, and exactly
@@ -694,8 +701,9 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
       chunk_loop(std::false_type());
     }
   } else if (fused) {
-    use_new_rows();
+    new_logit();
   }
+  if (fused) publish_new_rows();
 
   l = across16(l, OpAdd());
   l = across32(l, OpAdd());
@@ -773,7 +781,7 @@ __device__ __forceinline__ void decode_unit(const DecodeParams& a, const int w,
 #pragma unroll
       for (int e = 0; e < D / 64; ++e)
         vc[(size_t)(lane + 64 * e) * VS] =
-            WG ? from_f32<DT>(sh_vnew[k * D + lane + 64 * e]) : vrow[0][e];
+            WG ? from_f32<DT>(sh_vnew[k * D + lane + 64 * e]) : vrow[e];
     }
   }
 }
