@@ -48,13 +48,15 @@ PAGES_CLAIM = {
     "hardware": "not stated on the page"}
 
 # Launch configuration the benchmark uses for each workload: (kernel family, partition size,
-# cached K/V loads). With longest-first dispatch, single-pass decode is fastest up to 4k-token
-# contexts; the lognormal long-context batch (up to ~31k tokens) splits into the 512-token
-# partitions its statement names; the prefix-shared batch keeps K/V in cache so the shared
-# prefix is reused.
+# cached K/V loads). With longest-first dispatch, single-pass decode is fastest for the GQA
+# batch (matrix-core workgroups fill two whole rounds of the GPU); the MHA batch's vector-ALU
+# grid is 1.33 rounds, and 768-token partitions plus the merge even out its last round (step
+# 183.4 against 185.9 us single pass, back to back); the lognormal long-context batch (up to
+# ~31k tokens) splits into the 512-token partitions its statement names; the prefix-shared
+# batch keeps K/V in cache so the shared prefix is reused.
 LAUNCH = {
     "c1": ("auto", 0, False),
-    "c2": ("auto", 0, False),
+    "c2": ("auto", 768, False),
     "c3": ("auto", 0, False),
     "c4": ("auto", 0, True),
     "c5": ("auto", 512, False),
@@ -241,10 +243,10 @@ def parity(out, expected, dtype: str, what: str) -> dict:
 
 # ------------------------------------------------------------------ GPU helpers
 
-def counter_traffic(kernel_sources, workload, shared=False):
+def counter_traffic(kernel_sources, workload, shared=False, partition_size=0):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary, if the summary
     was taken on the kernel sources as they are now and in the same decode mode (the grouped
-    shared-prefix launches or not), else None."""
+    shared-prefix launches or not, the same partition size), else None."""
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(root, "profiles", f"decode_{workload}_counters.txt")
@@ -261,6 +263,8 @@ def counter_traffic(kernel_sources, workload, shared=False):
     if vals.get("source_sha256") != h.hexdigest():
         return None
     if vals.get("shared_prefix", "0") != str(shared if isinstance(shared, str) else int(bool(shared))):
+        return None
+    if vals.get("partition_size", "0") != str(int(partition_size)):
         return None
     return int(float(vals["traffic_bytes_per_launch"]))
 
@@ -826,7 +830,7 @@ def main():
     span = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     span[0].record()
     for _ in range(args.steps):
-        s.step(None if alone else ev)
+        s.step()
     span[1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -835,13 +839,16 @@ def main():
     if alone:
         dec_ms = span[0].elapsed_time(span[1]) / args.steps
     else:
-        # The step has other kernels too: an event pair around each decode launch also times
-        # the gaps the events themselves open (a few us per launch), so the launch duration is
-        # taken the way it is for a step of the decode alone -- the same launch repeated
-        # `steps` times back to back under one event pair (its inputs are unchanged by a
-        # repeat) -- and the per-launch event figure is reported beside it.
-        in_step_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+        # The step has other kernels too. The timed steps above hold no events: an event pair
+        # around each decode launch opens gaps of its own (a few us per step), which would be
+        # charged to the step. The launch duration is taken the way it is for a step of the
+        # decode alone -- the same launch repeated `steps` times back to back under one event
+        # pair (its inputs are unchanged by a repeat) -- and a further `steps` steps with an
+        # event pair around each decode give the in-step figure reported beside it.
+        for _ in range(args.steps):
+            s.step(ev)
         torch.cuda.synchronize()
+        in_step_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.steps):
@@ -865,7 +872,7 @@ def main():
     traffic = None if shard or args.layout != "paged" or \
         cfg.block_size != W.CONFIGS[name].block_size \
         else counter_traffic(KERNEL_SOURCES[s.family], name,
-                             "whole" if s.whole is not None else s.plan is not None)
+                             "whole" if s.whole is not None else s.plan is not None, s.P)
     value = kvb / (ms_step * 1e-3) / 1e9
     rb = roofline_bytes(wl)
     # With shared prefix blocks the logical bytes count the prefix once per sequence, but it is
