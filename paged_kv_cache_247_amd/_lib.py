@@ -576,22 +576,37 @@ def v_cache_to_rows(v_cache, v_rows):
     _v_layout("pkv_v_cache_to_rows", v_cache, v_rows, False)
 
 
-AUTO_PARTITION_TOKENS = 2048
+AUTO_PARTITION_TOKENS = 2048       # matrix-core decode (16-bit, query groups of 4 or more)
+AUTO_PARTITION_TOKENS_VALU = 768   # vector-ALU decode (fp32, or groups of 1-2)
 
 
 def auto_partition_size(num_seqs: int, num_kv_heads: int, block_size: int,
-                        device=None, num_cus: int | None = None) -> int:
-    """Host policy for split-context decode: single pass (0) when the (sequence, kv head) units
-    fill two rounds of the GPU's workgroup slots (two per CU), else 2048-token partitions, so
-    that a few long sequences do not leave most CUs idle behind them. Measured on the GQA shape
-    at equal total tokens: 128 sequences single pass 188 us; 64 sequences 195.5 -> 190.3 us and
-    32 sequences 218.7 -> 187.3 us with 2048-token partitions (merge included)."""
+                        device=None, num_cus: int | None = None, group: int = 4,
+                        dtype: str = "bf16") -> int:
+    """Host policy for split-context decode: single pass (0) when the single-pass grid fills two
+    rounds of the GPU's workgroup slots, else partitions, so that a few long sequences do not
+    leave most CUs idle behind them and the last round stays even. The kernel family is the one
+    the library picks for `group` (query heads per kv head) and `dtype`:
+    * matrix cores (16-bit, group >= 4): a workgroup per (sequence, kv head), two per CU; else
+      2048-token partitions. Measured on the GQA shape at equal total tokens: 128 sequences
+      single pass 188 us; 64 sequences 195.5 -> 190.3 us and 32 sequences 218.7 -> 187.3 us with
+      2048-token partitions (merge included).
+    * vector ALUs (fp32, or group < 4): a workgroup per (sequence, two kv heads when their count
+      is even), three per CU; else 768-token partitions. Measured on the MHA batch (64
+      sequences, 32 heads, contexts up to 2048: 1.33 rounds): step 185.9 us single pass, 183.4
+      us in 768-token partitions with the merge (512: 184.4, 1024: 186.0)."""
     if num_cus is None:
         num_cus = torch.cuda.get_device_properties(device if device is not None else
                                                    torch.cuda.current_device()).multi_processor_count
-    if num_seqs * num_kv_heads >= 4 * num_cus:
+    mfma = dtype != "f32" and group >= 4
+    if mfma:
+        workgroups, per_cu, tokens = num_seqs * num_kv_heads, 2, AUTO_PARTITION_TOKENS
+    else:
+        hpw = 2 if num_kv_heads % 2 == 0 else 1
+        workgroups, per_cu, tokens = num_seqs * (num_kv_heads // hpw), 3, AUTO_PARTITION_TOKENS_VALU
+    if workgroups >= 2 * per_cu * num_cus:
         return 0
-    return max(block_size, AUTO_PARTITION_TOKENS // block_size * block_size)
+    return max(block_size, tokens // block_size * block_size)
 
 
 def paged_attention(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
@@ -601,8 +616,10 @@ def paged_attention(out, q, k_cache, v_cache, block_tables, context_lens, max_co
     partition_size="auto" applies auto_partition_size (a work list, if given, must have been
     built for the size it picks)."""
     if partition_size == "auto":
-        partition_size = auto_partition_size(q.shape[0], k_cache.shape[1], k_cache.shape[2],
-                                             q.device)
+        partition_size = auto_partition_size(
+            q.shape[0], k_cache.shape[1], k_cache.shape[2], q.device,
+            group=q.shape[1] // k_cache.shape[1],
+            dtype={torch.float32: "f32", torch.float16: "f16"}.get(q.dtype, "bf16"))
     kw = dict(kernel=kernel, work_items=work_items, cached_kv=cached_kv, new_key=new_key,
               new_value=new_value, max_blocks_per_seq=max_blocks_per_seq)
     if partition_size:

@@ -318,14 +318,22 @@ def test_prefill_tile_tokens(lib):
 
 
 def test_auto_partition_policy():
-    """Single pass while (sequence, kv head) units fill two rounds of two workgroups per CU,
-    else 2048-token partitions (a multiple of the block size)."""
+    """Single pass while the single-pass grid fills two rounds of workgroup slots (matrix
+    cores: a workgroup per (sequence, kv head), two per CU; vector ALUs: per (sequence, two kv
+    heads), three per CU), else 2048- or 768-token partitions (a multiple of the block size)."""
     import paged_kv_cache_247_amd as pk
     assert pk.auto_partition_size(128, 8, 16, num_cus=256) == 0      # 1024 units
     assert pk.auto_partition_size(64, 8, 16, num_cus=256) == 2048    # 512 units
     assert pk.auto_partition_size(32, 8, 32, num_cus=256) == 2048
     assert pk.auto_partition_size(1, 1, 16, num_cus=256) == 2048
     assert pk.auto_partition_size(2048, 32, 16, num_cus=256) == 0
+    # the vector-ALU family: MHA 64 x 32 heads is 1024 workgroups (1.33 rounds of 768 slots)
+    assert pk.auto_partition_size(64, 32, 16, num_cus=256, group=1) == 768
+    assert pk.auto_partition_size(96, 32, 16, num_cus=256, group=1) == 0     # 1536 workgroups
+    assert pk.auto_partition_size(128, 8, 16, num_cus=256, dtype="f32") == 768  # fp32 GQA
+    assert pk.auto_partition_size(3, 3, 256, num_cus=256, group=2) == 768
+    assert pk.auto_partition_size(3, 3, 512, num_cus=256, group=2) == 512   # at least a block
+    assert pk.auto_partition_size(512, 8, 16, num_cus=256, group=2) == 0
 
 
 def test_binding_refuses_another_abi(monkeypatch):

@@ -406,13 +406,16 @@ def test_full_size_against_oracle(name, P_over):
     assert oracle.max_abs_err(out, ref) <= TOL[cfg.dtype], detail
 
 
-def test_auto_partition_size_matches_oracle():
-    """partition_size="auto" on a batch of few long sequences picks split-context partitions
-    and still matches the oracle; on many sequences it stays single pass."""
-    cfg = W.SMALL["c5"]
+@pytest.mark.parametrize("name", ["c5", "c2"])
+def test_auto_partition_size_matches_oracle(name):
+    """partition_size="auto" on a small batch picks split-context partitions (2048 tokens on
+    the matrix cores, 768 on the vector ALUs for MHA) and still matches the oracle; on many
+    sequences it stays single pass."""
+    cfg = W.SMALL[name]
     wl = W.generate(cfg)
     dt = cfg.dtype
-    P = pk.auto_partition_size(cfg.num_seqs, cfg.num_kv_heads, cfg.block_size)
+    P = pk.auto_partition_size(cfg.num_seqs, cfg.num_kv_heads, cfg.block_size,
+                               group=cfg.num_heads // cfg.num_kv_heads, dtype=dt)
     assert P > 0 and P % cfg.block_size == 0
     d = upload(wl)
     if len(wl.block_mapping):
