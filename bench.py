@@ -119,6 +119,13 @@ def parse():
                          "1/N of the kv heads (and their q heads), seq:N 1/N of the sequences")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
+    ap.add_argument("--between-launches", default=None, choices=list(BETWEEN),
+                    help="also time single decode launches (an event pair around each, a "
+                         "synchronisation between them) with nothing before each and with this "
+                         "work before each: l2 = a copy moving 32 MiB (the L2s), llc = a copy "
+                         "moving 1 GiB (also the last-level cache and many page translations), "
+                         "tlb = one byte read per 64 KiB of 8 GiB (page translations, little "
+                         "data)")
     args = ap.parse_args()
     layout = args.layout
     if not (layout in ("paged", "contiguous", "contiguous-table") or
@@ -267,6 +274,44 @@ def counter_traffic(kernel_sources, workload, shared=False, partition_size=0):
     if vals.get("partition_size", "0") != str(int(partition_size)):
         return None
     return int(float(vals["traffic_bytes_per_launch"]))
+
+
+# Work run before each launch by --between-launches: what a layer's decode finds in the memory
+# system when other work ran since its previous launch.
+BETWEEN = {"l2": "device copy of 16 MiB (32 MiB moved)",
+           "llc": "device copy of 512 MiB (1 GiB moved)",
+           "tlb": "one byte read per 64 KiB of an 8 GiB buffer"}
+
+
+def between_launches(torch, fn, mode: str, rounds: int = 3, launches: int = 20):
+    """Microseconds per single launch of fn (an event pair around it, a synchronisation after
+    it), medians over `launches` for each of `rounds` rounds, without and with the work named
+    by `mode` before each launch."""
+    if mode == "tlb":
+        buf = torch.zeros(8 << 30, dtype=torch.uint8, device="cuda").view(-1, 65536)
+        before = lambda: buf[:, 0].sum()  # noqa: E731
+    else:
+        n = (32 << 20) if mode == "l2" else (1 << 30)
+        a = torch.zeros(n // 2, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        before = lambda: b.copy_(a)  # noqa: E731
+    res = {"nothing": [], mode: []}
+    for _ in range(rounds):
+        for key in res:
+            ts = []
+            for _ in range(launches):
+                if key != "nothing":
+                    before()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            ts.sort()
+            res[key].append(round(ts[len(ts) // 2], 2))
+    return {"before_each_launch": BETWEEN[mode], "us_with_nothing_before": res["nothing"],
+            "us_with_it_before": res[mode], "rounds": rounds, "launches_per_round": launches}
 
 
 def launch_stats(torch, fn, launches: int, reps: int, warmup: int = 10):
@@ -924,6 +969,10 @@ def main():
     }
     if cpu is not None:
         line["cpu_baseline"] = cpu
+    if args.between_launches:
+        print(f"[bench] single launches, {BETWEEN[args.between_launches]} before each",
+              file=sys.stderr, flush=True)
+        line["between_launches"] = between_launches(torch, s.decode, args.between_launches)
 
     default_run = (name == "c3" and args.layout == "paged" and not shard and not args.unfused
                    and args.block_size in (None, W.CONFIGS[name].block_size)
