@@ -75,3 +75,8 @@ def test_counter_traffic_is_gated_on_sources_mode_and_partition_size(name, famil
     assert bench.counter_traffic(src, name, "whole" if mode is False else False, P) is None
     other = bench.KERNEL_SOURCES["mfma" if family == "valu" else "valu"]
     assert bench.counter_traffic(other, name, mode, P) is None
+
+
+def test_unknown_between_launches_work_is_refused():
+    r = run("--config", "c3", "--between-launches", "everything", "--no-cpu-baseline")
+    assert r.returncode == 2 and "--between-launches" in r.stderr and not r.stdout
